@@ -1,0 +1,384 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Nothing here compares the oracle with itself: each check uses a closed form,
+a hand derivation stored under tests/golden/, an independent library routine
+(torch's float8_e4m3fn cast and scaled_dot_product_attention, Python's
+round-half-even), brute force, or an invariant of the definition.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, formats, fp8, nvfp4
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16_bits(x):
+    """bf16 bits of float values that bf16 represents exactly (test helper)."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32)
+    assert not np.any(u & 0xFFFF)
+    return (u >> 16).astype(np.uint16)
+
+
+def _all_bf16_finite():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        v = nvfp4.bf16_to_f64(b)
+    ok = np.isfinite(v)
+    return b[ok], v[ok]
+
+
+# ---------------------------------------------------------------------------
+# formats
+# ---------------------------------------------------------------------------
+
+def test_e2m1_table_matches_golden():
+    with open(os.path.join(GOLDEN, "e2m1_magnitudes.txt")) as f:
+        vals = [float(t) for line in f if not line.startswith("#") for t in line.split()]
+    assert vals == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    assert list(formats.E2M1_VALUES[:8]) == vals
+    assert list(formats.E2M1_VALUES[8:]) == [-v for v in vals]
+    assert math.copysign(1.0, formats.E2M1_VALUES[8]) == -1.0
+
+
+def test_e4m3_closed_form_points():
+    v = formats.E4M3_VALUES
+    assert v[0x7E] == 448.0 and formats.E4M3_MAX == 448.0
+    assert v[0x01] == 2.0 ** -9
+    assert v[0x07] == 7 * 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    assert v[0x38] == 1.0
+    assert math.isnan(v[0x7F]) and math.isnan(v[0xFF])
+    assert v[0x80] == 0.0 and math.copysign(1.0, v[0x80]) == -1.0
+    finite = v[:127]
+    assert np.all(np.diff(finite) > 0)
+
+
+def test_e4m3_decode_matches_torch():
+    b = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = b.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = formats.E4M3_VALUES
+    assert np.array_equal(np.isnan(ref), np.isnan(ours))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ref[m], ours[m])
+
+
+def test_e4m3_encode_matches_torch_on_every_bf16():
+    bits, vals = _all_bf16_finite()
+    in_range = np.abs(vals) < 464.0          # torch's cast does not saturate beyond
+    x = vals[in_range]
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = formats.e4m3_encode(x)
+    assert np.array_equal(ours, ref)
+    big = vals[~in_range]
+    enc = formats.e4m3_encode(big)
+    assert np.all((enc & 0x7F) == 0x7E)      # saturation to +-448
+    assert np.array_equal(enc >> 7, np.signbit(big).astype(np.uint8))
+
+
+def _e2m1_code_by_round(r: float) -> int:
+    """Independent rounding: the E2M1 grid is uniform on [0,2] (step 0.5),
+    [2,4] (step 1) and [4,6] (step 2); Python's round() is half-to-even, and on
+    each piece an even rounded value is an even code."""
+    if r >= 6:
+        return 7
+    if r <= 2:
+        return int(round(r * 2))            # codes 0..4 are 0, .5, 1, 1.5, 2
+    if r <= 4:
+        return int(round(r)) + 2            # codes 4..6 are 2, 3, 4
+    return 6 if round(r / 2) == 2 else 7    # codes 6..7 are 4, 6
+
+
+def test_e2m1_rounding_matches_piecewise_round():
+    _, vals = _all_bf16_finite()
+    r = np.abs(vals[(np.abs(vals) <= 8)])
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    r = np.unique(np.concatenate([r, mids, mids + 1e-12, mids - 1e-12]))
+    ours = formats.e2m1_magnitude_code(r)
+    ref = np.array([_e2m1_code_by_round(float(x)) for x in r])
+    assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 block encode
+# ---------------------------------------------------------------------------
+
+def _golden_vectors():
+    cases = []
+    with open(os.path.join(GOLDEN, "nvfp4_block_vectors.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, xs, s, data = [p.strip() for p in line.split("|")]
+            x = [float(t) for t in xs.split()]
+            cases.append((name, x, int(s, 16), [int(t, 16) for t in data.split()]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_vectors(), ids=lambda c: c[0])
+def test_block_vectors_golden(case):
+    name, x, s_exp, data_exp = case
+    bits = _bf16_bits(np.array(x, dtype=np.float64)).reshape(1, 1, 16)
+    data, scale = nvfp4.quantize_rows(bits)
+    assert int(scale[0, 0, 0]) == s_exp
+    assert list(data[0, 0]) == data_exp
+
+
+def test_round_trip_every_scale():
+    """Blocks built as S * (E2M1 values including +-6) encode to S's own byte
+    and decode back exactly, for every positive finite E4M3 scale."""
+    rng = np.random.default_rng(0)
+    for sb in range(1, 0x7F):
+        S = formats.E4M3_VALUES[sb]
+        codes = rng.integers(0, 16, size=16)
+        codes[rng.integers(0, 16)] = 7 if rng.random() < 0.5 else 15   # amax = 6 S
+        x = formats.E2M1_VALUES[codes] * S
+        bits = _bf16_bits(x).reshape(1, 1, 16)
+        data, scale = nvfp4.quantize_rows(bits)
+        assert int(scale[0, 0, 0]) == sb
+        back = nvfp4.dequant_rows(data, scale)
+        assert np.array_equal(back.reshape(16), x)
+
+
+def test_encode_is_nearest_by_brute_force():
+    """Scale = nearest E4M3 to amax/6 and each code = nearest E2M1 to |x|/S,
+    checked by exhaustive argmin over the candidates (ties to the even code)."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2000, 16)).astype(np.float32)
+    x[::7] *= 20.0
+    x[::11] *= 1e-3
+    bits = np.asarray(x).view(np.uint32)
+    bits = ((bits.astype(np.uint64) + 0x7FFF + ((bits >> 16) & 1)) >> 16).astype(np.uint16)
+    xv = nvfp4.bf16_to_f64(bits)
+    data, scale = nvfp4.quantize_rows(bits.reshape(2000, 1, 16))
+    codes = nvfp4.unpack_nibbles(data.reshape(2000, 8))
+    e4 = formats.E4M3_VALUES[:127]
+    e2 = formats.E2M1_VALUES[:8]
+    for i in range(2000):
+        target = np.max(np.abs(xv[i])) / 6.0
+        dist = np.abs(e4 - target)
+        best = np.flatnonzero(dist == dist.min())
+        sb = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+        if target > 448:
+            sb = 0x7E
+        assert scale[i, 0, 0] == sb
+        S = e4[sb]
+        for j in range(16):
+            c = codes[i, j]
+            assert (c >> 3) == (1 if math.copysign(1.0, xv[i, j]) < 0 else 0)
+            if S == 0:
+                assert (c & 7) == 0
+                continue
+            r = abs(xv[i, j]) / S
+            dd = np.abs(e2 - r)
+            cand = np.flatnonzero(dd == dd.min())
+            want = cand[0] if len(cand) == 1 else [c2 for c2 in cand if c2 % 2 == 0][0]
+            if r > 6:
+                want = 7
+            assert (c & 7) == want
+
+
+def test_storage_ratio_golden():
+    facts = {}
+    with open(os.path.join(GOLDEN, "storage_ratio.txt")) as f:
+        for line in f:
+            if not line.startswith("#") and line.strip():
+                k, v = line.split()
+                facts[k] = float(v)
+    for d in (64, 128):
+        nv = nvfp4.storage_bytes(1000, 8, d)
+        f8 = 1000 * 8 * d
+        assert nv / f8 == facts["ratio"] == (facts["nvfp4_bytes_per_16"] / facts["fp8_bytes_per_16"])
+        data, scale = nvfp4.empty_cache(10, 8, 16, d)
+        assert (data.nbytes + scale.nbytes) / (10 * 8 * 16 * d) == facts["ratio"]
+    assert round(1 / facts["ratio"], 2) == facts["capacity_gain_rounded"]
+
+
+def test_nibble_order_and_cache_layout():
+    assert list(nvfp4.pack_nibbles(np.array([1, 2, 0xF, 0x8], dtype=np.uint8))) == [0x21, 0x8F]
+    rng = np.random.default_rng(2)
+    P, H, d = 16, 2, 32
+    x = _bf16_bits(formats.E2M1_VALUES[rng.integers(0, 16, size=(3, H, d))])
+    data, scale = nvfp4.empty_cache(4, H, P, d, fill=0xAB)
+    nvfp4.write_cache(data, scale, x, np.array([2 * P + 5, -1, 0 * P + 15]))
+    rd, rs = nvfp4.quantize_rows(x)
+    assert np.array_equal(data[2, :, 5], rd[0]) and np.array_equal(scale[2, :, 5], rs[0])
+    assert np.array_equal(data[0, :, 15], rd[2]) and np.array_equal(scale[0, :, 15], rs[2])
+    untouched = np.ones(data.shape[:3], bool)
+    untouched[2, :, 5] = untouched[0, :, 15] = False
+    assert np.all(data[untouched] == 0xAB) and np.all(scale[untouched] == 0xAB)
+
+
+def test_planted_tie_mistake_is_caught():
+    """A rounding mistake planted in the oracle (ties away from zero) must
+    fail the golden vectors: the pins are sensitive to it."""
+    orig = formats._rne_on_grid
+
+    def ties_away(x, grid):
+        x = np.asarray(x, dtype=np.float64)
+        hi = np.minimum(np.searchsorted(grid, x, side="left"), len(grid) - 1)
+        lo = np.maximum(hi - 1, 0)
+        idx = np.where(grid[hi] - x <= x - grid[lo], hi, lo)
+        return np.where(x >= grid[-1], len(grid) - 1, np.where(x == 0, 0, idx))
+
+    formats._rne_on_grid = ties_away
+    try:
+        bad = 0
+        for name, x, s_exp, data_exp in _golden_vectors():
+            bits = _bf16_bits(np.array(x)).reshape(1, 1, 16)
+            data, scale = nvfp4.quantize_rows(bits)
+            bad += int(scale[0, 0, 0]) != s_exp or list(data[0, 0]) != data_exp
+        assert bad > 0
+    finally:
+        formats._rne_on_grid = orig
+
+
+# ---------------------------------------------------------------------------
+# FP8 baseline
+# ---------------------------------------------------------------------------
+
+def test_fp8_rows_match_torch_cast():
+    _, vals = _all_bf16_finite()
+    x = vals[np.abs(vals) < 464]
+    bits = _bf16_bits(x)
+    ours = fp8.quantize_rows(bits)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+    back = torch.from_numpy(ref).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(fp8.dequant_cache(ours), back)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _small_problem(seed=3, B=2, Hq=4, Hkv=2, d=32, P=16, lens=(37, 64)):
+    rng = np.random.default_rng(seed)
+    max_pages = max(-(-L // P) for L in lens)
+    num_pages = B * max_pages + 3
+    perm = rng.permutation(num_pages)
+    bt = perm[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    k_hat = rng.standard_normal((num_pages, Hkv, P, d))
+    v_hat = rng.standard_normal((num_pages, Hkv, P, d))
+    q = _bf16_bits(np.round(rng.standard_normal((B, Hq, d)) * 64) / 64)
+    return q, k_hat, v_hat, bt, np.array(lens, dtype=np.int32)
+
+
+def test_attention_matches_torch_sdpa():
+    q, k_hat, v_hat, bt, lens = _small_problem()
+    sm = 1 / math.sqrt(q.shape[-1])
+    out, mass = attention.paged_decode(q, k_hat, v_hat, bt, lens, sm)
+    qf = nvfp4.bf16_to_f64(q)
+    G = q.shape[1] // k_hat.shape[1]
+    for b in range(q.shape[0]):
+        k = attention.gather_tokens(k_hat, bt[b], lens[b])
+        v = attention.gather_tokens(v_hat, bt[b], lens[b])
+        kq = torch.from_numpy(np.repeat(k.transpose(1, 0, 2), G, axis=0))[None]
+        vq = torch.from_numpy(np.repeat(v.transpose(1, 0, 2), G, axis=0))[None]
+        qq = torch.from_numpy(qf[b])[None, :, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kq, vq, scale=sm)
+        np.testing.assert_allclose(out[b], ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+    assert np.all(mass >= np.abs(out) - 1e-12)
+
+
+def test_attention_brute_force_loops():
+    q, k_hat, v_hat, bt, lens = _small_problem(seed=4, B=1, Hq=2, Hkv=1, d=8, P=4, lens=(9,))
+    sm = 0.3
+    out, _ = attention.paged_decode(q, k_hat, v_hat, bt, lens, sm)
+    qf = nvfp4.bf16_to_f64(q)
+    P = k_hat.shape[2]
+    for h in range(2):
+        logits = []
+        for t in range(9):
+            page = bt[0][t // P]
+            s = 0.0
+            for c in range(8):
+                s += qf[0, h, c] * k_hat[page, 0, t % P, c]
+            logits.append(s * sm)
+        mx = max(logits)
+        w = [math.exp(z - mx) for z in logits]
+        for c in range(8):
+            acc = sum(w[t] * v_hat[bt[0][t // P], 0, t % P, c] for t in range(9))
+            assert abs(out[0, h, c] - acc / sum(w)) < 1e-13
+
+
+def test_attention_special_cases():
+    q, k_hat, v_hat, bt, lens = _small_problem(seed=5)
+    sm = 0.2
+    # L = 1: the output is the first value row
+    one = np.array([1, 1], dtype=np.int32)
+    out, _ = attention.paged_decode(q, k_hat, v_hat, bt, one, sm)
+    G = 2
+    for b in range(2):
+        for h in range(4):
+            np.testing.assert_array_equal(out[b, h], v_hat[bt[b, 0], h // G, 0])
+    # q = 0: uniform weights, the output is the mean value row
+    z = np.zeros_like(q)
+    out, _ = attention.paged_decode(z, k_hat, v_hat, bt, lens, sm)
+    for b in range(2):
+        v = attention.gather_tokens(v_hat, bt[b], lens[b])
+        for h in range(4):
+            np.testing.assert_allclose(out[b, h], v[:, h // G].mean(axis=0), rtol=1e-12, atol=1e-13)
+    # empty sequence: zeros
+    out, _ = attention.paged_decode(q, k_hat, v_hat, bt, np.array([0, 5], np.int32), sm)
+    assert np.all(out[0] == 0)
+
+
+def test_attention_dominant_key_selects_its_value():
+    d, P, L = 16, 8, 20
+    k = np.zeros((4, 1, P, d))
+    v = np.random.default_rng(6).standard_normal((4, 1, P, d))
+    bt = np.array([[2, 0, 3]], np.int32)
+    for t in range(L):                       # orthogonal one-hot keys
+        k[bt[0, t // P], 0, t % P, t % d] = 1.0
+    j = 13
+    q = _bf16_bits(np.eye(d)[j % d][None, None, :] * 256.0)
+    out, _ = attention.paged_decode(q, k, v, bt, np.array([L], np.int32), 1.0)
+    # tokens j and j - d share the one-hot direction only if j >= d; j=13 < 16 is unique
+    np.testing.assert_allclose(out[0, 0], v[bt[0, j // P], 0, j % P], atol=1e-100)
+
+
+def test_attention_page_permutation_invariance():
+    q, k_hat, v_hat, bt, lens = _small_problem(seed=7)
+    out1, _ = attention.paged_decode(q, k_hat, v_hat, bt, lens, 0.25)
+    perm = np.random.default_rng(8).permutation(k_hat.shape[0])
+    inv = np.argsort(perm)
+    out2, _ = attention.paged_decode(q, k_hat[perm], v_hat[perm], inv[bt].astype(np.int32), lens, 0.25)
+    np.testing.assert_array_equal(out1, out2)
+
+
+def test_gqa_group_one_is_mha():
+    q, k_hat, v_hat, bt, lens = _small_problem(seed=9, Hq=2, Hkv=2)
+    out, _ = attention.paged_decode(q, k_hat, v_hat, bt, lens, 0.3)
+    for h in range(2):
+        o1, _ = attention.paged_decode(q[:, h:h + 1], k_hat[:, h:h + 1], v_hat[:, h:h + 1], bt, lens, 0.3)
+        np.testing.assert_allclose(out[:, h], o1[:, 0], rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# extend-path workspace
+# ---------------------------------------------------------------------------
+
+def test_workspace_is_exact_bf16_of_dequantized_prefix():
+    rng = np.random.default_rng(10)
+    H, d, P, num_pages = 2, 32, 16, 12
+    x = _bf16_bits(np.round(rng.standard_normal((num_pages * P, H, d)) * 16) / 16)
+    data, scale = nvfp4.empty_cache(num_pages, H, P, d)
+    slots = rng.permutation(num_pages * P)
+    nvfp4.write_cache(data, scale, x, slots)
+    hat = nvfp4.dequant_cache(data, scale)
+    bt = rng.permutation(num_pages).astype(np.int32).reshape(3, 4)
+    prefix = np.array([17, 0, 64], np.int32)
+    offs = np.array([0, 20, 25, 100], np.int64)
+    ws = attention.dequant_workspace(hat, bt, prefix, offs, 100, fill=0x7FC0)
+    for b in range(3):
+        got = nvfp4.bf16_to_f64(ws[offs[b]:offs[b] + prefix[b]])
+        np.testing.assert_array_equal(got, attention.gather_tokens(hat, bt[b], prefix[b]))
+    assert np.all(ws[17:20] == 0x7FC0) and np.all(ws[20:25] == 0x7FC0) and np.all(ws[89:] == 0x7FC0)
+    # every E2M1 * E4M3 product is exact in bf16
+    prod = np.outer(formats.E2M1_VALUES, formats.E4M3_VALUES[:127]).reshape(-1)
+    attention.f64_to_bf16_exact(prod)
