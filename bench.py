@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 paged decode path on one MI355X.
+
+Workload (default): batch 44, 40 query / 8 KV heads, head_dim 128, context
+32,768, page 64, 32 splits, K/V ~ N(0,1) bf16 with 2% of channels x20 --
+the iso-concurrency long-context point of "Accelerating Long-Context and
+Agentic Inference with NVFP4 KV Cache" (section A4, Fig. 6), with the same
+layer also run over an FP8-E4M3 cache.
+
+One step = quantize-on-write of the step's new token of every sequence into
+the NVFP4 pool (it overwrites the last slot, so the shape stays fixed) +
+split-KV decode partials + log-sum-exp merge. Inputs are resident in HBM
+before timing. Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+  value           KV GB/s of the step: (packed + scale bytes) / step time
+  roofline        dominant kernel (decode partial): algorithmic bytes per
+                  launch / mean launch time (HIP events on the launch stream)
+  cpu_baseline    the CPU oracle (dequantize + fp64 attention) on a bounded
+                  sample of (sequence, KV head) slices of the same workload
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "NVFP4 paged decode attn: KV GB/s + % HBM roofline; steps/s vs FP8-KV kernel"
+DECODE_SOURCES = ["nvfp4_quantized_paged_amd/csrc/decode_mfma.hip", "nvfp4_quantized_paged_amd/csrc/decode_valu.hip",
+                  "nvfp4_quantized_paged_amd/csrc/common.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes(wl, fp8=False):
+    per = wl.head_dim if fp8 else wl.head_dim // 2 + wl.head_dim // 16
+    return 2 * wl.batch * wl.context * wl.num_kv_heads * per
+
+
+def io_bytes(wl):
+    return 2 * wl.batch * wl.num_q_heads * wl.head_dim * 2      # q read + out written (bf16)
+
+
+def partial_bytes(wl, splits):
+    return wl.batch * wl.num_q_heads * splits * (wl.head_dim + 2) * 4
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in DECODE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current decode kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Bench:
+    def __init__(self, nk, wl, fp8, variant):
+        import torch
+        from synth.workload import build_uniform_workload
+        self.torch = torch
+        self.nk, self.wl, self.fp8, self.variant = nk, wl, fp8, variant
+        t = time.time()
+        self.w = build_uniform_workload(nk, wl, fp8=fp8)
+        log(f"[bench] built {'fp8' if fp8 else 'nvfp4'} {wl.name} in {time.time() - t:.1f}s")
+        B, H, d, P, L = wl.batch, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.context
+        g = torch.Generator(device="cuda")
+        g.manual_seed(wl.seed + 1000)
+        self.k_new = torch.randn((B, H, d), generator=g, device="cuda").to(torch.bfloat16)
+        self.v_new = torch.randn((B, H, d), generator=g, device="cuda").to(torch.bfloat16)
+        last = L - 1
+        self.slots_new = (self.w.bt[:, last // P].to(torch.int64) * P + last % P).contiguous()
+        self.S = wl.num_splits or nk.nvfp4_paged_decode_num_splits(B, H, self.w.bt.shape[1], P)
+        self.ws = nk.decode_workspace(B, wl.num_q_heads, d, self.S)
+        self.out = torch.empty_like(self.w.q)
+
+    def quantize(self):
+        f = self.nk.fp8_kv_quantize if self.fp8 else self.nk.nvfp4_kv_quantize
+        f(self.k_new, self.v_new, self.slots_new, self.w.kp, self.w.vp)
+
+    def partial(self):
+        f = self.nk.fp8_paged_decode_partial if self.fp8 else self.nk.nvfp4_paged_decode_partial
+        f(self.w.q, self.w.kp, self.w.vp, self.w.bt, self.w.sl, self.wl.sm_scale, self.S,
+          variant=self.variant, workspace=self.ws)
+
+    def merge(self):
+        scale = self.w.vp.scale if self.fp8 else self.w.vp.global_scale
+        self.nk.nvfp4kv_lse_merge(self.ws, self.wl.batch, self.wl.num_q_heads, self.wl.head_dim, self.S,
+                                  scale, self.out)
+
+    def step(self):
+        self.quantize()
+        self.partial()
+        self.merge()
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def time_partial(self, launches):
+        """Mean duration of the decode-partial kernel, HIP events on its stream."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        self.partial()
+        for a, b in ev:
+            a.record(stream)
+            self.partial()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        return sum(ms) / len(ms) / 1e3, min(ms) / 1e3
+
+    def free(self):
+        del self.w, self.ws, self.out
+        self.torch.cuda.empty_cache()
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle (dequantize + fp64 attention) on (sequence, KV head) slices of
+    the workload, single-threaded, until ~budget_s of work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import attention as oatt
+    from oracle import nvfp4 as onv
+
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    gain_k = synth.outlier_mask(rng, 1, wl.head_dim) if wl.outliers else None
+    gain_v = synth.outlier_mask(rng, 1, wl.head_dim) if wl.outliers else None
+    caches = []
+    for _ in range(2):                                # two distinct slices, quantized before timing
+        kb = synth.host_values(rng, (wl.context, 1, wl.head_dim), gain_k)
+        vb = synth.host_values(rng, (wl.context, 1, wl.head_dim), gain_v)
+        caches.append(onv.quantize_rows(kb) + onv.quantize_rows(vb))
+    slices, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        while elapsed < budget_s and slices < 10000:
+            kd, ks, vd, vs = caches[slices % len(caches)]
+            qb = synth.host_values(rng, (wl.group, wl.head_dim))
+            t = time.perf_counter()
+            kh = onv.dequant_rows(kd, ks)
+            vh = onv.dequant_rows(vd, vs)
+            oatt.decode_heads(onv.bf16_to_f64(qb), kh, vh, wl.sm_scale)
+            elapsed += time.perf_counter() - t
+            slices += 1
+    per_slice = wl.context * (wl.head_dim // 2 + wl.head_dim // 16) * 2
+    gbs = slices * per_slice / elapsed / 1e9
+    step_bytes = kv_bytes(wl)
+    return {
+        "value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{slices} (sequence, KV head) slices of {wl.name}: oracle NVFP4 dequantize + float64 "
+                  f"softmax attention of {wl.group} query heads over {wl.context} tokens each, "
+                  f"{elapsed:.1f}s on 1 thread (BLAS limited to 1)",
+        "steps_per_s": round(gbs * 1e9 / step_bytes, 6),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--variant", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--only", choices=["nvfp4", "all"], default="all",
+                    help="nvfp4: only the headline NVFP4 step (for profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path runs on a single "
+              f"MI355X; see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_quantized_paged_amd as nk
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    nk.lib()
+    variant = {"auto": nk.VARIANT_AUTO, "valu": nk.VARIANT_VALU, "mfma": nk.VARIANT_MFMA}[args.variant]
+    wl = synth.WORKLOADS[3]
+
+    nv = Bench(nk, wl, False, variant)
+    t_step = nv.time_steps(args.steps, args.warmup)
+    t_part, t_part_min = nv.time_partial(max(10, args.steps))
+    log(f"[bench] nvfp4 step {t_step * 1e3:.3f} ms, partial mean {t_part * 1e3:.3f} ms min {t_part_min * 1e3:.3f} ms")
+    S = nv.S
+    nv.free()
+
+    kvb = kv_bytes(wl)
+    result = {
+        "metric": METRIC,
+        "value": round(kvb / t_step / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if args.variant == "valu" else "f16 (MFMA, f32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: batch {wl.batch}, {wl.num_q_heads} q / {wl.num_kv_heads} kv heads, "
+                               f"head_dim {wl.head_dim}, context {wl.context}, page {wl.page_size}, "
+                               f"{S} splits, 2% outlier channels x20, NVFP4 KV (E2M1 + E4M3/16, global scale 1.0)",
+                   "batch": wl.batch, "context": wl.context, "num_splits": S},
+        "steps_per_s": round(1.0 / t_step, 2),
+        "hbm_roofline_frac": round((kvb + io_bytes(wl)) / t_step / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    alg = kvb + wl.batch * wl.num_q_heads * wl.head_dim * 2 + partial_bytes(wl, S)
+    achieved = alg / t_part / 1e9
+    result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_partial_nvfp4_32k"),
+                          "kernel": "decode_partial (NVFP4)", "algorithmic_bytes_per_launch": alg,
+                          "mean_launch_ms": round(t_part * 1e3, 4)}
+
+    if args.only == "all":
+        f8 = Bench(nk, wl, True, variant)
+        t8 = f8.time_steps(args.steps, args.warmup)
+        f8.free()
+        result["fp8"] = {"ms_per_step": round(t8 * 1e3, 4), "steps_per_s": round(1.0 / t8, 2),
+                         "kv_gbs": round(kv_bytes(wl, True) / t8 / 1e9, 2),
+                         "hbm_roofline_frac": round((kv_bytes(wl, True) + io_bytes(wl)) / t8 / 1e9 / HBM_PEAK_GBS, 4)}
+        result["nvfp4_over_fp8_steps"] = round(t8 / t_step, 3)
+        log(f"[bench] fp8 step {t8 * 1e3:.3f} ms")
+
+        wl4 = synth.WORKLOADS[4]
+        b4 = Bench(nk, wl4, False, variant)
+        t4 = b4.time_steps(max(5, args.steps // 2), args.warmup)
+        b4.free()
+        result["extreme_context_1m"] = {
+            "ms_per_step": round(t4 * 1e3, 4), "steps_per_s": round(1.0 / t4, 2),
+            "kv_gbs": round(kv_bytes(wl4) / t4 / 1e9, 2),
+            "hbm_roofline_frac": round((kv_bytes(wl4) + io_bytes(wl4)) / t4 / 1e9 / HBM_PEAK_GBS, 4),
+            "num_splits": wl4.num_splits}
+        log(f"[bench] 1m step {t4 * 1e3:.3f} ms")
+
+    if not args.no_cpu_baseline:
+        t = time.time()
+        result["cpu_baseline"] = cpu_baseline(wl)
+        log(f"[bench] cpu baseline {time.time() - t:.1f}s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,244 @@
+/*
+ * nvfp4kv.h -- C ABI of the MI355X (gfx950) NVFP4 paged KV-cache library.
+ *
+ * The operations follow "Accelerating Long-Context and Agentic Inference with
+ * NVFP4 KV Cache" (papercache summary of the LMSYS / SGLang / Qwen / NVIDIA
+ * blog, 2026-09-16):
+ *   - section A3: NVFP4 = 4-bit E2M1 values, one FP8 E4M3 scale per block of
+ *     16 values, one FP32 tensor-level scale;
+ *   - section A2, paths 1 and 2: new K/V are quantized and written into the
+ *     persistent paged NVFP4 pool (quantize-on-write);
+ *   - section A2, path 2: the cached prefix is gathered from the pool,
+ *     dequantized and written into a workspace read by extend attention;
+ *   - section A2, path 3 and Fig. 3: decode attention reads the packed cache
+ *     and its block scales, unpacks E2M1 pairs in registers, applies the block
+ *     scale, and applies the tensor-level K/V scales as scaling parameters of
+ *     the two attention products;
+ *   - sections A3/A4: the FP8-E4M3 KV cache is the comparison baseline.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers named as device buffers are device memory of the current
+ *    HIP device. The caller owns every buffer; the library never allocates,
+ *    frees or keeps a pointer after returning.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued asynchronously on it; no entry point synchronizes.
+ *  - Concurrent calls are allowed on different streams if they write
+ *    different buffers. The only global state is a thread-local error text.
+ *  - Every entry point validates its arguments on the host before any HIP
+ *    call and returns 0 on success or a negative NVFP4KV_E* code; the text
+ *    of the last failure on the calling thread is nvfp4kv_last_error().
+ *    No C++ exception crosses the ABI.
+ *  - Data-dependent contract violations cannot be checked on the host and
+ *    are undefined behaviour: block-table entries >= num_pages, seq_len or
+ *    prefix_len > max_pages_per_seq * page_size, slots outside the pool, or
+ *    two tokens of one call mapping to the same slot.
+ *  - bf16 tensors are IEEE bfloat16 bit patterns (uint16). Base pointers of
+ *    packed/bf16 buffers must be 16-byte aligned (128-bit accesses).
+ *  - Supported shapes: head_dim 64 or 128; page_size a positive multiple of
+ *    16; num_q_heads a multiple of num_kv_heads with a group of at most 16.
+ *
+ * NVFP4 paged pool layout (one pool each for K and V)
+ *   data  [num_pages][num_kv_heads][page_size][head_dim/2]  uint8
+ *         byte i of a token row holds channels 2i (low nibble) and 2i+1
+ *         (high nibble) as E2M1 codes (bit 3 = sign);
+ *   scale [num_pages][num_kv_heads][page_size][head_dim/16] uint8
+ *         OCP E4M3FN block scale of channels [16j, 16j+16) of the token row.
+ *   A token's physical slot is page * page_size + position within the page.
+ *   Dequantized value = e2m1(code) * e4m3(scale) * global_scale.
+ *   Bytes per token per head: head_dim/2 + head_dim/16 = 0.5625 * head_dim,
+ *   the (8 + 1) / 16 ratio of the page's storage equation (section A2).
+ *
+ * FP8 paged pool layout
+ *   data  [num_pages][num_kv_heads][page_size][head_dim] uint8 (OCP E4M3FN),
+ *   value = e4m3(byte) * scale.
+ */
+#ifndef NVFP4KV_H
+#define NVFP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4KV_ABI_VERSION 1
+
+/* Return codes. */
+#define NVFP4KV_OK 0
+#define NVFP4KV_EINVAL (-1)      /* null pointer, negative or inconsistent size */
+#define NVFP4KV_EUNSUPPORTED (-2) /* head_dim, page_size or group not supported */
+#define NVFP4KV_EALIGN (-3)      /* a buffer or stride breaks 16-byte alignment */
+#define NVFP4KV_EWORKSPACE (-4)  /* decode workspace smaller than required */
+#define NVFP4KV_ELAUNCH (-5)     /* the HIP runtime reported an error at launch */
+
+/* Decode kernel variants (argument `variant` of the *_decode_partial calls). */
+#define NVFP4KV_VARIANT_AUTO 0   /* the library's choice (the MFMA kernel when built) */
+#define NVFP4KV_VARIANT_VALU 1   /* fp32 vector-ALU dot products, one wave per work item */
+#define NVFP4KV_VARIANT_MFMA 2   /* f16 matrix-core products (gfx950 MFMA) */
+
+typedef struct {
+  int32_t num_pages;    /* pages in the pool */
+  int32_t page_size;    /* tokens per page (P) */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* d */
+} nvfp4kv_geom;
+
+/* One NVFP4 pool (K or V). */
+typedef struct {
+  uint8_t* data;        /* device [num_pages][Hkv][P][d/2] */
+  uint8_t* scale;       /* device [num_pages][Hkv][P][d/16] */
+  float global_scale;   /* FP32 tensor-level dequantization multiplier (1.0 on the pages, section A7) */
+} nvfp4kv_cache;
+
+/* One FP8-E4M3 pool (K or V). */
+typedef struct {
+  uint8_t* data;        /* device [num_pages][Hkv][P][d] */
+  float scale;          /* per-tensor dequantization multiplier */
+} fp8kv_cache;
+
+/*
+ * nvfp4_kv_quantize -- quantize-on-write of new K and V into the NVFP4 pools
+ * (section A2, paths 1 and 2).
+ *
+ *   k, v          device bf16; element (t, h, c) at [t * src_token_stride + h * d + c]
+ *   src_token_stride  elements between consecutive tokens (>= Hkv * d, multiple of 8)
+ *   num_tokens    T >= 0 (0 is a no-op)
+ *   slot_mapping  device int64 [T]; slot of token t, or < 0 to skip the token
+ *   k_cache, v_cache  the two pools (data and scale are written at the slots)
+ *
+ * Per token, head and 16-channel block with amax = max|x|:
+ *   S = E4M3(amax / (6 * global_scale)), rounded to nearest even, saturating
+ *   at 448; each element gets the E2M1 code nearest to |x| / (S * global_scale),
+ *   ties to the even code, saturating at 6 (S == 0 gives magnitude 0); the
+ *   sign bit is always kept. For a global_scale that is a power of two the
+ *   result is bit-exact against that definition.
+ * Nothing outside the addressed slots is written; shared (aliased) pages are
+ * never touched unless a slot names them.
+ */
+int nvfp4_kv_quantize(const nvfp4kv_geom* geom, const void* k, const void* v,
+                      int64_t src_token_stride, int32_t num_tokens,
+                      const int64_t* slot_mapping, const nvfp4kv_cache* k_cache,
+                      const nvfp4kv_cache* v_cache, void* stream);
+
+/*
+ * nvfp4_kv_dequant_workspace -- gather and dequantize cached prefixes into a
+ * bf16 workspace for extend / chunked-prefill attention (section A2, path 2).
+ *
+ *   block_tables    device int32 [batch][max_pages_per_seq]; logical page -> physical page
+ *   prefix_lens     device int32 [batch]; tokens [0, prefix_len) of each sequence
+ *   ws_row_offsets  device int64 [batch + 1], non-decreasing; sequence b owns
+ *                   workspace rows [ws_row_offsets[b], ws_row_offsets[b+1]) and
+ *                   its prefix goes to the first prefix_len of them (the rest,
+ *                   e.g. the current chunk's rows, are left untouched)
+ *   k_ws, v_ws      device bf16 [ws_row_offsets[batch]][Hkv][d]
+ * Row off_b + t receives e2m1 * S * global_scale of token t, rounded to bf16
+ * (exact when global_scale is a power of two: every E2M1 x E4M3 product is a
+ * bf16 value). Requires prefix_len <= ws_row_offsets[b+1] - ws_row_offsets[b].
+ */
+int nvfp4_kv_dequant_workspace(const nvfp4kv_geom* geom, const nvfp4kv_cache* k_cache,
+                               const nvfp4kv_cache* v_cache, const int32_t* block_tables,
+                               int32_t max_pages_per_seq, const int32_t* prefix_lens,
+                               const int64_t* ws_row_offsets, int32_t batch, void* k_ws,
+                               void* v_ws, void* stream);
+
+/*
+ * Split-KV decode. Each (sequence b, KV head g, split j) item attends the G =
+ * num_q_heads / Hkv query heads h = g*G .. g*G+G-1 to the tokens
+ * [j*C, min(L_b, (j+1)*C)) with C = ceil(ceil(L_b / num_splits) / P) * P
+ * (page-aligned), producing an unnormalised partial (m, l, o[d]); a second
+ * kernel merges the splits by log-sum-exp. Query head h reads KV head h / G.
+ *
+ * nvfp4_paged_decode_num_splits -- the library's split count for a batch when
+ *   the caller passes num_splits = 0 (depends on sizes only: fills the GPU
+ *   with >= ~2048 work items, at most one split per 256 tokens of the
+ *   longest possible sequence, max_pages_per_seq * page_size).
+ * nvfp4_paged_decode_workspace_bytes -- bytes of the fp32 partials:
+ *   batch * num_q_heads * num_splits * (head_dim + 2) * 4.
+ */
+int32_t nvfp4_paged_decode_num_splits(int32_t batch, int32_t num_kv_heads,
+                                      int32_t max_pages_per_seq, int32_t page_size);
+size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                          int32_t head_dim, int32_t num_splits);
+
+/*
+ * nvfp4_paged_decode_attn -- decode attention over the NVFP4 pools
+ * (section A2, path 3): out[b][h] = sum_t softmax_t(sm_scale * q.k_t) v_t over
+ * t < seq_lens[b], with k_t, v_t dequantized in registers.
+ *
+ *   q            device bf16 [batch][num_q_heads][d]
+ *   block_tables device int32 [batch][max_pages_per_seq]
+ *   seq_lens     device int32 [batch]; 0 gives an all-zero output row
+ *   sm_scale     softmax scale (1/sqrt(d) in the pages' models)
+ *   num_splits   1..4096, or 0 for nvfp4_paged_decode_num_splits(...)
+ *   workspace    device, >= nvfp4_paged_decode_workspace_bytes(...) bytes
+ *   out          device bf16 [batch][num_q_heads][d], rounded to nearest even
+ * The K global scale multiplies the logits and the V global scale multiplies
+ * the output (the page's "BMM scale parameters"). Pages may be shared by
+ * several sequences (prefix aliasing); the cache is only read.
+ */
+int nvfp4_paged_decode_attn(const nvfp4kv_geom* geom, const void* q,
+                            const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                            const int32_t* block_tables, int32_t max_pages_per_seq,
+                            const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                            float sm_scale, int32_t num_splits, void* workspace,
+                            size_t workspace_bytes, void* out, void* stream);
+
+/*
+ * nvfp4_paged_decode_partial -- phase 1 only: writes the partials of every
+ * (b, h, split) into `workspace` (layout: fp32 o [batch][Hq][num_splits][d]
+ * followed by fp32 (m, l) [batch][Hq][num_splits][2]; m is in base-2 logit
+ * units, l = sum of 2^(logit2 - m); an empty split has m = -inf, l = 0).
+ * `variant` selects the kernel (NVFP4KV_VARIANT_*). num_splits must be >= 1.
+ */
+int nvfp4_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,
+                               const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                               const int32_t* block_tables, int32_t max_pages_per_seq,
+                               const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                               float sm_scale, int32_t num_splits, int32_t variant,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4kv_lse_merge -- phase 2: for each (b, h), M = max m_j over non-empty
+ * splits, out = out_scale * sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j,
+ * rounded to bf16 (zeros when every split is empty). out_scale is the V
+ * global scale (or FP8 v scale).
+ */
+int nvfp4kv_lse_merge(const void* workspace, size_t workspace_bytes, int32_t batch,
+                      int32_t num_q_heads, int32_t head_dim, int32_t num_splits,
+                      float out_scale, void* out, void* stream);
+
+/*
+ * FP8-E4M3 baseline (sections A3/A4: the fp8_e4m3 KV cache the pages compare
+ * against). Same arguments and semantics as the NVFP4 calls, with one byte
+ * per element: byte = E4M3(fl32(x / scale)), nearest even, saturating to +-448.
+ */
+int fp8_kv_quantize(const nvfp4kv_geom* geom, const void* k, const void* v,
+                    int64_t src_token_stride, int32_t num_tokens, const int64_t* slot_mapping,
+                    const fp8kv_cache* k_cache, const fp8kv_cache* v_cache, void* stream);
+
+int fp8_paged_decode_attn(const nvfp4kv_geom* geom, const void* q, const fp8kv_cache* k_cache,
+                          const fp8kv_cache* v_cache, const int32_t* block_tables,
+                          int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                          int32_t num_q_heads, float sm_scale, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+int fp8_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,
+                             const fp8kv_cache* k_cache, const fp8kv_cache* v_cache,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                             float sm_scale, int32_t num_splits, int32_t variant,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text of the last non-zero return on the calling thread ("" if none). */
+const char* nvfp4kv_last_error(void);
+
+/* NVFP4KV_ABI_VERSION of the built library. */
+int nvfp4kv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4KV_H */

@@ -1,0 +1,321 @@
+"""Python binding of libnvfp4kv, the gfx950 NVFP4 paged KV-cache library.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libnvfp4kv.so (built in-tree by ``nvfp4_quantized_paged_amd.build``). torch
+supplies device memory and the current HIP stream. There is no fallback: if
+the library is missing or a call fails, an exception is raised.
+
+torch is imported before the library is loaded: torch ships its own HIP
+runtime (soname libamdhip64.so.7), and loading it first makes the library
+bind to that same runtime, so torch's stream handles are valid here.
+
+Function names and argument meanings follow include/nvfp4kv.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4kv.so")
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4, -5
+VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
+
+c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("num_pages", c_i32), ("page_size", c_i32), ("num_kv_heads", c_i32), ("head_dim", c_i32)]
+
+
+class NVFP4CacheDesc(ctypes.Structure):
+    _fields_ = [("data", c_vp), ("scale", c_vp), ("global_scale", c_f32)]
+
+
+class FP8CacheDesc(ctypes.Structure):
+    _fields_ = [("data", c_vp), ("scale", c_f32)]
+
+
+P_GEOM, P_NV, P_F8 = ctypes.POINTER(Geom), ctypes.POINTER(NVFP4CacheDesc), ctypes.POINTER(FP8CacheDesc)
+
+_SIGNATURES = {
+    "nvfp4kv_abi_version": (ctypes.c_int, []),
+    "nvfp4kv_last_error": (ctypes.c_char_p, []),
+    "nvfp4_paged_decode_num_splits": (c_i32, [c_i32, c_i32, c_i32, c_i32]),
+    "nvfp4_paged_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32]),
+    "nvfp4_kv_quantize": (ctypes.c_int, [P_GEOM, c_vp, c_vp, c_i64, c_i32, c_vp, P_NV, P_NV, c_vp]),
+    "fp8_kv_quantize": (ctypes.c_int, [P_GEOM, c_vp, c_vp, c_i64, c_i32, c_vp, P_F8, P_F8, c_vp]),
+    "nvfp4_kv_dequant_workspace": (ctypes.c_int, [P_GEOM, P_NV, P_NV, c_vp, c_i32, c_vp, c_vp, c_i32,
+                                                  c_vp, c_vp, c_vp]),
+    "nvfp4_paged_decode_attn": (ctypes.c_int, [P_GEOM, c_vp, P_NV, P_NV, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                               c_f32, c_i32, c_vp, c_size, c_vp, c_vp]),
+    "nvfp4_paged_decode_partial": (ctypes.c_int, [P_GEOM, c_vp, P_NV, P_NV, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                                  c_f32, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "fp8_paged_decode_attn": (ctypes.c_int, [P_GEOM, c_vp, P_F8, P_F8, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                             c_f32, c_i32, c_vp, c_size, c_vp, c_vp]),
+    "fp8_paged_decode_partial": (ctypes.c_int, [P_GEOM, c_vp, P_F8, P_F8, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                                c_f32, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "nvfp4kv_lse_merge": (ctypes.c_int, [c_vp, c_size, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_vp]),
+}
+
+_lib_handle = None
+
+
+class NVFP4KVError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+def lib():
+    """The loaded ctypes library (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m nvfp4_quantized_paged_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib_handle = handle
+    return _lib_handle
+
+
+def last_error() -> str:
+    return lib().nvfp4kv_last_error().decode()
+
+
+def abi_version() -> int:
+    return lib().nvfp4kv_abi_version()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise NVFP4KVError(rc, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_vp(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# pools
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class NVFP4Pool:
+    """One paged NVFP4 pool (K or V): data [pages][Hkv][P][d/2], scale [pages][Hkv][P][d/16]."""
+
+    data: torch.Tensor
+    scale: torch.Tensor
+    global_scale: float = 1.0
+
+    @staticmethod
+    def empty(num_pages, num_kv_heads, page_size, head_dim, device="cuda", global_scale=1.0):
+        return NVFP4Pool(
+            torch.empty((num_pages, num_kv_heads, page_size, head_dim // 2), dtype=torch.uint8, device=device),
+            torch.empty((num_pages, num_kv_heads, page_size, head_dim // 16), dtype=torch.uint8, device=device),
+            global_scale)
+
+    @property
+    def geom(self) -> Geom:
+        n, h, p, half = self.data.shape
+        return Geom(n, p, h, 2 * half)
+
+    def desc(self) -> NVFP4CacheDesc:
+        _need(self.data, torch.uint8, "pool data")
+        _need(self.scale, torch.uint8, "pool scale")
+        return NVFP4CacheDesc(self.data.data_ptr(), self.scale.data_ptr(), self.global_scale)
+
+
+@dataclasses.dataclass
+class FP8Pool:
+    """One paged FP8-E4M3 pool: data [pages][Hkv][P][d] uint8, per-tensor scale."""
+
+    data: torch.Tensor
+    scale: float = 1.0
+
+    @staticmethod
+    def empty(num_pages, num_kv_heads, page_size, head_dim, device="cuda", scale=1.0):
+        return FP8Pool(torch.empty((num_pages, num_kv_heads, page_size, head_dim), dtype=torch.uint8,
+                                   device=device), scale)
+
+    @property
+    def geom(self) -> Geom:
+        n, h, p, d = self.data.shape
+        return Geom(n, p, h, d)
+
+    def desc(self) -> FP8CacheDesc:
+        _need(self.data, torch.uint8, "pool data")
+        return FP8CacheDesc(self.data.data_ptr(), self.scale)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def _quantize(fn, k, v, slot_mapping, k_pool, v_pool, stream):
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError(f"{name} must be a bf16 device tensor")
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [T][Hkv][d]")
+        if t.shape[0] > 0 and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
+            raise ValueError(f"{name} must be [T][Hkv][d] with dense heads")
+    g = k_pool.geom
+    if k.shape[0] == 0:
+        stride = g.num_kv_heads * g.head_dim
+    else:
+        if k.stride(0) != v.stride(0):
+            raise ValueError("k and v must share a token stride")
+        stride = k.stride(0)
+    _check(fn(ctypes.byref(g), k.data_ptr(), v.data_ptr(), stride, k.shape[0],
+              slot_mapping.data_ptr(), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()),
+              _stream(stream)))
+
+
+def nvfp4_kv_quantize(k, v, slot_mapping, k_pool: NVFP4Pool, v_pool: NVFP4Pool, stream=None):
+    """Quantize-on-write of k, v [T][Hkv][d] (bf16) into the pools at slot_mapping [T] (int64)."""
+    _quantize(lib().nvfp4_kv_quantize, k, v, slot_mapping, k_pool, v_pool, stream)
+
+
+def fp8_kv_quantize(k, v, slot_mapping, k_pool: FP8Pool, v_pool: FP8Pool, stream=None):
+    _quantize(lib().fp8_kv_quantize, k, v, slot_mapping, k_pool, v_pool, stream)
+
+
+def nvfp4_kv_dequant_workspace(k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables, prefix_lens,
+                               ws_row_offsets, k_ws, v_ws, stream=None):
+    """Dequantize prefixes [0, prefix_lens[b]) into rows ws_row_offsets[b].. of k_ws, v_ws ([rows][Hkv][d] bf16)."""
+    _need(block_tables, torch.int32, "block_tables")
+    _need(prefix_lens, torch.int32, "prefix_lens")
+    _need(ws_row_offsets, torch.int64, "ws_row_offsets")
+    _need(k_ws, torch.bfloat16, "k_ws")
+    _need(v_ws, torch.bfloat16, "v_ws")
+    g = k_pool.geom
+    _check(lib().nvfp4_kv_dequant_workspace(
+        ctypes.byref(g), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()), block_tables.data_ptr(),
+        block_tables.shape[1], prefix_lens.data_ptr(), ws_row_offsets.data_ptr(), prefix_lens.shape[0],
+        k_ws.data_ptr(), v_ws.data_ptr(), _stream(stream)))
+
+
+def nvfp4_paged_decode_num_splits(batch, num_kv_heads, max_pages_per_seq, page_size) -> int:
+    return lib().nvfp4_paged_decode_num_splits(batch, num_kv_heads, max_pages_per_seq, page_size)
+
+
+def nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits) -> int:
+    return lib().nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits)
+
+
+def decode_workspace(batch, num_q_heads, head_dim, num_splits, device="cuda") -> torch.Tensor:
+    n = nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _decode_args(q, block_tables, seq_lens):
+    _need(q, torch.bfloat16, "q")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, Hq, d = q.shape
+    return B, Hq, d
+
+
+def _resolve_splits(num_splits, B, pool_geom, max_pages):
+    if num_splits == 0:
+        return nvfp4_paged_decode_num_splits(B, pool_geom.num_kv_heads, max_pages, pool_geom.page_size)
+    return num_splits
+
+
+def _decode(fn_name, pool_cls_desc, q, k_pool, v_pool, block_tables, seq_lens, sm_scale, num_splits,
+            workspace, out, stream):
+    B, Hq, d = _decode_args(q, block_tables, seq_lens)
+    g = k_pool.geom
+    splits = _resolve_splits(num_splits, B, g, block_tables.shape[1])
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, d, splits, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.bfloat16, "out")
+    _check(getattr(lib(), fn_name)(
+        ctypes.byref(g), q.data_ptr(), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()),
+        block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(), B, Hq, float(sm_scale),
+        splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(), out.data_ptr(),
+        _stream(stream)))
+    return out
+
+
+def _partial(fn_name, q, k_pool, v_pool, block_tables, seq_lens, sm_scale, num_splits, variant, workspace,
+             stream):
+    B, Hq, d = _decode_args(q, block_tables, seq_lens)
+    g = k_pool.geom
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, d, num_splits, q.device)
+    _check(getattr(lib(), fn_name)(
+        ctypes.byref(g), q.data_ptr(), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()),
+        block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(), B, Hq, float(sm_scale),
+        num_splits, variant, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return workspace
+
+
+def nvfp4_paged_decode_attn(q, k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables, seq_lens, sm_scale,
+                            num_splits=0, workspace=None, out=None, stream=None):
+    """Decode attention of q [B][Hq][d] (bf16) over the NVFP4 pools; returns out [B][Hq][d] bf16."""
+    return _decode("nvfp4_paged_decode_attn", None, q, k_pool, v_pool, block_tables, seq_lens, sm_scale,
+                   num_splits, workspace, out, stream)
+
+
+def fp8_paged_decode_attn(q, k_pool: FP8Pool, v_pool: FP8Pool, block_tables, seq_lens, sm_scale,
+                          num_splits=0, workspace=None, out=None, stream=None):
+    return _decode("fp8_paged_decode_attn", None, q, k_pool, v_pool, block_tables, seq_lens, sm_scale,
+                   num_splits, workspace, out, stream)
+
+
+def nvfp4_paged_decode_partial(q, k_pool, v_pool, block_tables, seq_lens, sm_scale, num_splits,
+                               variant=VARIANT_AUTO, workspace=None, stream=None):
+    return _partial("nvfp4_paged_decode_partial", q, k_pool, v_pool, block_tables, seq_lens, sm_scale,
+                    num_splits, variant, workspace, stream)
+
+
+def fp8_paged_decode_partial(q, k_pool, v_pool, block_tables, seq_lens, sm_scale, num_splits,
+                             variant=VARIANT_AUTO, workspace=None, stream=None):
+    return _partial("fp8_paged_decode_partial", q, k_pool, v_pool, block_tables, seq_lens, sm_scale,
+                    num_splits, variant, workspace, stream)
+
+
+def nvfp4kv_lse_merge(workspace, batch, num_q_heads, head_dim, num_splits, out_scale, out, stream=None):
+    _need(out, torch.bfloat16, "out")
+    _check(lib().nvfp4kv_lse_merge(workspace.data_ptr(), workspace.numel() * workspace.element_size(), batch,
+                                   num_q_heads, head_dim, num_splits, float(out_scale), out.data_ptr(),
+                                   _stream(stream)))
+    return out
+
+
+def split_partials(workspace: torch.Tensor, batch, num_q_heads, head_dim, num_splits):
+    """Views (o [B][Hq][S][d], ml [B][Hq][S][2]) of a decode workspace's fp32 partials."""
+    f = workspace.view(torch.float32)
+    n = batch * num_q_heads * num_splits * head_dim
+    o = f[:n].view(batch, num_q_heads, num_splits, head_dim)
+    ml = f[n:n + batch * num_q_heads * num_splits * 2].view(batch, num_q_heads, num_splits, 2)
+    return o, ml

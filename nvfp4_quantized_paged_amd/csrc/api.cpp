@@ -1,0 +1,411 @@
+// C ABI of libnvfp4kv: host-side argument validation and kernel launches.
+//
+// Every entry point validates its arguments on the host, before any HIP
+// call, so each error path can be exercised without a GPU. The operations
+// and their sources are documented in include/nvfp4kv.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/nvfp4kv.h"
+#include "common.hpp"
+
+#define NVFP4KV_API extern "C" __attribute__((visibility("default")))
+
+using namespace nvfp4kv;
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int kMaxSplits = 4096;
+constexpr int kMaxGroup = 16;
+constexpr int kGridYZ = 65535;
+
+int check_geom(const nvfp4kv_geom* g, const char* fn) {
+  if (!g) return fail(NVFP4KV_EINVAL, "%s: geom is NULL", fn);
+  if (g->num_pages <= 0 || g->page_size <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0)
+    return fail(NVFP4KV_EINVAL, "%s: geometry sizes must be positive (pages %d, page_size %d, kv_heads %d, head_dim %d)",
+                fn, g->num_pages, g->page_size, g->num_kv_heads, g->head_dim);
+  if (g->head_dim != 64 && g->head_dim != 128)
+    return fail(NVFP4KV_EUNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, g->head_dim);
+  if (g->page_size % 16 != 0)
+    return fail(NVFP4KV_EUNSUPPORTED, "%s: page_size %d is not a multiple of 16", fn, g->page_size);
+  if (g->num_kv_heads > kGridYZ)
+    return fail(NVFP4KV_EUNSUPPORTED, "%s: num_kv_heads %d too large", fn, g->num_kv_heads);
+  return NVFP4KV_OK;
+}
+
+int check_nvfp4_cache(const nvfp4kv_cache* c, const char* name, const char* fn) {
+  if (!c) return fail(NVFP4KV_EINVAL, "%s: %s cache descriptor is NULL", fn, name);
+  if (!c->data || !c->scale) return fail(NVFP4KV_EINVAL, "%s: %s cache data/scale pointer is NULL", fn, name);
+  if (!aligned16(c->data) || !aligned16(c->scale))
+    return fail(NVFP4KV_EALIGN, "%s: %s cache buffers must be 16-byte aligned", fn, name);
+  if (!(isfinite(c->global_scale) && c->global_scale > 0.0f))
+    return fail(NVFP4KV_EINVAL, "%s: %s global_scale must be finite and > 0", fn, name);
+  return NVFP4KV_OK;
+}
+
+int check_fp8_cache(const fp8kv_cache* c, const char* name, const char* fn) {
+  if (!c) return fail(NVFP4KV_EINVAL, "%s: %s cache descriptor is NULL", fn, name);
+  if (!c->data) return fail(NVFP4KV_EINVAL, "%s: %s cache data pointer is NULL", fn, name);
+  if (!aligned16(c->data)) return fail(NVFP4KV_EALIGN, "%s: %s cache data must be 16-byte aligned", fn, name);
+  if (!(isfinite(c->scale) && c->scale > 0.0f))
+    return fail(NVFP4KV_EINVAL, "%s: %s scale must be finite and > 0", fn, name);
+  return NVFP4KV_OK;
+}
+
+int check_quantize_src(const nvfp4kv_geom* g, const void* k, const void* v, int64_t stride,
+                       int32_t num_tokens, const int64_t* slots, const char* fn) {
+  if (num_tokens < 0) return fail(NVFP4KV_EINVAL, "%s: num_tokens %d < 0", fn, num_tokens);
+  if (num_tokens == 0) return NVFP4KV_OK;
+  if (!k || !v || !slots) return fail(NVFP4KV_EINVAL, "%s: k, v and slot_mapping must be non-NULL", fn);
+  if (stride < (int64_t)g->num_kv_heads * g->head_dim)
+    return fail(NVFP4KV_EINVAL, "%s: src_token_stride %lld < num_kv_heads * head_dim", fn, (long long)stride);
+  if (!aligned16(k) || !aligned16(v) || stride % 8 != 0)
+    return fail(NVFP4KV_EALIGN, "%s: k/v must be 16-byte aligned and src_token_stride a multiple of 8", fn);
+  const int64_t items = (int64_t)num_tokens * g->num_kv_heads * (g->head_dim / kBlock);
+  if ((items + 255) / 256 > 0x7FFFFFFFLL) return fail(NVFP4KV_EINVAL, "%s: too many tokens", fn);
+  return NVFP4KV_OK;
+}
+
+struct DecodeCheck {
+  int32_t group;
+  int32_t splits;
+};
+
+int check_decode(const nvfp4kv_geom* g, const void* q, const int32_t* block_tables,
+                 int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                 float sm_scale, int32_t num_splits, bool allow_auto, void* workspace,
+                 size_t workspace_bytes, const char* fn, DecodeCheck* out) {
+  if (!q || !block_tables || !seq_lens) return fail(NVFP4KV_EINVAL, "%s: q, block_tables and seq_lens must be non-NULL", fn);
+  if (!aligned16(q)) return fail(NVFP4KV_EALIGN, "%s: q must be 16-byte aligned", fn);
+  if (batch < 0 || batch > kGridYZ) return fail(NVFP4KV_EINVAL, "%s: batch %d out of range [0, %d]", fn, batch, kGridYZ);
+  if (max_pages <= 0) return fail(NVFP4KV_EINVAL, "%s: max_pages_per_seq %d must be > 0", fn, max_pages);
+  if (num_q_heads <= 0 || num_q_heads % g->num_kv_heads != 0)
+    return fail(NVFP4KV_EINVAL, "%s: num_q_heads %d must be a positive multiple of num_kv_heads %d", fn,
+                num_q_heads, g->num_kv_heads);
+  const int32_t group = num_q_heads / g->num_kv_heads;
+  if (group > kMaxGroup) return fail(NVFP4KV_EUNSUPPORTED, "%s: query group %d > %d", fn, group, kMaxGroup);
+  if (!isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "%s: sm_scale must be finite", fn);
+  int32_t splits = num_splits;
+  if (splits == 0 && allow_auto)
+    splits = nvfp4_paged_decode_num_splits(batch, g->num_kv_heads, max_pages, g->page_size);
+  if (splits < 1 || splits > kMaxSplits)
+    return fail(NVFP4KV_EINVAL, "%s: num_splits %d out of range [1, %d]%s", fn, num_splits, kMaxSplits,
+                allow_auto ? " (0 = auto)" : "");
+  const size_t need = nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, g->head_dim, splits);
+  if (need > 0 && !workspace) return fail(NVFP4KV_EINVAL, "%s: workspace is NULL", fn);
+  if (workspace && !aligned16(workspace)) return fail(NVFP4KV_EALIGN, "%s: workspace must be 16-byte aligned", fn);
+  if (workspace_bytes < need)
+    return fail(NVFP4KV_EWORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  out->group = group;
+  out->splits = splits;
+  return NVFP4KV_OK;
+}
+
+int launched(hipError_t e, const char* fn) {
+  if (e != hipSuccess) return fail(NVFP4KV_ELAUNCH, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  g_error[0] = '\0';
+  return NVFP4KV_OK;
+}
+
+DecodeParams make_decode(const nvfp4kv_geom* g, const void* q, const uint8_t* kd, const uint8_t* ks,
+                         const uint8_t* vd, const uint8_t* vs, const int32_t* bt, int32_t max_pages,
+                         const int32_t* seq_lens, int32_t batch, int32_t hq, const DecodeCheck& c,
+                         float sm_scale, float gs_k, void* workspace) {
+  DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.kd = kd;
+  p.ks = ks;
+  p.vd = vd;
+  p.vs = vs;
+  p.block_tables = bt;
+  p.seq_lens = seq_lens;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_ml = p.part_o + (size_t)batch * hq * c.splits * g->head_dim;
+  p.max_pages = max_pages;
+  p.batch = batch;
+  p.num_q_heads = hq;
+  p.num_kv_heads = g->num_kv_heads;
+  p.group = c.group;
+  p.page_size = g->page_size;
+  p.num_splits = c.splits;
+  p.qk_scale = sm_scale * gs_k * 1.4426950408889634f;
+  return p;
+}
+
+int check_variant(int32_t variant, const char* fn) {
+  if (variant != NVFP4KV_VARIANT_AUTO && variant != NVFP4KV_VARIANT_VALU && variant != NVFP4KV_VARIANT_MFMA)
+    return fail(NVFP4KV_EINVAL, "%s: unknown variant %d", fn, variant);
+  return NVFP4KV_OK;
+}
+
+hipError_t run_partial(const DecodeParams& p, int head_dim, bool fp8, int32_t variant, hipStream_t s) {
+  if (p.batch == 0) return hipSuccess;
+  if (variant == NVFP4KV_VARIANT_VALU) return launch_decode_valu(p, head_dim, fp8, s);
+  return launch_decode_mfma(p, head_dim, fp8, s);
+}
+
+hipError_t run_merge(const DecodeParams& d, int head_dim, float out_scale, void* out, hipStream_t s) {
+  if (d.batch == 0) return hipSuccess;
+  MergeParams m{};
+  m.part_o = d.part_o;
+  m.part_ml = d.part_ml;
+  m.batch = d.batch;
+  m.num_q_heads = d.num_q_heads;
+  m.head_dim = head_dim;
+  m.num_splits = d.num_splits;
+  m.out_scale = out_scale;
+  m.out = static_cast<uint16_t*>(out);
+  return launch_lse_merge(m, s);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// exported entry points
+// ---------------------------------------------------------------------------
+
+NVFP4KV_API int nvfp4kv_abi_version(void) { return NVFP4KV_ABI_VERSION; }
+
+NVFP4KV_API const char* nvfp4kv_last_error(void) { return g_error; }
+
+NVFP4KV_API int32_t nvfp4_paged_decode_num_splits(int32_t batch, int32_t num_kv_heads,
+                                                  int32_t max_pages_per_seq, int32_t page_size) {
+  const int64_t items = (int64_t)(batch > 0 ? batch : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+  int64_t n = (2048 + items - 1) / items;
+  const int64_t max_len = (int64_t)(max_pages_per_seq > 0 ? max_pages_per_seq : 1) * (page_size > 0 ? page_size : 16);
+  const int64_t cap = (max_len + 255) / 256;
+  if (n > cap) n = cap;
+  if (n < 1) n = 1;
+  if (n > kMaxSplits) n = kMaxSplits;
+  return (int32_t)n;
+}
+
+NVFP4KV_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                                      int32_t head_dim, int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  return (size_t)batch * num_q_heads * num_splits * (head_dim + 2) * sizeof(float);
+}
+
+NVFP4KV_API int nvfp4_kv_quantize(const nvfp4kv_geom* geom, const void* k, const void* v,
+                                  int64_t src_token_stride, int32_t num_tokens,
+                                  const int64_t* slot_mapping, const nvfp4kv_cache* k_cache,
+                                  const nvfp4kv_cache* v_cache, void* stream) {
+  const char* fn = "nvfp4_kv_quantize";
+  int rc;
+  if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
+      (rc = check_nvfp4_cache(v_cache, "V", fn)) ||
+      (rc = check_quantize_src(geom, k, v, src_token_stride, num_tokens, slot_mapping, fn)))
+    return rc;
+  if (num_tokens == 0) return launched(hipSuccess, fn);
+  QuantizeParams p{};
+  p.src[0] = static_cast<const uint16_t*>(k);
+  p.src[1] = static_cast<const uint16_t*>(v);
+  p.src_stride = src_token_stride;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = geom->num_kv_heads;
+  p.head_dim = geom->head_dim;
+  p.page_size = geom->page_size;
+  p.data[0] = k_cache->data;
+  p.data[1] = v_cache->data;
+  p.scale[0] = k_cache->scale;
+  p.scale[1] = v_cache->scale;
+  p.gscale[0] = k_cache->global_scale;
+  p.gscale[1] = v_cache->global_scale;
+  return launched(launch_nvfp4_quantize(p, static_cast<hipStream_t>(stream)), fn);
+}
+
+NVFP4KV_API int fp8_kv_quantize(const nvfp4kv_geom* geom, const void* k, const void* v,
+                                int64_t src_token_stride, int32_t num_tokens,
+                                const int64_t* slot_mapping, const fp8kv_cache* k_cache,
+                                const fp8kv_cache* v_cache, void* stream) {
+  const char* fn = "fp8_kv_quantize";
+  int rc;
+  if ((rc = check_geom(geom, fn)) || (rc = check_fp8_cache(k_cache, "K", fn)) ||
+      (rc = check_fp8_cache(v_cache, "V", fn)) ||
+      (rc = check_quantize_src(geom, k, v, src_token_stride, num_tokens, slot_mapping, fn)))
+    return rc;
+  if (num_tokens == 0) return launched(hipSuccess, fn);
+  QuantizeParams p{};
+  p.src[0] = static_cast<const uint16_t*>(k);
+  p.src[1] = static_cast<const uint16_t*>(v);
+  p.src_stride = src_token_stride;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = geom->num_kv_heads;
+  p.head_dim = geom->head_dim;
+  p.page_size = geom->page_size;
+  p.data[0] = k_cache->data;
+  p.data[1] = v_cache->data;
+  p.gscale[0] = k_cache->scale;
+  p.gscale[1] = v_cache->scale;
+  return launched(launch_fp8_quantize(p, static_cast<hipStream_t>(stream)), fn);
+}
+
+NVFP4KV_API int nvfp4_kv_dequant_workspace(const nvfp4kv_geom* geom, const nvfp4kv_cache* k_cache,
+                                           const nvfp4kv_cache* v_cache, const int32_t* block_tables,
+                                           int32_t max_pages_per_seq, const int32_t* prefix_lens,
+                                           const int64_t* ws_row_offsets, int32_t batch, void* k_ws,
+                                           void* v_ws, void* stream) {
+  const char* fn = "nvfp4_kv_dequant_workspace";
+  int rc;
+  if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
+      (rc = check_nvfp4_cache(v_cache, "V", fn)))
+    return rc;
+  if (batch < 0) return fail(NVFP4KV_EINVAL, "%s: batch %d < 0", fn, batch);
+  if (batch == 0) return launched(hipSuccess, fn);
+  if (!block_tables || !prefix_lens || !ws_row_offsets || !k_ws || !v_ws)
+    return fail(NVFP4KV_EINVAL, "%s: block_tables, prefix_lens, ws_row_offsets, k_ws and v_ws must be non-NULL", fn);
+  if (max_pages_per_seq <= 0) return fail(NVFP4KV_EINVAL, "%s: max_pages_per_seq %d must be > 0", fn, max_pages_per_seq);
+  if (!aligned16(k_ws) || !aligned16(v_ws)) return fail(NVFP4KV_EALIGN, "%s: workspaces must be 16-byte aligned", fn);
+  WorkspaceParams p{};
+  p.data[0] = k_cache->data;
+  p.data[1] = v_cache->data;
+  p.scale[0] = k_cache->scale;
+  p.scale[1] = v_cache->scale;
+  p.gscale[0] = k_cache->global_scale;
+  p.gscale[1] = v_cache->global_scale;
+  p.block_tables = block_tables;
+  p.prefix_lens = prefix_lens;
+  p.row_offsets = ws_row_offsets;
+  p.max_pages = max_pages_per_seq;
+  p.batch = batch;
+  p.num_kv_heads = geom->num_kv_heads;
+  p.head_dim = geom->head_dim;
+  p.page_size = geom->page_size;
+  p.ws[0] = static_cast<uint16_t*>(k_ws);
+  p.ws[1] = static_cast<uint16_t*>(v_ws);
+  return launched(launch_nvfp4_dequant_ws(p, static_cast<hipStream_t>(stream)), fn);
+}
+
+NVFP4KV_API int nvfp4_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,
+                                           const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                                           const int32_t* block_tables, int32_t max_pages_per_seq,
+                                           const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                           float sm_scale, int32_t num_splits, int32_t variant,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "nvfp4_paged_decode_partial";
+  int rc;
+  DecodeCheck c{};
+  if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
+      (rc = check_nvfp4_cache(v_cache, "V", fn)) || (rc = check_variant(variant, fn)) ||
+      (rc = check_decode(geom, q, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads,
+                         sm_scale, num_splits, false, workspace, workspace_bytes, fn, &c)))
+    return rc;
+  const DecodeParams p = make_decode(geom, q, k_cache->data, k_cache->scale, v_cache->data, v_cache->scale,
+                                     block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, c,
+                                     sm_scale, k_cache->global_scale, workspace);
+  return launched(run_partial(p, geom->head_dim, false, variant, static_cast<hipStream_t>(stream)), fn);
+}
+
+NVFP4KV_API int nvfp4_paged_decode_attn(const nvfp4kv_geom* geom, const void* q,
+                                        const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                                        const int32_t* block_tables, int32_t max_pages_per_seq,
+                                        const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                        float sm_scale, int32_t num_splits, void* workspace,
+                                        size_t workspace_bytes, void* out, void* stream) {
+  const char* fn = "nvfp4_paged_decode_attn";
+  int rc;
+  DecodeCheck c{};
+  if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
+      (rc = check_nvfp4_cache(v_cache, "V", fn)) ||
+      (rc = check_decode(geom, q, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads,
+                         sm_scale, num_splits, true, workspace, workspace_bytes, fn, &c)))
+    return rc;
+  if (!out) return fail(NVFP4KV_EINVAL, "%s: out is NULL", fn);
+  if (!aligned16(out)) return fail(NVFP4KV_EALIGN, "%s: out must be 16-byte aligned", fn);
+  const DecodeParams p = make_decode(geom, q, k_cache->data, k_cache->scale, v_cache->data, v_cache->scale,
+                                     block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, c,
+                                     sm_scale, k_cache->global_scale, workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_partial(p, geom->head_dim, false, NVFP4KV_VARIANT_AUTO, s);
+  if (e == hipSuccess) e = run_merge(p, geom->head_dim, v_cache->global_scale, out, s);
+  return launched(e, fn);
+}
+
+NVFP4KV_API int fp8_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,
+                                         const fp8kv_cache* k_cache, const fp8kv_cache* v_cache,
+                                         const int32_t* block_tables, int32_t max_pages_per_seq,
+                                         const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                         float sm_scale, int32_t num_splits, int32_t variant,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "fp8_paged_decode_partial";
+  int rc;
+  DecodeCheck c{};
+  if ((rc = check_geom(geom, fn)) || (rc = check_fp8_cache(k_cache, "K", fn)) ||
+      (rc = check_fp8_cache(v_cache, "V", fn)) || (rc = check_variant(variant, fn)) ||
+      (rc = check_decode(geom, q, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads,
+                         sm_scale, num_splits, false, workspace, workspace_bytes, fn, &c)))
+    return rc;
+  const DecodeParams p = make_decode(geom, q, k_cache->data, nullptr, v_cache->data, nullptr, block_tables,
+                                     max_pages_per_seq, seq_lens, batch, num_q_heads, c, sm_scale,
+                                     k_cache->scale, workspace);
+  return launched(run_partial(p, geom->head_dim, true, variant, static_cast<hipStream_t>(stream)), fn);
+}
+
+NVFP4KV_API int fp8_paged_decode_attn(const nvfp4kv_geom* geom, const void* q, const fp8kv_cache* k_cache,
+                                      const fp8kv_cache* v_cache, const int32_t* block_tables,
+                                      int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                      int32_t num_q_heads, float sm_scale, int32_t num_splits,
+                                      void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const char* fn = "fp8_paged_decode_attn";
+  int rc;
+  DecodeCheck c{};
+  if ((rc = check_geom(geom, fn)) || (rc = check_fp8_cache(k_cache, "K", fn)) ||
+      (rc = check_fp8_cache(v_cache, "V", fn)) ||
+      (rc = check_decode(geom, q, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads,
+                         sm_scale, num_splits, true, workspace, workspace_bytes, fn, &c)))
+    return rc;
+  if (!out) return fail(NVFP4KV_EINVAL, "%s: out is NULL", fn);
+  if (!aligned16(out)) return fail(NVFP4KV_EALIGN, "%s: out must be 16-byte aligned", fn);
+  const DecodeParams p = make_decode(geom, q, k_cache->data, nullptr, v_cache->data, nullptr, block_tables,
+                                     max_pages_per_seq, seq_lens, batch, num_q_heads, c, sm_scale,
+                                     k_cache->scale, workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_partial(p, geom->head_dim, true, NVFP4KV_VARIANT_AUTO, s);
+  if (e == hipSuccess) e = run_merge(p, geom->head_dim, v_cache->scale, out, s);
+  return launched(e, fn);
+}
+
+NVFP4KV_API int nvfp4kv_lse_merge(const void* workspace, size_t workspace_bytes, int32_t batch,
+                                  int32_t num_q_heads, int32_t head_dim, int32_t num_splits,
+                                  float out_scale, void* out, void* stream) {
+  const char* fn = "nvfp4kv_lse_merge";
+  if (batch < 0 || batch > kGridYZ) return fail(NVFP4KV_EINVAL, "%s: batch %d out of range", fn, batch);
+  if (num_q_heads <= 0) return fail(NVFP4KV_EINVAL, "%s: num_q_heads %d must be > 0", fn, num_q_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(NVFP4KV_EUNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(NVFP4KV_EINVAL, "%s: num_splits %d out of range [1, %d]", fn, num_splits, kMaxSplits);
+  if (!(isfinite(out_scale))) return fail(NVFP4KV_EINVAL, "%s: out_scale must be finite", fn);
+  if (batch == 0) return launched(hipSuccess, fn);
+  if (!workspace || !out) return fail(NVFP4KV_EINVAL, "%s: workspace and out must be non-NULL", fn);
+  if (!aligned16(workspace) || !aligned16(out)) return fail(NVFP4KV_EALIGN, "%s: buffers must be 16-byte aligned", fn);
+  const size_t need = nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, head_dim, num_splits);
+  if (workspace_bytes < need)
+    return fail(NVFP4KV_EWORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  MergeParams m{};
+  m.part_o = static_cast<const float*>(workspace);
+  m.part_ml = m.part_o + (size_t)batch * num_q_heads * num_splits * head_dim;
+  m.batch = batch;
+  m.num_q_heads = num_q_heads;
+  m.head_dim = head_dim;
+  m.num_splits = num_splits;
+  m.out_scale = out_scale;
+  m.out = static_cast<uint16_t*>(out);
+  return launched(launch_lse_merge(m, static_cast<hipStream_t>(stream)), fn);
+}

@@ -1,0 +1,145 @@
+// Shared device helpers and internal launch interface of libnvfp4kv (gfx950).
+//
+// Format facts used here come from "Accelerating Long-Context and Agentic
+// Inference with NVFP4 KV Cache", section A3 (E2M1 elements, one E4M3 scale
+// per 16 elements, an FP32 tensor scale) and section A2 / Fig. 3 (the decode
+// kernel unpacks E2M1 pairs in registers and multiplies by the block scale).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4kv {
+
+constexpr int kBlock = 16;   // elements per E4M3 block scale
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// f32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Non-negative f32 -> OCP E4M3FN byte: nearest value, ties to even, saturating
+// at 448 (0x7E). NaN -> 0x7F. Normal range rounds the f32 mantissa to 3 bits;
+// below 2^-6 the grid is k * 2^-9 and k = rint(x * 512) (exact scaling).
+__device__ inline uint32_t e4m3_encode_nonneg(float x) {
+  if (x != x) return 0x7Fu;
+  if (!(x < 448.0f)) return 0x7Eu;
+  if (x < 0.015625f) return (uint32_t)rintf(x * 512.0f);   // 0..8 (8 = 2^-6)
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  u &= 0xFFF00000u;
+  const uint32_t e = (u >> 23) - 127u + 7u;                // 1..15
+  return (e << 3) | ((u >> 20) & 7u);
+}
+
+// OCP E4M3FN byte -> f32 (finite bytes only; 0x7F/0xFF never come from the encoder).
+__device__ inline float e4m3_to_f32(uint32_t byte) {
+  const uint32_t e = (byte >> 3) & 0xFu, m = byte & 7u;
+  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * (1.0f / 512.0f);
+  return (byte & 0x80u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------
+// gfx950 hardware conversions (scale operand 1.0: the E4M3 block scale is not a
+// power of two, so it is applied separately)
+// ---------------------------------------------------------------------------
+
+// Eight E2M1 codes of a 32-bit word (element 2i in the low nibble of byte i)
+// -> eight floats, unscaled.
+__device__ inline void fp4x8_to_f32(uint32_t w, float out[8]) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  out[0] = a[0]; out[1] = a[1]; out[2] = b[0]; out[3] = b[1];
+  out[4] = c[0]; out[5] = c[1]; out[6] = d[0]; out[7] = d[1];
+}
+
+// Four OCP E4M3 bytes of a 32-bit word (byte i = element i) -> four floats.
+__device__ inline void fp8x4_to_f32(uint32_t w, float out[4]) {
+  const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+  const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+  out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions
+// ---------------------------------------------------------------------------
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// internal launch interface (host side, defined in the .hip files)
+// ---------------------------------------------------------------------------
+
+struct QuantizeParams {
+  const uint16_t* src[2];   // K, V (bf16)
+  int64_t src_stride;       // elements between tokens
+  const int64_t* slot_mapping;
+  int32_t num_tokens, num_kv_heads, head_dim, page_size;
+  uint8_t* data[2];         // NVFP4 data or FP8 bytes
+  uint8_t* scale[2];        // NVFP4 block scales (unused for FP8)
+  float gscale[2];          // NVFP4 global scale / FP8 per-tensor scale
+};
+
+struct WorkspaceParams {
+  const uint8_t* data[2];
+  const uint8_t* scale[2];
+  float gscale[2];
+  const int32_t* block_tables;
+  const int32_t* prefix_lens;
+  const int64_t* row_offsets;
+  int32_t max_pages, batch, num_kv_heads, head_dim, page_size;
+  uint16_t* ws[2];
+};
+
+struct DecodeParams {
+  const uint16_t* q;        // [B][Hq][D] bf16
+  const uint8_t* kd;        // K data (NVFP4 packed or FP8)
+  const uint8_t* ks;        // K block scales (NVFP4 only)
+  const uint8_t* vd;
+  const uint8_t* vs;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* part_o;            // [B][Hq][S][D]
+  float* part_ml;           // [B][Hq][S][2]
+  int32_t max_pages, batch, num_q_heads, num_kv_heads, group, page_size, num_splits;
+  float qk_scale;           // sm_scale * K global scale * log2(e)
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_ml;
+  int32_t batch, num_q_heads, head_dim, num_splits;
+  float out_scale;
+  uint16_t* out;
+};
+
+hipError_t launch_nvfp4_quantize(const QuantizeParams& p, hipStream_t s);
+hipError_t launch_fp8_quantize(const QuantizeParams& p, hipStream_t s);
+hipError_t launch_nvfp4_dequant_ws(const WorkspaceParams& p, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, bool fp8, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, hipStream_t s);
+hipError_t launch_lse_merge(const MergeParams& p, hipStream_t s);
+
+}  // namespace nvfp4kv

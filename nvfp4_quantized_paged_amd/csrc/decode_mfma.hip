@@ -1,0 +1,335 @@
+// Split-KV paged decode attention on the gfx950 matrix cores (NVFP4 and FP8 caches).
+//
+// "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
+// section A2, path 3 and Fig. 3: the decode kernel streams the packed K/V
+// tiles and their E4M3 block scales, unpacks pairs of E2M1 values in
+// registers, multiplies them by the block scale with packed multiplies and
+// runs both attention products on the matrix units; the tensor-level K/V
+// scales are applied as scaling parameters of the two products. The page's
+// kernel does this in BF16 on SM120; here it is rebuilt for CDNA4:
+//
+//  * One wave64 per (split, KV head, sequence). The G query heads of the
+//    group are the 16 columns of v_mfma_f32_16x16x32_f16 (G <= 16, the rest
+//    zero), so every K/V element is unpacked once for the whole group.
+//  * Unpack: v_cvt_scalef32_pk_f16_fp4 turns one byte (two E2M1 codes) into an
+//    f16 pair (hardware scale operand 1.0: the E4M3 block scale is not a power
+//    of two), then v_pk_mul_f16 applies the block scale. Every E2M1 x E4M3
+//    product is exact in f16, so the dequantized K/V are exact.
+//  * QK: A = K (16 tokens x 32 channels per MFMA, one 128-bit load per lane
+//    covers four MFMAs: lane (row r, group g) holds channels
+//    [g*D/4, (g+1)*D/4) of token r), B = q (f16, scaled into f16 range by a
+//    power of two). C[t][h]: lane (h, g) holds tokens 4g..4g+3 of the tile.
+//  * Softmax in base 2, f32, running max and per-lane sums per head; the
+//    output accumulators are rescaled only when some head's max grows.
+//  * PV contracts over tokens, but a lane holds channels of one token. The
+//    token-major operand is made on the matrix unit: multiplying the V tile
+//    by a 0/1 selection matrix returns it transposed in the MFMA output
+//    layout (lane (c, g) = tokens 4g..4g+3 of channel c), exactly (one
+//    nonzero product per output). Two such outputs, packed to f16, are the A
+//    operand of O^T[c][h] += V^T[c][t] P[t][h], and the softmax output C of
+//    the same two tiles is already the B operand in the same lane: no
+//    cross-lane data movement anywhere in the loop.
+//  * Loads: direct 128-bit global loads into registers, one chunk (64 tokens
+//    NVFP4, 32 tokens FP8) prefetched while the previous chunk computes.
+#include "common.hpp"
+
+namespace nvfp4kv {
+
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+
+
+template <int D, bool FP8>
+struct Cfg {
+  static constexpr int kTiles = FP8 ? 2 : 4;           // 16-token tiles per chunk
+  static constexpr int kChunk = 16 * kTiles;
+  static constexpr int kRowBytes = FP8 ? D : D / 2;    // bytes of one token row
+  static constexpr int kLaneBytes = kRowBytes / 4;     // bytes per lane per tile
+  static constexpr int kLaneWords = kLaneBytes / 4;
+  static constexpr int kKSteps = D / 32;               // QK MFMAs per tile
+  static constexpr int kCTiles = D / 16;               // PV output channel tiles
+  static constexpr int kChanPerGroup = D / 4;          // channels per lane group
+};
+
+template <int D, bool FP8>
+struct TileRaw {
+  uint32_t k[Cfg<D, FP8>::kLaneWords];
+  uint32_t v[Cfg<D, FP8>::kLaneWords];
+  uint32_t ks, vs;   // NVFP4: the lane's block-scale byte(s)
+};
+
+__device__ inline float4_t mfma(const half8_t& a, const half8_t& b, const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline half2_t splat_lo(half2_t s) { return __builtin_shufflevector(s, s, 0, 0); }
+__device__ inline half2_t splat_hi(half2_t s) { return __builtin_shufflevector(s, s, 1, 1); }
+
+// Eight E2M1 codes of one word -> eight f16 values times the block scale pair s.
+__device__ inline half8_t fp4x8_scaled(uint32_t w, half2_t s) {
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight E4M3 bytes of two words -> eight f16 values.
+__device__ inline half8_t fp8x8(uint32_t w0, uint32_t w1) {
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The lane's A-operand slice for QK step kk (or the transpose of V): eight
+// consecutive channels (g*D/4 + 8kk .. +7) of its token, dequantized to f16.
+template <int D, bool FP8>
+__device__ inline half8_t unpack(const uint32_t* words, uint32_t scale_bits, int kk) {
+  if constexpr (FP8) {
+    return fp8x8(words[2 * kk], words[2 * kk + 1]);
+  } else {
+    // NVFP4: word kk holds the 8 channels; block scale byte(s) of the lane
+    const half2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scale_bits, 1.0f, false);
+    const half2_t s = (D == 128 && kk >= 2) ? splat_hi(s2) : splat_lo(s2);
+    return fp4x8_scaled(words[kk], s);
+  }
+}
+
+__device__ inline uint32_t pack_f16x2(float a, float b) {
+  const fp16x2_t r = __builtin_amdgcn_cvt_pkrtz(a, b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ inline half8_t pack_half8(const float4_t& x, const float4_t& y) {
+  const uint32_t w[4] = {pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(y[0], y[1]),
+                         pack_f16x2(y[2], y[3])};
+  return __builtin_bit_cast(half8_t, w);
+}
+
+template <int D, bool FP8>
+__device__ inline void load_tile(const DecodeParams& p, const int32_t* bt, int g, int tok0, int t1, int lane,
+                                 TileRaw<D, FP8>& raw) {
+  using C = Cfg<D, FP8>;
+  const int r = lane & 15, grp = lane >> 4;
+  if (tok0 < t1) {
+    const int P = p.page_size;
+    const int64_t row = ((int64_t)bt[tok0 / P] * p.num_kv_heads + g) * P + (tok0 % P) + r;
+    const uint8_t* kp = p.kd + row * C::kRowBytes + grp * C::kLaneBytes;
+    const uint8_t* vp = p.vd + row * C::kRowBytes + grp * C::kLaneBytes;
+    if constexpr (C::kLaneWords == 2) {
+      const uint2 a = *reinterpret_cast<const uint2*>(kp);
+      const uint2 b = *reinterpret_cast<const uint2*>(vp);
+      raw.k[0] = a.x; raw.k[1] = a.y;
+      raw.v[0] = b.x; raw.v[1] = b.y;
+    } else {
+#pragma unroll
+      for (int w = 0; w < C::kLaneWords / 4; ++w) {
+        const uint4 a = reinterpret_cast<const uint4*>(kp)[w];
+        const uint4 b = reinterpret_cast<const uint4*>(vp)[w];
+        raw.k[4 * w] = a.x; raw.k[4 * w + 1] = a.y; raw.k[4 * w + 2] = a.z; raw.k[4 * w + 3] = a.w;
+        raw.v[4 * w] = b.x; raw.v[4 * w + 1] = b.y; raw.v[4 * w + 2] = b.z; raw.v[4 * w + 3] = b.w;
+      }
+    }
+    if constexpr (!FP8) {
+      constexpr int nb = D / kBlock;
+      if constexpr (D == 128) {
+        raw.ks = *reinterpret_cast<const uint16_t*>(p.ks + row * nb + 2 * grp);
+        raw.vs = *reinterpret_cast<const uint16_t*>(p.vs + row * nb + 2 * grp);
+      } else {
+        raw.ks = p.ks[row * nb + grp];
+        raw.vs = p.vs[row * nb + grp];
+      }
+    }
+    // tokens past the end: V must be exactly zero (the bytes there are arbitrary)
+    if (tok0 + r >= t1) {
+      if constexpr (FP8) {
+#pragma unroll
+        for (int w = 0; w < C::kLaneWords; ++w) raw.v[w] = 0;
+      } else {
+        raw.vs = 0;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < C::kLaneWords; ++w) { raw.k[w] = 0; raw.v[w] = 0; }
+    raw.ks = 0;
+    raw.vs = 0;
+  }
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_partial_mfma_kernel(DecodeParams p) {
+  using C = Cfg<D, FP8>;
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int col = lane & 15;        // head (QK/PV columns) or channel (transpose columns)
+  const int grp = lane >> 4;        // lane group: token rows 4grp..4grp+3 of a tile
+  const int G = p.group;
+  const int S = p.num_splits;
+  const int L = p.seq_lens[b];
+  const int P = p.page_size;
+  const int per = ceil_div(ceil_div(L, S), P) * P;
+  const int t0 = j * per;
+  const int t1 = min(L, t0 + per);
+  const int64_t qh0 = (int64_t)b * p.num_q_heads + (int64_t)g * G;
+
+  float4_t acc[C::kCTiles];
+#pragma unroll
+  for (int c = 0; c < C::kCTiles; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.0f;
+
+  if (t0 < t1) {
+    // ---- q as the B operand: lane (head col, group grp), step kk: channels grp*D/4 + 8kk .. +7
+    const bool hv = col < G;
+    float qf[C::kKSteps][8];
+    float qmax = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < C::kKSteps; ++kk) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (hv) w = *reinterpret_cast<const uint4*>(p.q + (qh0 + col) * D + grp * C::kChanPerGroup + 8 * kk);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qf[kk][2 * e] = __uint_as_float(ww[e] << 16);
+        qf[kk][2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+        qmax = fmaxf(qmax, fmaxf(fabsf(qf[kk][2 * e]), fabsf(qf[kk][2 * e + 1])));
+      }
+    }
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+    // power-of-two shift that keeps the head's largest |q| below 2^15 in f16
+    const int qexp = (qmax > 0.0f) ? max(0, (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 14) : 0;
+    const float qdown = __uint_as_float((uint32_t)(127 - qexp) << 23);
+    half8_t qb[C::kKSteps];
+#pragma unroll
+    for (int kk = 0; kk < C::kKSteps; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[kk][e] = (_Float16)(qf[kk][e] * qdown);
+    // scaled logit (base 2) = raw score * c
+    const float cscale = p.qk_scale * __uint_as_float((uint32_t)(127 + qexp) << 23);
+
+    // ---- 0/1 selection operands for the V transposes: column n takes A slot (group 2hs + n/8, item n%8)
+    half8_t sel[2];
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sel[hs][e] = (grp == 2 * hs + (col >> 3) && e == (col & 7)) ? (_Float16)1.0f : (_Float16)0.0f;
+
+    const int32_t* bt = p.block_tables + (int64_t)b * p.max_pages;
+    TileRaw<D, FP8> cur[C::kTiles], nxt[C::kTiles];
+#pragma unroll
+    for (int t = 0; t < C::kTiles; ++t) load_tile<D, FP8>(p, bt, g, t0 + 16 * t, t1, lane, cur[t]);
+
+    for (int ts = t0; ts < t1; ts += C::kChunk) {
+      // prefetch the next chunk
+#pragma unroll
+      for (int t = 0; t < C::kTiles; ++t)
+        load_tile<D, FP8>(p, bt, g, ts + C::kChunk + 16 * t, t1, lane, nxt[t]);
+
+      // ---- QK: scores of the chunk, lane (head col, rows 4grp..) per tile
+      float sc[C::kTiles][4];
+#pragma unroll
+      for (int t = 0; t < C::kTiles; ++t) {
+        float4_t c4 = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < C::kKSteps; ++kk) c4 = mfma(unpack<D, FP8>(cur[t].k, cur[t].ks, kk), qb[kk], c4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = ts + 16 * t + 4 * grp + i;
+          sc[t][i] = (tok < t1) ? c4[i] * cscale : -INFINITY;
+        }
+      }
+
+      // ---- online softmax (base 2) per head
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < C::kTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[t][i]);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float mnew = fmaxf(m, cmax);
+      const float alpha = exp2f(m - mnew);
+      m = mnew;
+      float psum = 0.0f;
+#pragma unroll
+      for (int t = 0; t < C::kTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[t][i] = exp2f(sc[t][i] - mnew);
+          psum += sc[t][i];
+        }
+      l = l * alpha + psum;
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int c = 0; c < C::kCTiles; ++c) acc[c] *= alpha;
+      }
+
+      // ---- PV over pairs of tiles (32 tokens = one MFMA K)
+#pragma unroll
+      for (int t = 0; t < C::kTiles; t += 2) {
+        const half8_t pb = pack_half8(float4_t{sc[t][0], sc[t][1], sc[t][2], sc[t][3]},
+                                      float4_t{sc[t + 1][0], sc[t + 1][1], sc[t + 1][2], sc[t + 1][3]});
+#pragma unroll
+        for (int kk = 0; kk < C::kKSteps; ++kk) {
+          const half8_t va = unpack<D, FP8>(cur[t].v, cur[t].vs, kk);
+          const half8_t vb = unpack<D, FP8>(cur[t + 1].v, cur[t + 1].vs, kk);
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            const float4_t zero = float4_t{0.f, 0.f, 0.f, 0.f};
+            const float4_t da = mfma(va, sel[hs], zero);     // tile t,   transposed
+            const float4_t db = mfma(vb, sel[hs], zero);     // tile t+1, transposed
+            acc[2 * kk + hs] = mfma(pack_half8(da, db), pb, acc[2 * kk + hs]);
+          }
+        }
+      }
+
+#pragma unroll
+      for (int t = 0; t < C::kTiles; ++t) cur[t] = nxt[t];
+    }
+  }
+
+  // ---- partial results: lane (head col, channel group grp)
+  float lt = l + __shfl_xor(l, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (col < G) {
+    const int64_t idx = (qh0 + col) * S + j;
+    float* o = p.part_o + idx * D;
+#pragma unroll
+    for (int kk = 0; kk < C::kKSteps; ++kk)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const int ch = (2 * hs + (grp >> 1)) * C::kChanPerGroup + 8 * kk + 4 * (grp & 1);
+        const float4_t a = acc[2 * kk + hs];
+        *reinterpret_cast<float4*>(o + ch) = make_float4(a[0], a[1], a[2], a[3]);
+      }
+    if (grp == 0) {
+      p.part_ml[idx * 2] = m;
+      p.part_ml[idx * 2 + 1] = lt;
+    }
+  }
+}
+
+template <int D, bool FP8>
+hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
+  dim3 grid(p.num_splits, p.num_kv_heads, p.batch);
+  hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8>), grid, dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, hipStream_t s) {
+  if (head_dim == 64) return fp8 ? launch_mfma<64, true>(p, s) : launch_mfma<64, false>(p, s);
+  return fp8 ? launch_mfma<128, true>(p, s) : launch_mfma<128, false>(p, s);
+}
+
+}  // namespace nvfp4kv

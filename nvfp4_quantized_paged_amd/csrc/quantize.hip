@@ -1,0 +1,134 @@
+// Quantize-on-write of new K/V into the paged NVFP4 pool and into the FP8
+// baseline pool.
+//
+// "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
+// section A2 (paths 1 and 2: new K/V are quantized and appended to the
+// persistent paged NVFP4 pool) and section A3 (E2M1 elements with one E4M3
+// scale per 16 elements and an FP32 tensor scale).
+//
+// One thread encodes one 16-channel block of one (token, head): it reads 32
+// bytes of bf16 with two 128-bit loads and writes 8 packed bytes plus one
+// scale byte. The element codes come from exact threshold compares: with
+// block scale S (E4M3) and tensor scale gs, the E2M1 midpoints m*S*gs are
+// exact fp32 products, so "a > m*S*gs" (or ">=" where the tie goes up to an
+// even code) is the round-to-nearest-even decision with no division.
+#include "common.hpp"
+
+namespace nvfp4kv {
+
+namespace {
+
+__device__ inline void load_block16(const uint16_t* src, float x[16]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(src);
+  const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// E2M1 magnitude code (0..7) of a = |x| given the block's effective scale sg.
+// Midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5; a tie rounds up only where the
+// upper neighbour has an even code (0.75 -> 1.0, 1.75 -> 2.0, 3.5 -> 4.0).
+__device__ inline uint32_t e2m1_code(float a, const float t[7]) {
+  uint32_t c = 0;
+  c += a > t[0];
+  c += a >= t[1];
+  c += a > t[2];
+  c += a >= t[3];
+  c += a > t[4];
+  c += a >= t[5];
+  c += a > t[6];
+  return c;
+}
+
+__global__ __launch_bounds__(256) void nvfp4_quantize_kernel(QuantizeParams p) {
+  const int which = blockIdx.y;                       // 0 = K, 1 = V
+  const int nb = p.head_dim / kBlock;
+  const int64_t items = (int64_t)p.num_tokens * p.num_kv_heads * nb;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= items) return;
+  const int blk = (int)(i % nb);
+  const int64_t th = i / nb;
+  const int h = (int)(th % p.num_kv_heads);
+  const int64_t t = th / p.num_kv_heads;
+  const int64_t slot = p.slot_mapping[t];
+  if (slot < 0) return;
+
+  float x[16];
+  load_block16(p.src[which] + t * p.src_stride + (int64_t)h * p.head_dim + blk * kBlock, x);
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  const float gs = p.gscale[which];
+  const uint32_t sbyte = e4m3_encode_nonneg(amax / (6.0f * gs));
+  const float sg = e4m3_to_f32(sbyte) * gs;
+  const float t7[7] = {0.25f * sg, 0.75f * sg, 1.25f * sg, 1.75f * sg,
+                       2.5f * sg, 3.5f * sg, 5.0f * sg};
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t sign = (__float_as_uint(x[e]) >> 31) << 3;
+    const uint32_t mag = sg > 0.0f ? e2m1_code(fabsf(x[e]), t7) : 0u;
+    const uint32_t nib = sign | mag;
+    if (e < 8) lo |= nib << (4 * e);
+    else hi |= nib << (4 * (e - 8));
+  }
+  const int64_t page = slot / p.page_size, off = slot % p.page_size;
+  const int64_t row = (page * p.num_kv_heads + h) * p.page_size + off;
+  *reinterpret_cast<uint2*>(p.data[which] + row * (p.head_dim / 2) + blk * 8) = make_uint2(lo, hi);
+  p.scale[which][row * nb + blk] = (uint8_t)sbyte;
+}
+
+// FP8: one thread per 16 elements, one 128-bit store.
+__global__ __launch_bounds__(256) void fp8_quantize_kernel(QuantizeParams p) {
+  const int which = blockIdx.y;
+  const int nb = p.head_dim / kBlock;
+  const int64_t items = (int64_t)p.num_tokens * p.num_kv_heads * nb;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= items) return;
+  const int blk = (int)(i % nb);
+  const int64_t th = i / nb;
+  const int h = (int)(th % p.num_kv_heads);
+  const int64_t t = th / p.num_kv_heads;
+  const int64_t slot = p.slot_mapping[t];
+  if (slot < 0) return;
+
+  float x[16];
+  load_block16(p.src[which] + t * p.src_stride + (int64_t)h * p.head_dim + blk * kBlock, x);
+  const float s = p.gscale[which];
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float y = (s == 1.0f) ? x[e] : x[e] / s;
+    const uint32_t byte = e4m3_encode_nonneg(fabsf(y)) | ((__float_as_uint(y) >> 31) << 7);
+    w[e / 4] |= byte << (8 * (e % 4));
+  }
+  const int64_t page = slot / p.page_size, off = slot % p.page_size;
+  const int64_t row = (page * p.num_kv_heads + h) * p.page_size + off;
+  *reinterpret_cast<uint4*>(p.data[which] + row * p.head_dim + blk * kBlock) =
+      make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4_quantize(const QuantizeParams& p, hipStream_t s) {
+  const int64_t items = (int64_t)p.num_tokens * p.num_kv_heads * (p.head_dim / kBlock);
+  if (items == 0) return hipSuccess;
+  dim3 grid((unsigned)((items + 255) / 256), 2);
+  hipLaunchKernelGGL(nvfp4_quantize_kernel, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize(const QuantizeParams& p, hipStream_t s) {
+  const int64_t items = (int64_t)p.num_tokens * p.num_kv_heads * (p.head_dim / kBlock);
+  if (items == 0) return hipSuccess;
+  dim3 grid((unsigned)((items + 255) / 256), 2);
+  hipLaunchKernelGGL(fp8_quantize_kernel, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

@@ -287,3 +287,25 @@ def page_layout(num_seqs: int, context: int, page_size: int, seed: int):
     pages_per_seq = max(1, -(-context // page_size))
     perm = rng.permutation(num_seqs * pages_per_seq).astype(np.int32)
     return perm.reshape(num_seqs, pages_per_seq)
+
+
+# ---------------------------------------------------------------------------
+# host -> device plumbing (no arithmetic)
+# ---------------------------------------------------------------------------
+
+def to_device_bf16(bits: np.ndarray, device="cuda"):
+    """uint16 bf16 bit patterns -> torch.bfloat16 device tensor (same bits)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def to_device(a: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def bf16_tensor_bits(t) -> np.ndarray:
+    """torch bf16 tensor (any device) -> uint16 bit patterns on the host."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,178 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared
+symbol, and rejects invalid arguments before any HIP call (no GPU needed).
+
+The pointers passed here are never dereferenced: validation runs on the
+host and returns before anything is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4kv.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import nvfp4_quantized_paged_amd as nk
+    if not os.path.exists(nk.LIB_PATH):
+        from nvfp4_quantized_paged_amd import build
+        build.build()
+    return nk
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:const\s+char\s*\*|int32_t|int|size_t)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("nvfp4_kv_quantize", "nvfp4_kv_dequant_workspace", "nvfp4_paged_decode_attn",
+                     "fp8_paged_decode_attn", "fp8_kv_quantize", "nvfp4kv_lse_merge"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert L.abi_version() == 1
+
+
+def test_exported_symbols_are_only_the_abi(L):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.split()[-2] in ("T", "W")}
+    ours = {n for n in exported if not n.startswith("_")}
+    assert ours == set(declared_functions())
+
+
+def test_split_heuristic_and_workspace_size(L):
+    # fills ~2048 items, at most one split per 256 tokens of the longest sequence
+    assert L.nvfp4_paged_decode_num_splits(44, 8, 512, 64) == 6
+    assert L.nvfp4_paged_decode_num_splits(2, 8, 16384, 64) == 128
+    assert L.nvfp4_paged_decode_num_splits(8, 8, 256, 16) == 16
+    assert L.nvfp4_paged_decode_num_splits(1, 1, 16, 16) == 1
+    assert L.nvfp4_paged_decode_workspace_bytes(44, 40, 128, 32) == 44 * 40 * 32 * 130 * 4
+    assert L.nvfp4_paged_decode_workspace_bytes(0, 40, 128, 32) == 0
+
+
+FAKE = 0x100000  # aligned, never dereferenced
+
+
+def _geom(L, pages=16, P=16, H=1, d=64):
+    return L.Geom(pages, P, H, d)
+
+
+def _nv(L, data=FAKE, scale=FAKE, gs=1.0):
+    return L.NVFP4CacheDesc(data, scale, gs)
+
+
+def _quant(L, g, k=FAKE, v=FAKE, stride=64, T=4, slots=FAKE, kc=None, vc=None):
+    kc = kc or _nv(L)
+    vc = vc or _nv(L)
+    gp = ctypes.byref(g) if g is not None else None
+    return L.lib().nvfp4_kv_quantize(gp, k, v, stride, T, slots, ctypes.byref(kc), ctypes.byref(vc), None)
+
+
+def test_quantize_rejects_bad_arguments(L):
+    assert _quant(L, None) == L.EINVAL
+    assert _quant(L, _geom(L, d=96)) == L.EUNSUPPORTED
+    assert _quant(L, _geom(L, d=80)) == L.EUNSUPPORTED
+    assert _quant(L, _geom(L, P=8)) == L.EUNSUPPORTED
+    assert _quant(L, _geom(L, pages=0)) == L.EINVAL
+    assert _quant(L, _geom(L), T=-1) == L.EINVAL
+    assert _quant(L, _geom(L), k=None) == L.EINVAL
+    assert _quant(L, _geom(L), slots=None) == L.EINVAL
+    assert _quant(L, _geom(L), stride=32) == L.EINVAL
+    assert _quant(L, _geom(L), stride=68) == L.EALIGN
+    assert _quant(L, _geom(L), k=FAKE + 2) == L.EALIGN
+    assert _quant(L, _geom(L), kc=_nv(L, data=FAKE + 8)) == L.EALIGN
+    assert _quant(L, _geom(L), vc=_nv(L, scale=None)) == L.EINVAL
+    assert _quant(L, _geom(L), kc=_nv(L, gs=0.0)) == L.EINVAL
+    assert _quant(L, _geom(L), kc=_nv(L, gs=float("nan"))) == L.EINVAL
+    assert "global_scale" in L.last_error()
+    # zero tokens: accepted, nothing launched
+    assert _quant(L, _geom(L), T=0, k=None, v=None, slots=None) == L.OK
+
+
+def _decode(L, g, q=FAKE, bt=FAKE, maxp=16, sl=FAKE, B=1, Hq=4, sm=0.125, S=1, ws=FAKE,
+            ws_bytes=1 << 20, out=FAKE, fn="nvfp4_paged_decode_attn"):
+    kc, vc = _nv(L), _nv(L)
+    return getattr(L.lib(), fn)(ctypes.byref(g), q, ctypes.byref(kc), ctypes.byref(vc), bt, maxp, sl, B, Hq,
+                                sm, S, ws, ws_bytes, out, None)
+
+
+def test_decode_rejects_bad_arguments(L):
+    g = _geom(L)
+    assert _decode(L, g, q=None) == L.EINVAL
+    assert _decode(L, g, q=FAKE + 4) == L.EALIGN
+    assert _decode(L, g, out=FAKE + 2) == L.EALIGN
+    assert _decode(L, g, out=None) == L.EINVAL
+    assert _decode(L, g, B=-1) == L.EINVAL
+    assert _decode(L, g, maxp=0) == L.EINVAL
+    assert _decode(L, _geom(L, H=2), Hq=3) == L.EINVAL
+    assert _decode(L, g, Hq=32) == L.EUNSUPPORTED
+    assert _decode(L, g, S=5000) == L.EINVAL
+    assert _decode(L, g, S=-1) == L.EINVAL
+    assert _decode(L, g, sm=float("inf")) == L.EINVAL
+    assert _decode(L, g, ws_bytes=100) == L.EWORKSPACE
+    assert "workspace" in L.last_error()
+    assert _decode(L, g, ws=None) == L.EINVAL
+    # batch 0 needs no workspace and launches nothing
+    assert _decode(L, g, B=0, ws=None, ws_bytes=0) == L.OK
+
+
+def test_partial_rejects_bad_variant_and_auto_splits(L):
+    g = _geom(L)
+    kc, vc = _nv(L), _nv(L)
+    f = L.lib().nvfp4_paged_decode_partial
+    args = lambda S, variant: (ctypes.byref(g), FAKE, ctypes.byref(kc), ctypes.byref(vc), FAKE, 16, FAKE, 1, 4,
+                               0.125, S, variant, FAKE, 1 << 20, None)
+    assert f(*args(1, 7)) == L.EINVAL
+    assert f(*args(0, 0)) == L.EINVAL      # the partial call needs an explicit split count
+
+
+def test_merge_rejects_bad_arguments(L):
+    f = L.lib().nvfp4kv_lse_merge
+    assert f(FAKE, 1 << 20, 1, 4, 96, 1, 1.0, FAKE, None) == L.EUNSUPPORTED
+    assert f(FAKE, 1 << 20, 1, 4, 64, 0, 1.0, FAKE, None) == L.EINVAL
+    assert f(FAKE, 10, 1, 4, 64, 1, 1.0, FAKE, None) == L.EWORKSPACE
+    assert f(None, 1 << 20, 1, 4, 64, 1, 1.0, FAKE, None) == L.EINVAL
+    assert f(FAKE, 1 << 20, 1, 4, 64, 1, float("nan"), FAKE, None) == L.EINVAL
+    assert f(FAKE, 0, 0, 4, 64, 1, 1.0, None, None) == L.OK
+
+
+def test_workspace_dequant_rejects_bad_arguments(L):
+    g = _geom(L)
+    kc, vc = _nv(L), _nv(L)
+    f = L.lib().nvfp4_kv_dequant_workspace
+    ok = dict(bt=FAKE, maxp=16, pl=FAKE, offs=FAKE, B=2, kw=FAKE, vw=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(ctypes.byref(g), ctypes.byref(kc), ctypes.byref(vc), a["bt"], a["maxp"], a["pl"], a["offs"],
+                 a["B"], a["kw"], a["vw"], None)
+
+    assert call(B=-1) == L.EINVAL
+    assert call(bt=None) == L.EINVAL
+    assert call(offs=None) == L.EINVAL
+    assert call(maxp=0) == L.EINVAL
+    assert call(kw=FAKE + 2) == L.EALIGN
+    assert call(B=0, bt=None, pl=None, offs=None, kw=None, vw=None) == L.OK
+
+
+def test_fp8_entry_points_validate(L):
+    g = _geom(L)
+    kc = L.FP8CacheDesc(FAKE, 1.0)
+    bad = L.FP8CacheDesc(FAKE, -1.0)
+    f = L.lib().fp8_kv_quantize
+    assert f(ctypes.byref(g), FAKE, FAKE, 64, 4, FAKE, ctypes.byref(kc), ctypes.byref(bad), None) == L.EINVAL
+    assert f(ctypes.byref(g), FAKE, FAKE, 64, 0, FAKE, ctypes.byref(kc), ctypes.byref(kc), None) == L.OK
+    d = L.lib().fp8_paged_decode_attn
+    assert d(ctypes.byref(g), FAKE, ctypes.byref(kc), ctypes.byref(kc), FAKE, 16, FAKE, 1, 4, 0.125, 1, FAKE, 8,
+             FAKE, None) == L.EWORKSPACE

@@ -1,0 +1,510 @@
+"""GPU parity of the HIP path (called through the C ABI) against the CPU oracle.
+
+Bars:
+  * quantize (NVFP4 and FP8) and the dequantized workspace: bit-exact, over
+    the whole pool including bytes that must stay untouched;
+  * decode output: per element e = |gpu - ref| / max(1, sum_t p_t |v_t|) with
+    max e <= 2e-2 and mean e <= 2e-3 (the absolute tolerance read against
+    each output's natural magnitude; raw errors are printed too).
+Every case prints its name, shape and seed before touching the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as oatt
+from oracle import fp8 as of8
+from oracle import nvfp4 as onv
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0xAB
+TOL_MAX, TOL_MEAN = 2e-2, 2e-3
+
+
+@pytest.fixture(scope="module")
+def nk():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import nvfp4_quantized_paged_amd as m
+    m.lib()
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def nv_pools(nk, num_pages, H, P, d, gs=1.0):
+    k = nk.NVFP4Pool.empty(num_pages, H, P, d, global_scale=gs)
+    v = nk.NVFP4Pool.empty(num_pages, H, P, d, global_scale=gs)
+    for t in (k.data, k.scale, v.data, v.scale):
+        t.fill_(SENT)
+    return k, v
+
+
+def f8_pools(nk, num_pages, H, P, d, scale=1.0):
+    k = nk.FP8Pool.empty(num_pages, H, P, d, scale=scale)
+    v = nk.FP8Pool.empty(num_pages, H, P, d, scale=scale)
+    k.data.fill_(SENT)
+    v.data.fill_(SENT)
+    return k, v
+
+
+def oracle_nv(num_pages, H, P, d, k_bits, v_bits, slots, gs=1.0):
+    kd, ks = onv.empty_cache(num_pages, H, P, d, fill=SENT)
+    vd, vs = onv.empty_cache(num_pages, H, P, d, fill=SENT)
+    onv.write_cache(kd, ks, k_bits, slots, gs)
+    onv.write_cache(vd, vs, v_bits, slots, gs)
+    return kd, ks, vd, vs
+
+
+def gpu_quantize_nv(nk, num_pages, H, P, d, k_bits, v_bits, slots, gs=1.0, kt=None, vt=None):
+    kp, vp = nv_pools(nk, num_pages, H, P, d, gs)
+    kt = synth.to_device_bf16(k_bits) if kt is None else kt
+    vt = synth.to_device_bf16(v_bits) if vt is None else vt
+    nk.nvfp4_kv_quantize(kt, vt, synth.to_device(slots.astype(np.int64)), kp, vp)
+    torch.cuda.synchronize()
+    return kp, vp
+
+
+def assert_pool_equal(gpu_t, ref, what):
+    got = gpu_t.cpu().numpy()
+    if not np.array_equal(got, ref):
+        bad = np.argwhere(got != ref)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} bytes differ; first at {i}: gpu {got[i]:#04x} oracle {ref[i]:#04x}")
+
+
+def check_out(out_t, ref, mass, what):
+    got = out_t.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    raw = np.abs(got - ref)
+    e = raw / np.maximum(1.0, mass)
+    say(f"  {what}: max e {e.max():.3e} mean e {e.mean():.3e} | raw max {raw.max():.3e} mean {raw.mean():.3e}")
+    assert e.max() <= TOL_MAX and e.mean() <= TOL_MEAN, what
+
+
+def decode_problem(nk, inp, splits_list=(0,), variants=(None,), gs=1.0, label=""):
+    """Quantize inp on both sides, check bytes, decode on the GPU, compare."""
+    wl = inp.wl
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    kp, vp = gpu_quantize_nv(nk, inp.num_pages, H, P, d, inp.k, inp.v, inp.slot_mapping, gs)
+    kd, ks, vd, vs = oracle_nv(inp.num_pages, H, P, d, inp.k, inp.v, inp.slot_mapping, gs)
+    assert_pool_equal(kp.data, kd, f"{label} K data")
+    assert_pool_equal(kp.scale, ks, f"{label} K scale")
+    assert_pool_equal(vp.data, vd, f"{label} V data")
+    assert_pool_equal(vp.scale, vs, f"{label} V scale")
+    ref, mass = oatt.paged_decode(inp.q, onv.dequant_cache(kd, ks, gs), onv.dequant_cache(vd, vs, gs),
+                                  inp.block_tables, inp.seq_lens, wl.sm_scale)
+    q = synth.to_device_bf16(inp.q)
+    bt = synth.to_device(inp.block_tables)
+    sl = synth.to_device(inp.seq_lens)
+    outs = []
+    for S in splits_list:
+        for var in variants:
+            if var is None:
+                out = nk.nvfp4_paged_decode_attn(q, kp, vp, bt, sl, wl.sm_scale, num_splits=S)
+            else:
+                Sx = S or nk.nvfp4_paged_decode_num_splits(q.shape[0], H, bt.shape[1], P)
+                ws = nk.nvfp4_paged_decode_partial(q, kp, vp, bt, sl, wl.sm_scale, Sx, variant=var)
+                out = torch.empty_like(q)
+                nk.nvfp4kv_lse_merge(ws, q.shape[0], q.shape[1], d, Sx, vp.global_scale, out)
+            torch.cuda.synchronize()
+            check_out(out, ref, mass, f"{label} splits={S} variant={var}")
+            outs.append(out)
+    return outs, (kp, vp), (ref, mass)
+
+
+# ---------------------------------------------------------------------------
+# quantize-on-write
+# ---------------------------------------------------------------------------
+
+def test_quantize_tiny_workload(nk):
+    wl = synth.WORKLOADS[1]
+    say(f"case quantize tiny: {wl} seed {wl.seed}")
+    inp = synth.host_uniform_decode(wl)
+    kp, vp = gpu_quantize_nv(nk, inp.num_pages, 1, 16, 64, inp.k, inp.v, inp.slot_mapping)
+    kd, ks, vd, vs = oracle_nv(inp.num_pages, 1, 16, 64, inp.k, inp.v, inp.slot_mapping)
+    for t, r, n in ((kp.data, kd, "K data"), (kp.scale, ks, "K scale"), (vp.data, vd, "V data"),
+                    (vp.scale, vs, "V scale")):
+        assert_pool_equal(t, r, n)
+
+
+def test_quantize_moderate_workload_with_outliers(nk):
+    wl = synth.WORKLOADS[2]
+    say(f"case quantize moderate: {wl} seed {wl.seed}")
+    inp = synth.host_uniform_decode(wl)
+    kp, vp = gpu_quantize_nv(nk, inp.num_pages, 8, 16, 128, inp.k, inp.v, inp.slot_mapping)
+    kd, ks, vd, vs = oracle_nv(inp.num_pages, 8, 16, 128, inp.k, inp.v, inp.slot_mapping)
+    for t, r, n in ((kp.data, kd, "K data"), (kp.scale, ks, "K scale"), (vp.data, vd, "V data"),
+                    (vp.scale, vs, "V scale")):
+        assert_pool_equal(t, r, n)
+
+
+def _crafted_rows(rng, T, H, d):
+    """bf16 rows mixing exact E2M1 midpoints, saturating values, tiny and huge
+    magnitudes, negative zeros and every-bf16 sweeps."""
+    x = rng.standard_normal((T, H, d)).astype(np.float32)
+    blocks = x.reshape(T, H, d // 16, 16)
+    S = np.float32(2.0) ** rng.integers(-12, 8, size=blocks.shape[:3]).astype(np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.0, 0.5, 1, 1.5, 2, 3, 4, 6.375], np.float32)
+    kind = rng.integers(0, 5, size=blocks.shape[:3])
+    for idx in np.argwhere(kind == 0):                       # exact ties against S
+        blocks[tuple(idx)] = rng.permutation(mids) * S[tuple(idx)] * rng.choice([-1, 1], 16)
+    blocks[kind == 1] *= 1e-30                                 # scale underflows to 0
+    blocks[kind == 2] *= 1e30                                  # scale saturates at 448
+    blocks[kind == 3] = -0.0
+    bits = synth.f32_to_bf16_bits(blocks.reshape(T, H, d))
+    sweep = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    sweep = sweep[np.isfinite(synth.bf16_bits_to_f64(sweep))]
+    n = min(sweep.size, bits.size // 2)
+    flat = bits.reshape(-1)
+    flat[:n] = rng.permutation(sweep)[:n]
+    return flat.reshape(T, H, d)
+
+
+@pytest.mark.parametrize("gs", [1.0, 2.0, 0.5])
+def test_quantize_crafted_values_and_skipped_slots(nk, gs):
+    rng = np.random.default_rng(11)
+    T, H, P, d, pages = 1536, 2, 32, 64, 64
+    say(f"case quantize crafted: T {T} H {H} P {P} d {d} gs {gs}")
+    with np.errstate(over="ignore", invalid="ignore"):
+        k = _crafted_rows(rng, T, H, d)
+        v = _crafted_rows(rng, T, H, d)
+    slots = rng.permutation(pages * P)[:T].astype(np.int64)
+    slots[rng.random(T) < 0.05] = -1                           # padding tokens
+    kp, vp = gpu_quantize_nv(nk, pages, H, P, d, k, v, slots, gs)
+    kd, ks, vd, vs = oracle_nv(pages, H, P, d, k, v, slots, gs)
+    for t, r, n in ((kp.data, kd, "K data"), (kp.scale, ks, "K scale"), (vp.data, vd, "V data"),
+                    (vp.scale, vs, "V scale")):
+        assert_pool_equal(t, r, n)
+
+
+def test_quantize_golden_blocks(nk):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_block_vectors.txt")
+    rows = []
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        rows.append([float(t) for t in line.split("|")[1].split()])
+    x = np.zeros((1, 1, 128), np.float32)
+    blocks = np.array(rows, np.float32)[:8]
+    x[0, 0, :16 * len(blocks)] = blocks.reshape(-1)
+    bits = synth.f32_to_bf16_bits(x)
+    say("case quantize golden blocks")
+    kp, vp = gpu_quantize_nv(nk, 1, 1, 16, 128, bits, bits, np.array([3], np.int64))
+    kd, ks, _, _ = oracle_nv(1, 1, 16, 128, bits, bits, np.array([3], np.int64))
+    assert_pool_equal(kp.data, kd, "golden data")
+    assert_pool_equal(kp.scale, ks, "golden scale")
+
+
+def test_quantize_strided_source(nk):
+    """K and V read out of a fused [T][3][Hkv][d] buffer (token stride 3*Hkv*d)."""
+    rng = np.random.default_rng(12)
+    T, H, P, d, pages = 200, 4, 16, 128, 16
+    say(f"case quantize strided: T {T} H {H} d {d}")
+    qkv = synth.f32_to_bf16_bits(rng.standard_normal((T, 3, H, d)).astype(np.float32))
+    slots = rng.permutation(pages * P)[:T].astype(np.int64)
+    dev = synth.to_device_bf16(qkv)
+    kt, vt = dev[:, 1], dev[:, 2]
+    kp, vp = gpu_quantize_nv(nk, pages, H, P, d, None, None, slots, kt=kt, vt=vt)
+    kd, ks, vd, vs = oracle_nv(pages, H, P, d, qkv[:, 1].copy(), qkv[:, 2].copy(), slots)
+    assert_pool_equal(kp.data, kd, "K data")
+    assert_pool_equal(vp.scale, vs, "V scale")
+
+
+def test_fp8_quantize_every_bf16_value(nk):
+    rng = np.random.default_rng(13)
+    sweep = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    sweep = sweep[np.isfinite(synth.bf16_bits_to_f64(sweep))]
+    H, P, d = 1, 16, 64
+    T = -(-sweep.size // d)
+    pad = np.zeros(T * d, np.uint16)
+    pad[:sweep.size] = rng.permutation(sweep)
+    k = pad.reshape(T, H, d)
+    v = k[::-1].copy()
+    pages = -(-T // P)
+    slots = np.arange(T, dtype=np.int64)
+    say(f"case fp8 quantize sweep: T {T}")
+    kp, vp = f8_pools(nk, pages, H, P, d)
+    nk.fp8_kv_quantize(synth.to_device_bf16(k), synth.to_device_bf16(v), synth.to_device(slots), kp, vp)
+    torch.cuda.synchronize()
+    kr = np.full((pages, H, P, d), SENT, np.uint8)
+    vr = np.full((pages, H, P, d), SENT, np.uint8)
+    of8.write_cache(kr, k, slots)
+    of8.write_cache(vr, v, slots)
+    assert_pool_equal(kp.data, kr, "fp8 K")
+    assert_pool_equal(vp.data, vr, "fp8 V")
+
+
+# ---------------------------------------------------------------------------
+# dequantize-to-workspace
+# ---------------------------------------------------------------------------
+
+def test_dequant_workspace_agentic_small(nk):
+    wl = synth.WORKLOADS[5]
+    a = synth.host_agentic(wl, batch=7, len_min=48, len_max=131, shared_prefix=32, chunk=9)
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    say(f"case workspace small agentic: B 7 pages {a.num_pages}")
+    kp, vp = gpu_quantize_nv(nk, a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached)
+    kd, ks, vd, vs = oracle_nv(a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached)
+    prefix = a.cached_lens.copy()
+    prefix[3] = 0                                         # an empty prefix
+    prefix[5] = 17                                        # a ragged partial page
+    rows = int(a.ws_row_offsets[-1])
+    kws = torch.full((rows, H, d), -7.0, dtype=torch.bfloat16, device="cuda")
+    vws = torch.full((rows, H, d), -7.0, dtype=torch.bfloat16, device="cuda")
+    nk.nvfp4_kv_dequant_workspace(kp, vp, synth.to_device(a.block_tables), synth.to_device(prefix),
+                                  synth.to_device(a.ws_row_offsets), kws, vws)
+    torch.cuda.synchronize()
+    fill = int(synth.bf16_tensor_bits(torch.tensor([-7.0], dtype=torch.bfloat16))[0])
+    kref = oatt.dequant_workspace(onv.dequant_cache(kd, ks), a.block_tables, prefix, a.ws_row_offsets, rows, fill)
+    vref = oatt.dequant_workspace(onv.dequant_cache(vd, vs), a.block_tables, prefix, a.ws_row_offsets, rows, fill)
+    assert np.array_equal(synth.bf16_tensor_bits(kws), kref)
+    assert np.array_equal(synth.bf16_tensor_bits(vws), vref)
+
+
+# ---------------------------------------------------------------------------
+# decode attention
+# ---------------------------------------------------------------------------
+
+def test_decode_tiny_workload(nk):
+    wl = synth.WORKLOADS[1]
+    say(f"case decode tiny: {wl}")
+    inp = synth.host_uniform_decode(wl)
+    decode_problem(nk, inp, splits_list=(1, 3, 16), variants=(None, nk.VARIANT_VALU, nk.VARIANT_MFMA),
+                   label="tiny")
+
+
+def test_decode_moderate_workload(nk):
+    wl = synth.WORKLOADS[2]
+    say(f"case decode moderate: {wl}")
+    inp = synth.host_uniform_decode(wl)
+    decode_problem(nk, inp, splits_list=(0, 1, 7), variants=(None, nk.VARIANT_VALU), label="moderate")
+
+
+@pytest.mark.parametrize("L", [0, 1, 17, 100, 1000])
+def test_decode_ragged_and_degenerate_lengths(nk, L):
+    wl = synth.Workload(90, "ragged", 3, 10, 2, 128, 32, L, True, 4)
+    say(f"case decode ragged: L {L}")
+    inp = synth.host_uniform_decode(wl)
+    inp.seq_lens[:] = np.array([L, max(0, L - 5), L // 2], np.int32)[:inp.seq_lens.size]
+    decode_problem(nk, inp, splits_list=(1, 4), variants=(None, nk.VARIANT_VALU), label=f"L={L}")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 64, 16), (16, 1, 128, 64), (4, 4, 64, 48), (7, 1, 128, 16)])
+def test_decode_group_and_shape_coverage(nk, shape):
+    G, H, d, P = shape
+    wl = synth.Workload(91, "shape", 2, G * H, H, d, P, 333, False, 3)
+    say(f"case decode shape: G {G} Hkv {H} d {d} P {P}")
+    inp = synth.host_uniform_decode(wl)
+    decode_problem(nk, inp, splits_list=(1, 3), variants=(None, nk.VARIANT_VALU), label=f"G{G}-H{H}-d{d}-P{P}")
+
+
+def test_decode_global_scale_power_of_two(nk):
+    wl = synth.Workload(92, "gs", 2, 8, 2, 128, 16, 300, True, 2)
+    inp = synth.host_uniform_decode(wl)
+    say("case decode global scale 2.0")
+    decode_problem(nk, inp, splits_list=(2,), variants=(None,), gs=2.0, label="gs2")
+
+
+def test_decode_invariants(nk):
+    wl = synth.Workload(93, "inv", 4, 16, 2, 128, 16, 700, True, 0)
+    inp = synth.host_uniform_decode(wl)
+    say("case decode invariants: determinism, page permutation, aliasing")
+    outs, (kp, vp), _ = decode_problem(nk, inp, splits_list=(5, 5), variants=(None,), label="inv")
+    assert torch.equal(outs[0], outs[1]), "run-to-run determinism"
+    # page permutation: move every page, remap the block tables
+    perm = np.random.default_rng(14).permutation(inp.num_pages)
+    inv = np.argsort(perm)
+    kp2 = nk.NVFP4Pool(kp.data[torch.from_numpy(perm).cuda()].contiguous(),
+                       kp.scale[torch.from_numpy(perm).cuda()].contiguous())
+    vp2 = nk.NVFP4Pool(vp.data[torch.from_numpy(perm).cuda()].contiguous(),
+                       vp.scale[torch.from_numpy(perm).cuda()].contiguous())
+    bt2 = inv[inp.block_tables].astype(np.int32)
+    q = synth.to_device_bf16(inp.q)
+    o2 = nk.nvfp4_paged_decode_attn(q, kp2, vp2, synth.to_device(bt2), synth.to_device(inp.seq_lens),
+                                    wl.sm_scale, num_splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, outs[0]), "page-permutation invariance"
+    # aliasing: two rows naming the same pages with the same query give identical rows
+    bt3 = inp.block_tables.copy()
+    bt3[1] = bt3[0]
+    q3 = inp.q.copy()
+    q3[1] = q3[0]
+    data_before = kp.data.clone()
+    o3 = nk.nvfp4_paged_decode_attn(synth.to_device_bf16(q3), kp, vp, synth.to_device(bt3),
+                                    synth.to_device(inp.seq_lens), wl.sm_scale, num_splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(o3[0], o3[1])
+    assert torch.equal(kp.data, data_before), "decode must not write the cache"
+
+
+def test_fp8_decode_moderate(nk):
+    wl = synth.WORKLOADS[2]
+    inp = synth.host_uniform_decode(wl, batch=4)
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    say(f"case fp8 decode moderate (batch 4): {wl}")
+    kp, vp = f8_pools(nk, inp.num_pages, H, P, d)
+    nk.fp8_kv_quantize(synth.to_device_bf16(inp.k), synth.to_device_bf16(inp.v), synth.to_device(inp.slot_mapping),
+                       kp, vp)
+    kr = np.full((inp.num_pages, H, P, d), SENT, np.uint8)
+    vr = kr.copy()
+    of8.write_cache(kr, inp.k, inp.slot_mapping)
+    of8.write_cache(vr, inp.v, inp.slot_mapping)
+    torch.cuda.synchronize()
+    assert_pool_equal(kp.data, kr, "fp8 K")
+    ref, mass = oatt.paged_decode(inp.q, of8.dequant_cache(kr), of8.dequant_cache(vr), inp.block_tables,
+                                  inp.seq_lens, wl.sm_scale)
+    q = synth.to_device_bf16(inp.q)
+    bt, sl = synth.to_device(inp.block_tables), synth.to_device(inp.seq_lens)
+    for S in (0, 1, 5):
+        out = nk.fp8_paged_decode_attn(q, kp, vp, bt, sl, wl.sm_scale, num_splits=S)
+        torch.cuda.synchronize()
+        check_out(out, ref, mass, f"fp8 splits={S}")
+    for var in (nk.VARIANT_VALU, nk.VARIANT_MFMA):
+        ws = nk.fp8_paged_decode_partial(q, kp, vp, bt, sl, wl.sm_scale, 3, variant=var)
+        out = torch.empty_like(q)
+        nk.nvfp4kv_lse_merge(ws, q.shape[0], q.shape[1], wl.head_dim, 3, vp.scale, out)
+        torch.cuda.synchronize()
+        check_out(out, ref, mass, f"fp8 variant={var}")
+
+
+# ---------------------------------------------------------------------------
+# the agentic prefix-reuse step at a reduced size
+# ---------------------------------------------------------------------------
+
+def test_agentic_step_small(nk):
+    wl = synth.WORKLOADS[5]
+    a = synth.host_agentic(wl, batch=12, len_min=120, len_max=300, shared_prefix=96, chunk=37)
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    say(f"case agentic step small: B 12 pages {a.num_pages}")
+    kp, vp = gpu_quantize_nv(nk, a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached)
+    shared = torch.from_numpy(a.shared_pages.astype(np.int64)).cuda()
+    shared_before = (kp.data[shared].clone(), kp.scale[shared].clone(), vp.data[shared].clone())
+    # step: quantize the chunk, dequantize prefixes, decode at the new length
+    nk.nvfp4_kv_quantize(synth.to_device_bf16(a.k_chunk), synth.to_device_bf16(a.v_chunk),
+                         synth.to_device(a.slot_chunk), kp, vp)
+    rows = int(a.ws_row_offsets[-1])
+    kws = torch.zeros((rows, H, d), dtype=torch.bfloat16, device="cuda")
+    vws = torch.zeros((rows, H, d), dtype=torch.bfloat16, device="cuda")
+    bt = synth.to_device(a.block_tables)
+    nk.nvfp4_kv_dequant_workspace(kp, vp, bt, synth.to_device(a.cached_lens), synth.to_device(a.ws_row_offsets),
+                                  kws, vws)
+    q = synth.to_device_bf16(a.q)
+    out = nk.nvfp4_paged_decode_attn(q, kp, vp, bt, synth.to_device(a.seq_lens), wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(kp.data[shared], shared_before[0]) and torch.equal(kp.scale[shared], shared_before[1])
+    assert torch.equal(vp.data[shared], shared_before[2])
+    # oracle: the same three steps
+    kd, ks, vd, vs = oracle_nv(a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached)
+    onv.write_cache(kd, ks, a.k_chunk, a.slot_chunk)
+    onv.write_cache(vd, vs, a.v_chunk, a.slot_chunk)
+    assert_pool_equal(kp.data, kd, "K data after step")
+    assert_pool_equal(vp.scale, vs, "V scale after step")
+    kh, vh = onv.dequant_cache(kd, ks), onv.dequant_cache(vd, vs)
+    kref = oatt.dequant_workspace(kh, a.block_tables, a.cached_lens, a.ws_row_offsets, rows)
+    assert np.array_equal(synth.bf16_tensor_bits(kws), kref)
+    ref, mass = oatt.paged_decode(a.q, kh, vh, a.block_tables, a.seq_lens, wl.sm_scale)
+    check_out(out, ref, mass, "agentic decode")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled (launch configuration of the benchmark)
+# ---------------------------------------------------------------------------
+
+def _sample_rows(w, b, g, t0, t1):
+    """bf16 bits of K and V tokens [t0, t1) of sequence b, KV head g (logical order)."""
+    kb = synth.bf16_tensor_bits(w.k_bf16[b, t0:t1, g])
+    vb = synth.bf16_tensor_bits(w.v_bf16[b, t0:t1, g])
+    return kb[:, None, :], vb[:, None, :]
+
+
+def _check_sampled_bytes(w, b, g, t0, t1, rd, rs):
+    """GPU pool bytes of tokens [t0, t1) of (b, g) equal the oracle's encode of the same rows."""
+    P, d = w.wl.page_size, w.wl.head_dim
+    t = np.arange(t0, t1)
+    pages = torch.from_numpy(w.bt[b].cpu().numpy()[t // P].astype(np.int64)).cuda()
+    offs = torch.from_numpy(t % P).cuda()
+    gd = w.kp.data[pages, g, offs].cpu().numpy()
+    gsc = w.kp.scale[pages, g, offs].cpu().numpy()
+    assert np.array_equal(gd, rd[:, 0]) and np.array_equal(gsc, rs[:, 0]), "sampled K bytes"
+
+
+def test_full_size_long_context_32k_sampled(nk):
+    """Batch 44, 32K context, 32 splits (the benchmark's launch): whole (b, g)
+    outputs against the oracle over all 32,768 tokens."""
+    from synth.workload import build_uniform_workload
+    wl = synth.WORKLOADS[3]
+    say(f"case full size {wl.name}: B {wl.batch} L {wl.context} splits {wl.num_splits}")
+    w = build_uniform_workload(nk, wl, keep_bf16=True)
+    out = nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.sl, wl.sm_scale, num_splits=wl.num_splits)
+    torch.cuda.synchronize()
+    G = wl.group
+    rng = np.random.default_rng(15)
+    for b, g in [(0, 0), (43, 7), (int(rng.integers(44)), int(rng.integers(8)))]:
+        say(f"  sample b {b} g {g}")
+        kb, vb = _sample_rows(w, b, g, 0, wl.context)
+        rd, rs = onv.quantize_rows(kb)
+        _check_sampled_bytes(w, b, g, 0, wl.context, rd, rs)
+        vd_, vs_ = onv.quantize_rows(vb)
+        qb = synth.bf16_tensor_bits(w.q[b, g * G:(g + 1) * G])
+        ref, mass = oatt.decode_heads(onv.bf16_to_f64(qb), onv.dequant_rows(rd, rs), onv.dequant_rows(vd_, vs_),
+                                      wl.sm_scale)
+        check_out(out[b, g * G:(g + 1) * G], ref, mass, f"{wl.name} b{b} g{g}")
+    del w
+    torch.cuda.empty_cache()
+
+
+def test_full_size_extreme_context_1m_sampled(nk):
+    """Batch 2, 1M context, 256 splits (the benchmark's launch). Each sampled
+    split's normalised partial o/l is checked against the oracle's attention
+    over that split's 4,096 tokens, and the merged output against an fp64
+    log-sum-exp merge of all the kernel's partials (a property that holds at
+    any size)."""
+    from synth.workload import build_uniform_workload
+    wl = synth.WORKLOADS[4]
+    S, G, d = wl.num_splits, wl.group, wl.head_dim
+    say(f"case full size {wl.name}: B {wl.batch} L {wl.context} splits {S}")
+    w = build_uniform_workload(nk, wl, keep_bf16=True)
+    B, Hq = w.q.shape[0], w.q.shape[1]
+    ws = nk.nvfp4_paged_decode_partial(w.q, w.kp, w.vp, w.bt, w.sl, wl.sm_scale, S)
+    out = torch.empty_like(w.q)
+    nk.nvfp4kv_lse_merge(ws, B, Hq, d, S, 1.0, out)
+    torch.cuda.synchronize()
+    po, pml = nk.split_partials(ws, B, Hq, d, S)
+    po, pml = po.double().cpu().numpy(), pml.double().cpu().numpy()
+    per = wl.context // S
+    rng = np.random.default_rng(16)
+    for b, g, j in [(0, 3, 0), (1, 5, S - 1), (int(rng.integers(2)), int(rng.integers(8)), int(rng.integers(S)))]:
+        say(f"  sample b {b} g {g} split {j}")
+        kb, vb = _sample_rows(w, b, g, j * per, (j + 1) * per)
+        rd, rs = onv.quantize_rows(kb)
+        _check_sampled_bytes(w, b, g, j * per, (j + 1) * per, rd, rs)
+        vd_, vs_ = onv.quantize_rows(vb)
+        qb = synth.bf16_tensor_bits(w.q[b, g * G:(g + 1) * G])
+        qf = onv.bf16_to_f64(qb)
+        khat = onv.dequant_rows(rd, rs)
+        ref, mass = oatt.decode_heads(qf, khat, onv.dequant_rows(vd_, vs_), wl.sm_scale)
+        hs = slice(g * G, (g + 1) * G)
+        part = po[b, hs, j] / pml[b, hs, j, 1:2]
+        e = np.abs(part - ref) / np.maximum(1.0, mass)
+        say(f"    partial max e {e.max():.3e} mean e {e.mean():.3e}")
+        assert e.max() <= TOL_MAX and e.mean() <= TOL_MEAN
+        mref = (np.einsum("gd,td->gt", qf, khat[:, 0]) * wl.sm_scale).max(axis=1) / math.log(2.0)
+        assert np.allclose(pml[b, hs, j, 0], mref, rtol=1e-4, atol=1e-3)
+    M = pml[..., 0].max(axis=2, keepdims=True)
+    wgt = np.exp2(pml[..., 0] - M)
+    merged = (po * wgt[..., None]).sum(axis=2) / (pml[..., 1] * wgt).sum(axis=2)[..., None]
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - merged) <= 2.0 ** -8 * np.abs(merged) + 1e-6), "merge property"
+    del w, ws
+    torch.cuda.empty_cache()
