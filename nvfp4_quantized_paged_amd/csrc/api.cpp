@@ -142,6 +142,7 @@ DecodeParams make_decode(const nvfp4kv_geom* g, const void* q, const uint8_t* kd
   p.group = c.group;
   p.page_size = g->page_size;
   p.num_splits = c.splits;
+  p.num_pages = g->num_pages;
   p.qk_scale = sm_scale * gs_k * 1.4426950408889634f;
   return p;
 }

@@ -124,6 +124,7 @@ struct DecodeParams {
   float* part_o;            // [B][Hq][S][D]
   float* part_ml;           // [B][Hq][S][2]
   int32_t max_pages, batch, num_q_heads, num_kv_heads, group, page_size, num_splits;
+  int32_t num_pages;        // pool size: page indices are clamped into [0, num_pages)
   float qk_scale;           // sm_scale * K global scale * log2(e)
 };
 

@@ -15,7 +15,7 @@
 //    f16 pair (hardware scale operand 1.0: the E4M3 block scale is not a power
 //    of two), then v_pk_mul_f16 applies the block scale. Every E2M1 x E4M3
 //    product is exact in f16, so the dequantized K/V are exact.
-//  * QK: A = K (16 tokens x 32 channels per MFMA, one 128-bit load per lane
+//  * QK: A = K (16 tokens x 32 channels per MFMA; one 128-bit load per lane
 //    covers four MFMAs: lane (row r, group g) holds channels
 //    [g*D/4, (g+1)*D/4) of token r), B = q (f16, scaled into f16 range by a
 //    power of two). C[t][h]: lane (h, g) holds tokens 4g..4g+3 of the tile.
@@ -29,8 +29,11 @@
 //    operand of O^T[c][h] += V^T[c][t] P[t][h], and the softmax output C of
 //    the same two tiles is already the B operand in the same lane: no
 //    cross-lane data movement anywhere in the loop.
-//  * Loads: direct 128-bit global loads into registers, one chunk (64 tokens
-//    NVFP4, 32 tokens FP8) prefetched while the previous chunk computes.
+//  * Loads: buffer loads from a per-page descriptor built in scalar
+//    registers (page from the block table, clamped into the pool), with a
+//    fixed per-lane offset, so no vector ALU goes into addressing and no
+//    load can leave the page's slice. Registers hold three chunks (64 tokens
+//    NVFP4, 32 tokens FP8): one computing, two in flight.
 #include "common.hpp"
 
 namespace nvfp4kv {
@@ -42,6 +45,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
 
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer descriptor, 32-bit data format
 
 template <int D, bool FP8>
 struct Cfg {
@@ -50,6 +54,7 @@ struct Cfg {
   static constexpr int kRowBytes = FP8 ? D : D / 2;    // bytes of one token row
   static constexpr int kLaneBytes = kRowBytes / 4;     // bytes per lane per tile
   static constexpr int kLaneWords = kLaneBytes / 4;
+  static constexpr int kScaleRow = D / kBlock;         // NVFP4 scale bytes per token row
   static constexpr int kKSteps = D / 32;               // QK MFMAs per tile
   static constexpr int kCTiles = D / 16;               // PV output channel tiles
   static constexpr int kChanPerGroup = D / 4;          // channels per lane group
@@ -112,47 +117,61 @@ __device__ inline half8_t pack_half8(const float4_t& x, const float4_t& y) {
   return __builtin_bit_cast(half8_t, w);
 }
 
+// Wave-uniform state of one work item.
+struct Item {
+  const int32_t* bt;     // block-table row of the sequence
+  int g, t1;
+};
+
 template <int D, bool FP8>
-__device__ inline void load_tile(const DecodeParams& p, const int32_t* bt, int g, int tok0, int t1, int lane,
+__device__ inline void load_tile(const DecodeParams& p, const Item& it, int tok0, int lane,
                                  TileRaw<D, FP8>& raw) {
   using C = Cfg<D, FP8>;
   const int r = lane & 15, grp = lane >> 4;
-  if (tok0 < t1) {
+  if (tok0 < it.t1) {
     const int P = p.page_size;
-    const int64_t row = ((int64_t)bt[tok0 / P] * p.num_kv_heads + g) * P + (tok0 % P) + r;
-    const uint8_t* kp = p.kd + row * C::kRowBytes + grp * C::kLaneBytes;
-    const uint8_t* vp = p.vd + row * C::kRowBytes + grp * C::kLaneBytes;
+    int page = __builtin_amdgcn_readfirstlane(it.bt[tok0 / P]);
+    page = min(max(page, 0), p.num_pages - 1);
+    const int64_t slice = ((int64_t)page * p.num_kv_heads + it.g) * P;     // first row of the (page, head) slice
+    const int soff = (tok0 % P) * C::kRowBytes;
+    const int voff = r * C::kRowBytes + grp * C::kLaneBytes;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.kd + slice * C::kRowBytes), (short)0, P * C::kRowBytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.vd + slice * C::kRowBytes), (short)0, P * C::kRowBytes, kRsrcWord3);
     if constexpr (C::kLaneWords == 2) {
-      const uint2 a = *reinterpret_cast<const uint2*>(kp);
-      const uint2 b = *reinterpret_cast<const uint2*>(vp);
-      raw.k[0] = a.x; raw.k[1] = a.y;
-      raw.v[0] = b.x; raw.v[1] = b.y;
+      const auto a = __builtin_amdgcn_raw_buffer_load_b64(rk, voff, soff, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, soff, 0);
+      raw.k[0] = a[0]; raw.k[1] = a[1];
+      raw.v[0] = b[0]; raw.v[1] = b[1];
     } else {
 #pragma unroll
       for (int w = 0; w < C::kLaneWords / 4; ++w) {
-        const uint4 a = reinterpret_cast<const uint4*>(kp)[w];
-        const uint4 b = reinterpret_cast<const uint4*>(vp)[w];
-        raw.k[4 * w] = a.x; raw.k[4 * w + 1] = a.y; raw.k[4 * w + 2] = a.z; raw.k[4 * w + 3] = a.w;
-        raw.v[4 * w] = b.x; raw.v[4 * w + 1] = b.y; raw.v[4 * w + 2] = b.z; raw.v[4 * w + 3] = b.w;
-      }
-    }
-    if constexpr (!FP8) {
-      constexpr int nb = D / kBlock;
-      if constexpr (D == 128) {
-        raw.ks = *reinterpret_cast<const uint16_t*>(p.ks + row * nb + 2 * grp);
-        raw.vs = *reinterpret_cast<const uint16_t*>(p.vs + row * nb + 2 * grp);
-      } else {
-        raw.ks = p.ks[row * nb + grp];
-        raw.vs = p.vs[row * nb + grp];
-      }
-    }
-    // tokens past the end: V must be exactly zero (the bytes there are arbitrary)
-    if (tok0 + r >= t1) {
-      if constexpr (FP8) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 16 * w, soff, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + 16 * w, soff, 0);
 #pragma unroll
-        for (int w = 0; w < C::kLaneWords; ++w) raw.v[w] = 0;
+        for (int e = 0; e < 4; ++e) {
+          raw.k[4 * w + e] = a[e];
+          raw.v[4 * w + e] = b[e];
+        }
+      }
+    }
+    if constexpr (FP8) {
+      raw.ks = 0;
+      raw.vs = 0;
+    } else {
+      constexpr int nb = C::kScaleRow;
+      const __amdgpu_buffer_rsrc_t sk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.ks + slice * nb), (short)0, P * nb, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t sv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.vs + slice * nb), (short)0, P * nb, kRsrcWord3);
+      const int so = (tok0 % P) * nb;
+      if constexpr (D == 128) {
+        raw.ks = __builtin_amdgcn_raw_buffer_load_b16(sk, r * nb + 2 * grp, so, 0);
+        raw.vs = __builtin_amdgcn_raw_buffer_load_b16(sv, r * nb + 2 * grp, so, 0);
       } else {
-        raw.vs = 0;
+        raw.ks = __builtin_amdgcn_raw_buffer_load_b8(sk, r * nb + grp, so, 0);
+        raw.vs = __builtin_amdgcn_raw_buffer_load_b8(sv, r * nb + grp, so, 0);
       }
     }
   } else {
@@ -164,28 +183,131 @@ __device__ inline void load_tile(const DecodeParams& p, const int32_t* bt, int g
 }
 
 template <int D, bool FP8>
+__device__ inline void load_chunk(const DecodeParams& p, const Item& it, int ts, int lane,
+                                  TileRaw<D, FP8> (&buf)[Cfg<D, FP8>::kTiles]) {
+#pragma unroll
+  for (int t = 0; t < Cfg<D, FP8>::kTiles; ++t) load_tile<D, FP8>(p, it, ts + 16 * t, lane, buf[t]);
+}
+
+// Running softmax state and output accumulators of one wave.
+template <int D>
+struct Acc {
+  float4_t o[D / 16];
+  float m, l;
+};
+
+// One chunk: QK, online softmax, PV. `cs` > 0 maps raw scores to base-2 logits.
+template <int D, bool FP8>
+__device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D, FP8> (&cur)[Cfg<D, FP8>::kTiles],
+                                     const half8_t (&qb)[Cfg<D, FP8>::kKSteps], const half8_t (&sel)[2], float cs,
+                                     Acc<D>& a) {
+  using C = Cfg<D, FP8>;
+  const int grp = lane >> 4;
+
+  // ---- QK: raw scores, lane (head, rows 4grp..4grp+3) of every tile
+  float sc[C::kTiles][4];
+#pragma unroll
+  for (int t = 0; t < C::kTiles; ++t) {
+    float4_t c4 = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C::kKSteps; ++kk) c4 = mfma(unpack<D, FP8>(cur[t].k, cur[t].ks, kk), qb[kk], c4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[t][i] = c4[i];
+  }
+
+  // ---- the chunk that crosses the end of the split: mask scores, zero V past the end
+  if (ts + C::kChunk > it.t1) {
+    const int r = lane & 15;
+#pragma unroll
+    for (int t = 0; t < C::kTiles; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (ts + 16 * t + 4 * grp + i >= it.t1) sc[t][i] = -INFINITY;
+      if (ts + 16 * t + r >= it.t1) {
+        if constexpr (FP8) {
+#pragma unroll
+          for (int w = 0; w < C::kLaneWords; ++w) cur[t].v[w] = 0;
+        } else {
+          cur[t].vs = 0;
+        }
+      }
+    }
+  }
+
+  // ---- online softmax (base 2) per head
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < C::kTiles; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[t][i]);
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  const float mnew = fmaxf(a.m, cmax * cs);
+  const float alpha = __builtin_amdgcn_exp2f(a.m - mnew);
+  a.m = mnew;
+  float psum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < C::kTiles; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[t][i] = __builtin_amdgcn_exp2f(fmaf(sc[t][i], cs, -mnew));
+      psum += sc[t][i];
+    }
+  a.l = a.l * alpha + psum;
+  if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+    for (int c = 0; c < C::kCTiles; ++c) a.o[c] *= alpha;
+  }
+
+  // ---- PV over pairs of tiles (32 tokens = one MFMA K)
+#pragma unroll
+  for (int t = 0; t < C::kTiles; t += 2) {
+    const half8_t pb = pack_half8(float4_t{sc[t][0], sc[t][1], sc[t][2], sc[t][3]},
+                                  float4_t{sc[t + 1][0], sc[t + 1][1], sc[t + 1][2], sc[t + 1][3]});
+#pragma unroll
+    for (int kk = 0; kk < C::kKSteps; ++kk) {
+      const half8_t va = unpack<D, FP8>(cur[t].v, cur[t].vs, kk);
+      const half8_t vb = unpack<D, FP8>(cur[t + 1].v, cur[t + 1].vs, kk);
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        const float4_t zero = float4_t{0.f, 0.f, 0.f, 0.f};
+        const float4_t da = mfma(va, sel[hs], zero);     // tile t,   transposed
+        const float4_t db = mfma(vb, sel[hs], zero);     // tile t+1, transposed
+        a.o[2 * kk + hs] = mfma(pack_half8(da, db), pb, a.o[2 * kk + hs]);
+      }
+    }
+  }
+}
+
+template <int D, bool FP8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partial_mfma_kernel(DecodeParams p) {
   using C = Cfg<D, FP8>;
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int col = lane & 15;        // head (QK/PV columns) or channel (transpose columns)
-  const int grp = lane >> 4;        // lane group: token rows 4grp..4grp+3 of a tile
+  const int grp = lane >> 4;        // lane group
   const int G = p.group;
   const int S = p.num_splits;
   const int L = p.seq_lens[b];
   const int P = p.page_size;
   const int per = ceil_div(ceil_div(L, S), P) * P;
   const int t0 = j * per;
-  const int t1 = min(L, t0 + per);
+  const Item it{p.block_tables + (int64_t)b * p.max_pages, g, min(L, t0 + per)};
   const int64_t qh0 = (int64_t)b * p.num_q_heads + (int64_t)g * G;
 
-  float4_t acc[C::kCTiles];
+  Acc<D> a;
 #pragma unroll
-  for (int c = 0; c < C::kCTiles; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.0f;
+  for (int c = 0; c < C::kCTiles; ++c) a.o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  a.m = -INFINITY;
+  a.l = 0.0f;
 
-  if (t0 < t1) {
+  if (t0 < it.t1) {
+    TileRaw<D, FP8> b0[C::kTiles], b1[C::kTiles], b2[C::kTiles];
+    load_chunk<D, FP8>(p, it, t0, lane, b0);
+    load_chunk<D, FP8>(p, it, t0 + C::kChunk, lane, b1);
+    load_chunk<D, FP8>(p, it, t0 + 2 * C::kChunk, lane, b2);
+
     // ---- q as the B operand: lane (head col, group grp), step kk: channels grp*D/4 + 8kk .. +7
     const bool hv = col < G;
     float qf[C::kKSteps][8];
@@ -204,16 +326,17 @@ void decode_partial_mfma_kernel(DecodeParams p) {
     }
     qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
     qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
-    // power-of-two shift that keeps the head's largest |q| below 2^15 in f16
+    // power-of-two shift keeping the head's largest |q| below 2^15 in f16; the
+    // sign of the logit scale moves into q so that the scale is positive
     const int qexp = (qmax > 0.0f) ? max(0, (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 14) : 0;
-    const float qdown = __uint_as_float((uint32_t)(127 - qexp) << 23);
+    const float sgn = p.qk_scale < 0.0f ? -1.0f : 1.0f;
+    const float qdown = sgn * __uint_as_float((uint32_t)(127 - qexp) << 23);
     half8_t qb[C::kKSteps];
 #pragma unroll
     for (int kk = 0; kk < C::kKSteps; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qb[kk][e] = (_Float16)(qf[kk][e] * qdown);
-    // scaled logit (base 2) = raw score * c
-    const float cscale = p.qk_scale * __uint_as_float((uint32_t)(127 + qexp) << 23);
+    const float cs = fabsf(p.qk_scale) * __uint_as_float((uint32_t)(127 + qexp) << 23);
 
     // ---- 0/1 selection operands for the V transposes: column n takes A slot (group 2hs + n/8, item n%8)
     half8_t sel[2];
@@ -223,82 +346,21 @@ void decode_partial_mfma_kernel(DecodeParams p) {
       for (int e = 0; e < 8; ++e)
         sel[hs][e] = (grp == 2 * hs + (col >> 3) && e == (col & 7)) ? (_Float16)1.0f : (_Float16)0.0f;
 
-    const int32_t* bt = p.block_tables + (int64_t)b * p.max_pages;
-    TileRaw<D, FP8> cur[C::kTiles], nxt[C::kTiles];
-#pragma unroll
-    for (int t = 0; t < C::kTiles; ++t) load_tile<D, FP8>(p, bt, g, t0 + 16 * t, t1, lane, cur[t]);
-
-    for (int ts = t0; ts < t1; ts += C::kChunk) {
-      // prefetch the next chunk
-#pragma unroll
-      for (int t = 0; t < C::kTiles; ++t)
-        load_tile<D, FP8>(p, bt, g, ts + C::kChunk + 16 * t, t1, lane, nxt[t]);
-
-      // ---- QK: scores of the chunk, lane (head col, rows 4grp..) per tile
-      float sc[C::kTiles][4];
-#pragma unroll
-      for (int t = 0; t < C::kTiles; ++t) {
-        float4_t c4 = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < C::kKSteps; ++kk) c4 = mfma(unpack<D, FP8>(cur[t].k, cur[t].ks, kk), qb[kk], c4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = ts + 16 * t + 4 * grp + i;
-          sc[t][i] = (tok < t1) ? c4[i] * cscale : -INFINITY;
-        }
-      }
-
-      // ---- online softmax (base 2) per head
-      float cmax = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < C::kTiles; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[t][i]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      const float mnew = fmaxf(m, cmax);
-      const float alpha = exp2f(m - mnew);
-      m = mnew;
-      float psum = 0.0f;
-#pragma unroll
-      for (int t = 0; t < C::kTiles; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[t][i] = exp2f(sc[t][i] - mnew);
-          psum += sc[t][i];
-        }
-      l = l * alpha + psum;
-      if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-        for (int c = 0; c < C::kCTiles; ++c) acc[c] *= alpha;
-      }
-
-      // ---- PV over pairs of tiles (32 tokens = one MFMA K)
-#pragma unroll
-      for (int t = 0; t < C::kTiles; t += 2) {
-        const half8_t pb = pack_half8(float4_t{sc[t][0], sc[t][1], sc[t][2], sc[t][3]},
-                                      float4_t{sc[t + 1][0], sc[t + 1][1], sc[t + 1][2], sc[t + 1][3]});
-#pragma unroll
-        for (int kk = 0; kk < C::kKSteps; ++kk) {
-          const half8_t va = unpack<D, FP8>(cur[t].v, cur[t].vs, kk);
-          const half8_t vb = unpack<D, FP8>(cur[t + 1].v, cur[t + 1].vs, kk);
-#pragma unroll
-          for (int hs = 0; hs < 2; ++hs) {
-            const float4_t zero = float4_t{0.f, 0.f, 0.f, 0.f};
-            const float4_t da = mfma(va, sel[hs], zero);     // tile t,   transposed
-            const float4_t db = mfma(vb, sel[hs], zero);     // tile t+1, transposed
-            acc[2 * kk + hs] = mfma(pack_half8(da, db), pb, acc[2 * kk + hs]);
-          }
-        }
-      }
-
-#pragma unroll
-      for (int t = 0; t < C::kTiles; ++t) cur[t] = nxt[t];
+    // three register buffers: compute one chunk while the next two are in flight
+    for (int ts = t0; ts < it.t1; ts += 3 * C::kChunk) {
+      process_chunk<D, FP8>(it, ts, lane, b0, qb, sel, cs, a);
+      load_chunk<D, FP8>(p, it, ts + 3 * C::kChunk, lane, b0);
+      if (ts + C::kChunk >= it.t1) break;
+      process_chunk<D, FP8>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
+      load_chunk<D, FP8>(p, it, ts + 4 * C::kChunk, lane, b1);
+      if (ts + 2 * C::kChunk >= it.t1) break;
+      process_chunk<D, FP8>(it, ts + 2 * C::kChunk, lane, b2, qb, sel, cs, a);
+      load_chunk<D, FP8>(p, it, ts + 5 * C::kChunk, lane, b2);
     }
   }
 
   // ---- partial results: lane (head col, channel group grp)
-  float lt = l + __shfl_xor(l, 16, 64);
+  float lt = a.l + __shfl_xor(a.l, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
   if (col < G) {
     const int64_t idx = (qh0 + col) * S + j;
@@ -308,11 +370,11 @@ void decode_partial_mfma_kernel(DecodeParams p) {
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         const int ch = (2 * hs + (grp >> 1)) * C::kChanPerGroup + 8 * kk + 4 * (grp & 1);
-        const float4_t a = acc[2 * kk + hs];
-        *reinterpret_cast<float4*>(o + ch) = make_float4(a[0], a[1], a[2], a[3]);
+        const float4_t v = a.o[2 * kk + hs];
+        *reinterpret_cast<float4*>(o + ch) = make_float4(v[0], v[1], v[2], v[3]);
       }
     if (grp == 0) {
-      p.part_ml[idx * 2] = m;
+      p.part_ml[idx * 2] = a.m;
       p.part_ml[idx * 2 + 1] = lt;
     }
   }
