@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "NVFP4 paged decode attn: KV GB/s + % HBM roofline; steps/s vs FP8-KV kernel"
-DECODE_SOURCES = ["nvfp4_quantized_paged_amd/csrc/decode_mfma.hip", "nvfp4_quantized_paged_amd/csrc/decode_valu.hip",
+DECODE_SOURCES = ["nvfp4_quantized_paged_amd/csrc/decode_mfma.hip",
                   "nvfp4_quantized_paged_amd/csrc/common.hpp"]
 
 
@@ -194,9 +194,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--variant", choices=["auto", "valu", "mfma"], default="auto")
-    ap.add_argument("--only", choices=["nvfp4", "all"], default="all",
-                    help="nvfp4: only the headline NVFP4 step (for profiling)")
+    ap.add_argument("--only", choices=["nvfp4", "fp8", "all"], default="all",
+                    help="nvfp4 / fp8: only that 32K decode step (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path runs on a single "
@@ -208,9 +210,24 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+        return
     nk.lib()
     variant = {"auto": nk.VARIANT_AUTO, "valu": nk.VARIANT_VALU, "mfma": nk.VARIANT_MFMA}[args.variant]
     wl = synth.WORKLOADS[3]
+    if args.only == "fp8":
+        f8 = Bench(nk, wl, True, variant)
+        t8 = f8.time_steps(args.steps, args.warmup)
+        log(f"[bench] fp8 step {t8 * 1e3:.3f} ms")
+        print(json.dumps({"fp8_ms_per_step": round(t8 * 1e3, 4)}))
+        return
 
     nv = Bench(nk, wl, False, variant)
     t_step = nv.time_steps(args.steps, args.warmup)
