@@ -147,6 +147,66 @@ class Bench:
         self.torch.cuda.empty_cache()
 
 
+def agentic(nk, wl, steps, warmup):
+    """The prefix-reuse step (quantize the new chunk, dequantize every cached
+    prefix into the workspace, decode all sequences): whole-step time and
+    each kernel's mean duration from HIP events on the launch stream."""
+    import torch
+    from synth.workload import agentic_bytes, build_agentic_workload
+    t = time.time()
+    w = build_agentic_workload(nk, wl)
+    log(f"[bench] built agentic workload in {time.time() - t:.1f}s")
+    B, Hq, d = wl.batch, wl.num_q_heads, wl.head_dim
+    S = nk.nvfp4_paged_decode_num_splits(B, wl.num_kv_heads, w.bt.shape[1], wl.page_size)
+    ws = nk.decode_workspace(B, Hq, d, S)
+    out = torch.empty_like(w.q)
+    calls = [
+        ("quantize", lambda: nk.nvfp4_kv_quantize(w.k_chunk, w.v_chunk, w.slot_chunk, w.kp, w.vp)),
+        ("dequant_workspace", lambda: nk.nvfp4_kv_dequant_workspace(w.kp, w.vp, w.bt, w.cached_lens,
+                                                                    w.ws_row_offsets, w.k_ws, w.v_ws)),
+        ("decode", lambda: nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale,
+                                                      num_splits=S, workspace=ws, out=out)),
+    ]
+    for _ in range(warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    stream = torch.cuda.current_stream()
+    per = {}
+    for name, f in calls:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            f()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per[name] = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+    by = agentic_bytes(w)
+    res = {
+        "ms_per_step": round(t_step * 1e3, 4), "steps_per_s": round(1.0 / t_step, 2), "num_splits": S,
+        "quantize": {"ms": round(per["quantize"] * 1e3, 4),
+                     "gbs": round((by["quant_read"] + by["quant_write"]) / per["quantize"] / 1e9, 1)},
+        "dequant_workspace": {"ms": round(per["dequant_workspace"] * 1e3, 4),
+                              "gbs_unique": round((by["dequant_read_unique"] + by["dequant_write"])
+                                                  / per["dequant_workspace"] / 1e9, 1),
+                              "write_gbs": round(by["dequant_write"] / per["dequant_workspace"] / 1e9, 1)},
+        "decode": {"ms": round(per["decode"] * 1e3, 4),
+                   "kv_gbs_logical": round(by["decode_read_logical"] / per["decode"] / 1e9, 1),
+                   "kv_gbs_unique": round(by["decode_read_unique"] / per["decode"] / 1e9, 1)},
+        "bytes": by,
+    }
+    log(f"[bench] agentic step {t_step * 1e3:.3f} ms: " + ", ".join(f"{k} {v * 1e3:.3f} ms" for k, v in per.items()))
+    del w, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle (dequantize + fp64 attention) on (sequence, KV head) slices of
     the workload, single-threaded, until ~budget_s of work."""
@@ -284,6 +344,8 @@ def main():
             "hbm_roofline_frac": round((kv_bytes(wl4) + io_bytes(wl4)) / t4 / 1e9 / HBM_PEAK_GBS, 4),
             "num_splits": wl4.num_splits}
         log(f"[bench] 1m step {t4 * 1e3:.3f} ms")
+
+        result["agentic_prefix_reuse"] = agentic(nk, synth.WORKLOADS[5], max(5, args.steps // 2), args.warmup)
 
     if not args.no_cpu_baseline:
         t = time.time()

@@ -30,9 +30,11 @@
  *    of the last failure on the calling thread is nvfp4kv_last_error().
  *    No C++ exception crosses the ABI.
  *  - Data-dependent contract violations cannot be checked on the host and
- *    are undefined behaviour: block-table entries >= num_pages, seq_len or
- *    prefix_len > max_pages_per_seq * page_size, slots outside the pool, or
- *    two tokens of one call mapping to the same slot.
+ *    are undefined behaviour: block-table entries outside [0, num_pages),
+ *    seq_len or prefix_len > max_pages_per_seq * page_size, or two tokens of
+ *    one call mapping to the same slot. (As a safety net, not a guarantee of
+ *    meaningful results, the MFMA decode and the workspace kernels clamp page
+ *    indices into the pool and quantize skips slots outside it.)
  *  - bf16 tensors are IEEE bfloat16 bit patterns (uint16). Base pointers of
  *    packed/bf16 buffers must be 16-byte aligned (128-bit accesses).
  *  - Supported shapes: head_dim 64 or 128; page_size a positive multiple of
@@ -105,7 +107,8 @@ typedef struct {
  *   k, v          device bf16; element (t, h, c) at [t * src_token_stride + h * d + c]
  *   src_token_stride  elements between consecutive tokens (>= Hkv * d, multiple of 8)
  *   num_tokens    T >= 0 (0 is a no-op)
- *   slot_mapping  device int64 [T]; slot of token t, or < 0 to skip the token
+ *   slot_mapping  device int64 [T]; slot of token t; a slot < 0 or >= num_pages * page_size
+ *                 skips the token
  *   k_cache, v_cache  the two pools (data and scale are written at the slots)
  *
  * Per token, head and 16-channel block with amax = max|x|:

@@ -221,6 +221,7 @@ NVFP4KV_API int nvfp4_kv_quantize(const nvfp4kv_geom* geom, const void* k, const
   p.num_kv_heads = geom->num_kv_heads;
   p.head_dim = geom->head_dim;
   p.page_size = geom->page_size;
+  p.num_slots = (int64_t)geom->num_pages * geom->page_size;
   p.data[0] = k_cache->data;
   p.data[1] = v_cache->data;
   p.scale[0] = k_cache->scale;
@@ -250,6 +251,7 @@ NVFP4KV_API int fp8_kv_quantize(const nvfp4kv_geom* geom, const void* k, const v
   p.num_kv_heads = geom->num_kv_heads;
   p.head_dim = geom->head_dim;
   p.page_size = geom->page_size;
+  p.num_slots = (int64_t)geom->num_pages * geom->page_size;
   p.data[0] = k_cache->data;
   p.data[1] = v_cache->data;
   p.gscale[0] = k_cache->scale;
@@ -267,7 +269,7 @@ NVFP4KV_API int nvfp4_kv_dequant_workspace(const nvfp4kv_geom* geom, const nvfp4
   if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
       (rc = check_nvfp4_cache(v_cache, "V", fn)))
     return rc;
-  if (batch < 0) return fail(NVFP4KV_EINVAL, "%s: batch %d < 0", fn, batch);
+  if (batch < 0 || batch > kGridYZ) return fail(NVFP4KV_EINVAL, "%s: batch %d out of range [0, %d]", fn, batch, kGridYZ);
   if (batch == 0) return launched(hipSuccess, fn);
   if (!block_tables || !prefix_lens || !ws_row_offsets || !k_ws || !v_ws)
     return fail(NVFP4KV_EINVAL, "%s: block_tables, prefix_lens, ws_row_offsets, k_ws and v_ws must be non-NULL", fn);
@@ -288,6 +290,7 @@ NVFP4KV_API int nvfp4_kv_dequant_workspace(const nvfp4kv_geom* geom, const nvfp4
   p.num_kv_heads = geom->num_kv_heads;
   p.head_dim = geom->head_dim;
   p.page_size = geom->page_size;
+  p.num_pages = geom->num_pages;
   p.ws[0] = static_cast<uint16_t*>(k_ws);
   p.ws[1] = static_cast<uint16_t*>(v_ws);
   return launched(launch_nvfp4_dequant_ws(p, static_cast<hipStream_t>(stream)), fn);

@@ -29,6 +29,15 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two f32 -> packed bf16 pair (a in the low half), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // Non-negative f32 -> OCP E4M3FN byte: nearest value, ties to even, saturating
 // at 448 (0x7E). NaN -> 0x7F. Normal range rounds the f32 mantissa to 3 bits;
 // below 2^-6 the grid is k * 2^-9 and k = rint(x * 512) (exact scaling).
@@ -97,6 +106,7 @@ struct QuantizeParams {
   int64_t src_stride;       // elements between tokens
   const int64_t* slot_mapping;
   int32_t num_tokens, num_kv_heads, head_dim, page_size;
+  int64_t num_slots;        // num_pages * page_size: slots at or past it are skipped like negative ones
   uint8_t* data[2];         // NVFP4 data or FP8 bytes
   uint8_t* scale[2];        // NVFP4 block scales (unused for FP8)
   float gscale[2];          // NVFP4 global scale / FP8 per-tensor scale
@@ -110,6 +120,7 @@ struct WorkspaceParams {
   const int32_t* prefix_lens;
   const int64_t* row_offsets;
   int32_t max_pages, batch, num_kv_heads, head_dim, page_size;
+  int32_t num_pages;        // page indices are clamped into [0, num_pages)
   uint16_t* ws[2];
 };
 

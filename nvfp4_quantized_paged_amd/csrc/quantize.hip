@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(QuantizeParams p) {
   const int h = (int)(th % p.num_kv_heads);
   const int64_t t = th / p.num_kv_heads;
   const int64_t slot = p.slot_mapping[t];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= p.num_slots) return;
 
   float x[16];
   load_block16(p.src[which] + t * p.src_stride + (int64_t)h * p.head_dim + blk * kBlock, x);
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(QuantizeParams p) {
   const int h = (int)(th % p.num_kv_heads);
   const int64_t t = th / p.num_kv_heads;
   const int64_t slot = p.slot_mapping[t];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= p.num_slots) return;
 
   float x[16];
   load_block16(p.src[which] + t * p.src_stride + (int64_t)h * p.head_dim + blk * kBlock, x);

@@ -180,7 +180,11 @@ def test_quantize_crafted_values_and_skipped_slots(nk, gs):
         v = _crafted_rows(rng, T, H, d)
     slots = rng.permutation(pages * P)[:T].astype(np.int64)
     slots[rng.random(T) < 0.05] = -1                           # padding tokens
-    kp, vp = gpu_quantize_nv(nk, pages, H, P, d, k, v, slots, gs)
+    outside = rng.random(T) < 0.02                             # slots past the pool are skipped too
+    slots_gpu = slots.copy()
+    slots_gpu[outside] = pages * P + rng.integers(0, 1 << 20, size=int(outside.sum()))
+    slots[outside] = -1
+    kp, vp = gpu_quantize_nv(nk, pages, H, P, d, k, v, slots_gpu, gs)
     kd, ks, vd, vs = oracle_nv(pages, H, P, d, k, v, slots, gs)
     for t, r, n in ((kp.data, kd, "K data"), (kp.scale, ks, "K scale"), (vp.data, vd, "V data"),
                     (vp.scale, vs, "V scale")):
@@ -249,9 +253,12 @@ def test_fp8_quantize_every_bf16_value(nk):
 # dequantize-to-workspace
 # ---------------------------------------------------------------------------
 
-def test_dequant_workspace_agentic_small(nk):
-    wl = synth.WORKLOADS[5]
-    a = synth.host_agentic(wl, batch=7, len_min=48, len_max=131, shared_prefix=32, chunk=9)
+@pytest.mark.parametrize("shape", [(8, 128, 16), (1, 64, 16), (3, 64, 32)])
+def test_dequant_workspace_agentic_small(nk, shape):
+    H0, d0, P0 = shape
+    wl = synth.Workload(95, "ws", 7, 2 * H0, H0, d0, P0, 0, False, 0, len_min=48, len_max=131,
+                        shared_prefix=32, chunk=9)
+    a = synth.host_agentic(wl)
     H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
     say(f"case workspace small agentic: B 7 pages {a.num_pages}")
     kp, vp = gpu_quantize_nv(nk, a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached)
@@ -507,4 +514,52 @@ def test_full_size_extreme_context_1m_sampled(nk):
     got = out.float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - merged) <= 2.0 ** -8 * np.abs(merged) + 1e-6), "merge property"
     del w, ws
+    torch.cuda.empty_cache()
+
+
+def test_full_size_agentic_sampled(nk):
+    """64 sequences, L_b ~ U[3200, 10000], a 2,800-token prefix on 175 shared
+    pages, 500-token chunks: the whole step at full size, then sampled
+    sequences checked against the oracle (cache bytes, workspace rows,
+    decode output)."""
+    from synth.workload import build_agentic_workload
+    wl = synth.WORKLOADS[5]
+    say(f"case full size agentic: B {wl.batch} prefix {wl.shared_prefix} chunk {wl.chunk}")
+    w = build_agentic_workload(nk, wl, keep_bf16=True)
+    shared = torch.from_numpy(w.shared_pages.astype(np.int64)).cuda()
+    before = (w.kp.data[shared].clone(), w.kp.scale[shared].clone(), w.vp.data[shared].clone(),
+              w.vp.scale[shared].clone())
+    nk.nvfp4_kv_quantize(w.k_chunk, w.v_chunk, w.slot_chunk, w.kp, w.vp)
+    nk.nvfp4_kv_dequant_workspace(w.kp, w.vp, w.bt, w.cached_lens, w.ws_row_offsets, w.k_ws, w.v_ws)
+    out = nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale)
+    torch.cuda.synchronize()
+    after = (w.kp.data[shared], w.kp.scale[shared], w.vp.data[shared], w.vp.scale[shared])
+    assert all(torch.equal(x, y) for x, y in zip(before, after)), "shared prefix pages were written"
+    H, P, d, G, C = wl.num_kv_heads, wl.page_size, wl.head_dim, wl.group, wl.chunk
+    offs = w.ws_row_offsets.cpu().numpy()
+    for b in (0, 37, wl.batch - 1):
+        L = int(w.host_cached_lens[b])
+        say(f"  sample sequence {b}: cached {L}")
+        kb = np.concatenate([synth.bf16_tensor_bits(w.k_shared), synth.bf16_tensor_bits(w.k_private[b]),
+                             synth.bf16_tensor_bits(w.k_chunk[b * C:(b + 1) * C])])
+        vb = np.concatenate([synth.bf16_tensor_bits(w.v_shared), synth.bf16_tensor_bits(w.v_private[b]),
+                             synth.bf16_tensor_bits(w.v_chunk[b * C:(b + 1) * C])])
+        kd, ks = onv.quantize_rows(kb)
+        vd, vs = onv.quantize_rows(vb)
+        t = np.arange(L + C)
+        pages = torch.from_numpy(w.host_bt[b][t // P].astype(np.int64)).cuda()
+        offp = torch.from_numpy(t % P).cuda()
+        assert np.array_equal(w.kp.data[pages, :, offp].cpu().numpy(), kd), "K data"
+        assert np.array_equal(w.kp.scale[pages, :, offp].cpu().numpy(), ks), "K scale"
+        assert np.array_equal(w.vp.data[pages, :, offp].cpu().numpy(), vd), "V data"
+        assert np.array_equal(w.vp.scale[pages, :, offp].cpu().numpy(), vs), "V scale"
+        khat, vhat = onv.dequant_rows(kd, ks), onv.dequant_rows(vd, vs)
+        rows = synth.bf16_tensor_bits(w.k_ws[offs[b]:offs[b] + L])
+        assert np.array_equal(rows, oatt.f64_to_bf16_exact(khat[:L])), "K workspace"
+        rows = synth.bf16_tensor_bits(w.v_ws[offs[b]:offs[b] + L])
+        assert np.array_equal(rows, oatt.f64_to_bf16_exact(vhat[:L])), "V workspace"
+        qb = onv.bf16_to_f64(synth.bf16_tensor_bits(w.q[b]))
+        ref, mass = oatt.decode_heads(qb, khat, vhat, wl.sm_scale)
+        check_out(out[b], ref, mass, f"agentic b{b}")
+    del w
     torch.cuda.empty_cache()
