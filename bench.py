@@ -78,6 +78,22 @@ def read_traffic(kernel_tag):
         return None
 
 
+RAMP_S = 0.5
+
+
+def ramp(fn, seconds=RAMP_S):
+    """Untimed calls for `seconds` of wall time before the counted warm-up:
+    the first few hundred microseconds of a burst run measurably slower
+    (clocks and caches coming up), which a handful of sub-millisecond warm-up
+    steps does not cover."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
 class Bench:
     def __init__(self, nk, wl, fp8, variant):
         import torch
@@ -119,6 +135,7 @@ class Bench:
 
     def time_steps(self, steps, warmup):
         torch = self.torch
+        ramp(self.step)
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
@@ -167,6 +184,7 @@ def agentic(nk, wl, steps, warmup):
         ("decode", lambda: nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale,
                                                       num_splits=S, workspace=ws, out=out)),
     ]
+    ramp(lambda: [f() for _, f in calls], seconds=0.2)
     for _ in range(warmup):
         for _, f in calls:
             f()
@@ -304,6 +322,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_ramp_s": RAMP_S,
         "ms_per_step": round(t_step * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",

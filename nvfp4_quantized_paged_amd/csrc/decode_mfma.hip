@@ -29,11 +29,13 @@
 //    operand of O^T[c][h] += V^T[c][t] P[t][h], and the softmax output C of
 //    the same two tiles is already the B operand in the same lane: no
 //    cross-lane data movement anywhere in the loop.
-//  * Loads: buffer loads from a per-page descriptor built in scalar
-//    registers (page from the block table, clamped into the pool), with a
-//    fixed per-lane offset, so no vector ALU goes into addressing and no
-//    load can leave the page's slice. Registers hold three chunks (64 tokens
-//    NVFP4, 32 tokens FP8): one computing, two in flight.
+//  * Loads: buffer loads with a fixed per-lane offset and a scalar offset
+//    (page from the block table, clamped into the pool), so no vector ALU
+//    goes into addressing. Pools below 2 GiB use one descriptor per array,
+//    built once per wave (bounds: the whole pool); larger pools build a
+//    descriptor per page slice (bounds: the slice), because buffer offsets
+//    are 32-bit. Registers hold three chunks (64 tokens NVFP4, 32 tokens
+//    FP8): one computing, two in flight.
 #include "common.hpp"
 
 namespace nvfp4kv {
@@ -130,7 +132,8 @@ struct Item {
   int g, t1;
 };
 
-template <int D, bool FP8, int T>
+// PW: pool-wide descriptors (pool of one array < 2 GiB), else per page slice.
+template <int D, bool FP8, int T, bool PW>
 __device__ inline void load_tile(const DecodeParams& p, const Item& it, int tok0, int lane,
                                  TileRaw<D, FP8>& raw) {
   using C = Cfg<D, FP8, T>;
@@ -141,12 +144,13 @@ __device__ inline void load_tile(const DecodeParams& p, const Item& it, int tok0
     int page = __builtin_amdgcn_readfirstlane(it.bt[tok0 / P]);
     page = min(max(page, 0), p.num_pages - 1);
     const int64_t slice = ((int64_t)page * p.num_kv_heads + it.g) * P;     // first row of the (page, head) slice
-    const int soff = (tok0 % P) * C::kRowBytes;
+    const int64_t rows = PW ? (int64_t)p.num_pages * p.num_kv_heads * P : P;  // rows the descriptor covers
+    const int soff = (int)(((PW ? slice : 0) + tok0 % P) * C::kRowBytes);
     const int voff = r * C::kRowBytes + grp * C::kLaneBytes;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(p.kd + slice * C::kRowBytes), (short)0, P * C::kRowBytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(p.vd + slice * C::kRowBytes), (short)0, P * C::kRowBytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.kd + (PW ? 0 : slice) * C::kRowBytes), (short)0, (int)(rows * C::kRowBytes), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.vd + (PW ? 0 : slice) * C::kRowBytes), (short)0, (int)(rows * C::kRowBytes), kRsrcWord3);
     if constexpr (C::kLaneWords == 2) {
       const auto a = __builtin_amdgcn_raw_buffer_load_b64(rk, voff, soff, C::kStream);
       const auto b = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, soff, C::kStream);
@@ -169,11 +173,11 @@ __device__ inline void load_tile(const DecodeParams& p, const Item& it, int tok0
       raw.vs = 0;
     } else {
       constexpr int nb = C::kScaleRow;
-      const __amdgpu_buffer_rsrc_t sk =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(p.ks + slice * nb), (short)0, P * nb, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t sv =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(p.vs + slice * nb), (short)0, P * nb, kRsrcWord3);
-      const int so = (tok0 % P) * nb;
+      const __amdgpu_buffer_rsrc_t sk = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.ks + (PW ? 0 : slice) * nb), (short)0, (int)(rows * nb), kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t sv = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.vs + (PW ? 0 : slice) * nb), (short)0, (int)(rows * nb), kRsrcWord3);
+      const int so = (int)(((PW ? slice : 0) + tok0 % P) * nb);
       if constexpr (D == 128) {
         raw.ks = __builtin_amdgcn_raw_buffer_load_b16(sk, r * nb + 2 * grp, so, C::kStream);
         raw.vs = __builtin_amdgcn_raw_buffer_load_b16(sv, r * nb + 2 * grp, so, C::kStream);
@@ -190,11 +194,11 @@ __device__ inline void load_tile(const DecodeParams& p, const Item& it, int tok0
   }
 }
 
-template <int D, bool FP8, int T>
+template <int D, bool FP8, int T, bool PW>
 __device__ inline void load_chunk(const DecodeParams& p, const Item& it, int ts, int lane,
                                   TileRaw<D, FP8> (&buf)[Cfg<D, FP8, T>::kTiles]) {
 #pragma unroll
-  for (int t = 0; t < Cfg<D, FP8, T>::kTiles; ++t) load_tile<D, FP8, T>(p, it, ts + 16 * t, lane, buf[t]);
+  for (int t = 0; t < Cfg<D, FP8, T>::kTiles; ++t) load_tile<D, FP8, T, PW>(p, it, ts + 16 * t, lane, buf[t]);
 }
 
 // Running softmax state and output accumulators of one wave.
@@ -287,7 +291,7 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
   }
 }
 
-template <int D, bool FP8, int T, int W>
+template <int D, bool FP8, int T, int W, bool PW>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(W)))
 void decode_partial_mfma_kernel(DecodeParams p) {
   using C = Cfg<D, FP8, T>;
@@ -312,9 +316,9 @@ void decode_partial_mfma_kernel(DecodeParams p) {
 
   if (t0 < it.t1) {
     TileRaw<D, FP8> b0[C::kTiles], b1[C::kTiles], b2[C::kTiles];
-    load_chunk<D, FP8, T>(p, it, t0, lane, b0);
-    load_chunk<D, FP8, T>(p, it, t0 + C::kChunk, lane, b1);
-    load_chunk<D, FP8, T>(p, it, t0 + 2 * C::kChunk, lane, b2);
+    load_chunk<D, FP8, T, PW>(p, it, t0, lane, b0);
+    load_chunk<D, FP8, T, PW>(p, it, t0 + C::kChunk, lane, b1);
+    load_chunk<D, FP8, T, PW>(p, it, t0 + 2 * C::kChunk, lane, b2);
 
     // ---- q as the B operand: lane (head col, group grp), step kk: channels grp*D/4 + 8kk .. +7
     const bool hv = col < G;
@@ -357,13 +361,13 @@ void decode_partial_mfma_kernel(DecodeParams p) {
     // three register buffers: compute one chunk while the next two are in flight
     for (int ts = t0; ts < it.t1; ts += 3 * C::kChunk) {
       process_chunk<D, FP8, T>(it, ts, lane, b0, qb, sel, cs, a);
-      load_chunk<D, FP8, T>(p, it, ts + 3 * C::kChunk, lane, b0);
+      load_chunk<D, FP8, T, PW>(p, it, ts + 3 * C::kChunk, lane, b0);
       if (ts + C::kChunk >= it.t1) break;
       process_chunk<D, FP8, T>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
-      load_chunk<D, FP8, T>(p, it, ts + 4 * C::kChunk, lane, b1);
+      load_chunk<D, FP8, T, PW>(p, it, ts + 4 * C::kChunk, lane, b1);
       if (ts + 2 * C::kChunk >= it.t1) break;
       process_chunk<D, FP8, T>(it, ts + 2 * C::kChunk, lane, b2, qb, sel, cs, a);
-      load_chunk<D, FP8, T>(p, it, ts + 5 * C::kChunk, lane, b2);
+      load_chunk<D, FP8, T, PW>(p, it, ts + 5 * C::kChunk, lane, b2);
     }
   }
 
@@ -391,7 +395,12 @@ void decode_partial_mfma_kernel(DecodeParams p) {
 template <int D, bool FP8, int T, int W>
 hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.num_splits, p.num_kv_heads, p.batch);
-  hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W>), grid, dim3(64), 0, s, p);
+  // buffer offsets and bounds are 32-bit: whole-pool descriptors only below 2 GiB per array
+  const int64_t pool_bytes = (int64_t)p.num_pages * p.num_kv_heads * p.page_size * Cfg<D, FP8, T>::kRowBytes;
+  if (pool_bytes <= INT32_MAX)
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, true>), grid, dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, false>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -385,6 +385,53 @@ def test_fp8_decode_moderate(nk):
         check_out(out, ref, mass, f"fp8 variant={var}")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_decode_pool_above_2gib(nk, fmt):
+    """Pools of more than 2 GiB per array (buffer offsets are 32-bit, so the
+    decode kernel switches to per-page addressing): the same pages placed at
+    the far end of a large pool give bit-identical outputs to a small pool,
+    and both match the oracle."""
+    wl = synth.Workload(94, "bigpool", 3, 16, 2, 128, 64, 700, True, 3)
+    inp = synth.host_uniform_decode(wl)
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    row = d // 2 if fmt == "nvfp4" else d
+    big = (2 ** 31) // (H * P * row) + 64          # just past 2 GiB of data per array
+    say(f"case decode pool above 2 GiB: {fmt} pages {big} ({big * H * P * row / 2**30:.2f} GiB per array)")
+    # small page p -> big page: spread over the pool, the last one at its very end
+    remap = (big - 1 - np.arange(inp.num_pages, dtype=np.int64) * 997).astype(np.int32)
+    bt_big = remap[inp.block_tables]
+    slots_big = remap[inp.slot_mapping // P].astype(np.int64) * P + inp.slot_mapping % P
+    q = synth.to_device_bf16(inp.q)
+    kt, vt = synth.to_device_bf16(inp.k), synth.to_device_bf16(inp.v)
+    sl = synth.to_device(inp.seq_lens)
+    outs = []
+    for pages, bt, slots in ((inp.num_pages, inp.block_tables, inp.slot_mapping), (big, bt_big, slots_big)):
+        if fmt == "nvfp4":
+            kp, vp = nk.NVFP4Pool.empty(pages, H, P, d), nk.NVFP4Pool.empty(pages, H, P, d)
+            nk.nvfp4_kv_quantize(kt, vt, synth.to_device(slots), kp, vp)
+            out = nk.nvfp4_paged_decode_attn(q, kp, vp, synth.to_device(bt), sl, wl.sm_scale, num_splits=3)
+        else:
+            kp, vp = nk.FP8Pool.empty(pages, H, P, d), nk.FP8Pool.empty(pages, H, P, d)
+            nk.fp8_kv_quantize(kt, vt, synth.to_device(slots), kp, vp)
+            out = nk.fp8_paged_decode_attn(q, kp, vp, synth.to_device(bt), sl, wl.sm_scale, num_splits=3)
+        torch.cuda.synchronize()
+        outs.append(out)
+        del kp, vp
+    torch.cuda.empty_cache()
+    assert torch.equal(outs[0], outs[1]), "large-pool addressing changed the result"
+    if fmt == "nvfp4":
+        kd, ks, vd, vs = oracle_nv(inp.num_pages, H, P, d, inp.k, inp.v, inp.slot_mapping)
+        kh, vh = onv.dequant_cache(kd, ks), onv.dequant_cache(vd, vs)
+    else:
+        kr = np.zeros((inp.num_pages, H, P, d), np.uint8)
+        vr = kr.copy()
+        of8.write_cache(kr, inp.k, inp.slot_mapping)
+        of8.write_cache(vr, inp.v, inp.slot_mapping)
+        kh, vh = of8.dequant_cache(kr), of8.dequant_cache(vr)
+    ref, mass = oatt.paged_decode(inp.q, kh, vh, inp.block_tables, inp.seq_lens, wl.sm_scale)
+    check_out(outs[1], ref, mass, f"{fmt} large pool")
+
+
 # ---------------------------------------------------------------------------
 # the agentic prefix-reuse step at a reduced size
 # ---------------------------------------------------------------------------
