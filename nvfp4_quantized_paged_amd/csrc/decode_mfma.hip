@@ -133,20 +133,30 @@ struct Item {
 };
 
 // PW: pool-wide descriptors (pool of one array < 2 GiB), else per page slice.
+// Every call issues its loads, also for a tile at or past the end of the item
+// (the prefetch runs ahead of the last chunk): loads under a branch would make
+// the paths of the chunk rotation disagree on which loads are outstanding, and
+// the compiler then waits for all of them before every chunk. Such a tile
+// takes its page from the item's last tile and sets bit 31 of the per-lane
+// offset: the offset is then beyond the descriptor's range (below 2^31) with or
+// without the scalar offset added (their sum stays below 2^32), so the load
+// returns zeros without touching memory. Its contents are never used.
 template <int D, bool FP8, int T, bool PW>
 __device__ inline void load_tile(const DecodeParams& p, const Item& it, int tok0, int lane,
                                  TileRaw<D, FP8>& raw) {
   using C = Cfg<D, FP8, T>;
   const int r = lane & 15, grp = lane >> 4;
-  tok0 = __builtin_amdgcn_readfirstlane(tok0);   // scalar offsets (no per-lane induction variables)
-  if (tok0 < it.t1) {
+  // scalar offsets (no per-lane induction variables); t1 > 0 and t1 - 1 is in the item
+  const uint32_t oob = __builtin_amdgcn_readfirstlane(tok0) >= it.t1 ? 0x80000000u : 0u;
+  tok0 = __builtin_amdgcn_readfirstlane(min(tok0, (it.t1 - 1) & ~15));
+  {
     const int P = p.page_size;
     int page = __builtin_amdgcn_readfirstlane(it.bt[tok0 / P]);
     page = min(max(page, 0), p.num_pages - 1);
     const int64_t slice = ((int64_t)page * p.num_kv_heads + it.g) * P;     // first row of the (page, head) slice
     const int64_t rows = PW ? (int64_t)p.num_pages * p.num_kv_heads * P : P;  // rows the descriptor covers
     const int soff = (int)(((PW ? slice : 0) + tok0 % P) * C::kRowBytes);
-    const int voff = r * C::kRowBytes + grp * C::kLaneBytes;
+    const int voff = (int)((uint32_t)(r * C::kRowBytes + grp * C::kLaneBytes) | oob);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.kd + (PW ? 0 : slice) * C::kRowBytes), (short)0, (int)(rows * C::kRowBytes), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -179,18 +189,15 @@ __device__ inline void load_tile(const DecodeParams& p, const Item& it, int tok0
           (void*)(p.vs + (PW ? 0 : slice) * nb), (short)0, (int)(rows * nb), kRsrcWord3);
       const int so = (int)(((PW ? slice : 0) + tok0 % P) * nb);
       if constexpr (D == 128) {
-        raw.ks = __builtin_amdgcn_raw_buffer_load_b16(sk, r * nb + 2 * grp, so, C::kStream);
-        raw.vs = __builtin_amdgcn_raw_buffer_load_b16(sv, r * nb + 2 * grp, so, C::kStream);
+        const int lo = (int)((uint32_t)(r * nb + 2 * grp) | oob);
+        raw.ks = __builtin_amdgcn_raw_buffer_load_b16(sk, lo, so, C::kStream);
+        raw.vs = __builtin_amdgcn_raw_buffer_load_b16(sv, lo, so, C::kStream);
       } else {
-        raw.ks = __builtin_amdgcn_raw_buffer_load_b8(sk, r * nb + grp, so, C::kStream);
-        raw.vs = __builtin_amdgcn_raw_buffer_load_b8(sv, r * nb + grp, so, C::kStream);
+        const int lo = (int)((uint32_t)(r * nb + grp) | oob);
+        raw.ks = __builtin_amdgcn_raw_buffer_load_b8(sk, lo, so, C::kStream);
+        raw.vs = __builtin_amdgcn_raw_buffer_load_b8(sv, lo, so, C::kStream);
       }
     }
-  } else {
-#pragma unroll
-    for (int w = 0; w < C::kLaneWords; ++w) { raw.k[w] = 0; raw.v[w] = 0; }
-    raw.ks = 0;
-    raw.vs = 0;
   }
 }
 
@@ -315,6 +322,9 @@ void decode_partial_mfma_kernel(DecodeParams p) {
   a.l = 0.0f;
 
   if (t0 < it.t1) {
+    // The prologue's K/V loads are complete once q has arrived (q is loaded
+    // after them and the load counter is in order), so the loop below starts
+    // from a state with nothing outstanding and the same on every iteration.
     TileRaw<D, FP8> b0[C::kTiles], b1[C::kTiles], b2[C::kTiles];
     load_chunk<D, FP8, T, PW>(p, it, t0, lane, b0);
     load_chunk<D, FP8, T, PW>(p, it, t0 + C::kChunk, lane, b1);
@@ -358,17 +368,22 @@ void decode_partial_mfma_kernel(DecodeParams p) {
       for (int e = 0; e < 8; ++e)
         sel[hs][e] = (grp == 2 * hs + (col >> 3) && e == (col & 7)) ? (_Float16)1.0f : (_Float16)0.0f;
 
-    // three register buffers: compute one chunk while the next two are in flight
-    for (int ts = t0; ts < it.t1; ts += 3 * C::kChunk) {
+    // three register buffers: compute one chunk while the next two are in flight.
+    // The loop runs whole rotations only (no exit in the middle): every path
+    // back to the loop head has issued the same loads in the same order, so the
+    // compiler's wait before each chunk leaves the other two chunks in flight.
+    int ts = t0;
+    for (; ts + 2 * C::kChunk < it.t1; ts += 3 * C::kChunk) {
       process_chunk<D, FP8, T>(it, ts, lane, b0, qb, sel, cs, a);
       load_chunk<D, FP8, T, PW>(p, it, ts + 3 * C::kChunk, lane, b0);
-      if (ts + C::kChunk >= it.t1) break;
       process_chunk<D, FP8, T>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
       load_chunk<D, FP8, T, PW>(p, it, ts + 4 * C::kChunk, lane, b1);
-      if (ts + 2 * C::kChunk >= it.t1) break;
       process_chunk<D, FP8, T>(it, ts + 2 * C::kChunk, lane, b2, qb, sel, cs, a);
       load_chunk<D, FP8, T, PW>(p, it, ts + 5 * C::kChunk, lane, b2);
     }
+    // at most two chunks remain, already loaded
+    if (ts < it.t1) process_chunk<D, FP8, T>(it, ts, lane, b0, qb, sel, cs, a);
+    if (ts + C::kChunk < it.t1) process_chunk<D, FP8, T>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
   }
 
   // ---- partial results: lane (head col, channel group grp)
