@@ -386,20 +386,30 @@ void decode_partial_mfma_kernel(DecodeParams p) {
     if (ts + C::kChunk < it.t1) process_chunk<D, FP8, T>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
   }
 
-  // ---- partial results: lane (head col, channel group grp)
+  // ---- partial results. The accumulators sit in lane (head col, channel group grp) order;
+  // they go through LDS so that each store instruction writes whole rows of the output,
+  // with non-temporal stores (measured on MI355X, long-context-32k: 297 -> 281 us; the
+  // per-lane scattered 16-byte stores cost 9% of the kernel).
+  __shared__ float4_t stage[16 * D / 4];
   float lt = a.l + __shfl_xor(a.l, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
   if (col < G) {
-    const int64_t idx = (qh0 + col) * S + j;
-    float* o = p.part_o + idx * D;
 #pragma unroll
     for (int kk = 0; kk < C::kKSteps; ++kk)
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         const int ch = (2 * hs + (grp >> 1)) * C::kChanPerGroup + 8 * kk + 4 * (grp & 1);
-        const float4_t v = a.o[2 * kk + hs];
-        *reinterpret_cast<float4*>(o + ch) = make_float4(v[0], v[1], v[2], v[3]);
+        stage[(col * D + ch) / 4] = a.o[2 * kk + hs];
       }
+  }
+  __syncthreads();
+  for (int e = lane; e < G * D / 4; e += 64) {
+    const int row = e / (D / 4), c4 = e % (D / 4);
+    const int64_t idx = (qh0 + row) * S + j;
+    __builtin_nontemporal_store(stage[e], reinterpret_cast<float4_t*>(p.part_o + idx * D + 4 * c4));
+  }
+  if (col < G) {
+    const int64_t idx = (qh0 + col) * S + j;
     if (grp == 0) {
       p.part_ml[idx * 2] = a.m;
       p.part_ml[idx * 2 + 1] = lt;
