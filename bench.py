@@ -271,7 +271,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--variant", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--variant", choices=["auto", "valu", "mfma", "mfma_lut"], default="auto")
     ap.add_argument("--only", choices=["nvfp4", "fp8", "all"], default="all",
                     help="nvfp4 / fp8: only that 32K decode step (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -298,7 +298,8 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
         return
     nk.lib()
-    variant = {"auto": nk.VARIANT_AUTO, "valu": nk.VARIANT_VALU, "mfma": nk.VARIANT_MFMA}[args.variant]
+    variant = {"auto": nk.VARIANT_AUTO, "valu": nk.VARIANT_VALU, "mfma": nk.VARIANT_MFMA,
+               "mfma_lut": nk.VARIANT_MFMA_LUT}[args.variant]
     wl = synth.WORKLOADS[3]
     if args.only == "fp8":
         f8 = Bench(nk, wl, True, variant)

@@ -79,6 +79,9 @@ extern "C" {
 #define NVFP4KV_VARIANT_AUTO 0   /* the library's choice (the MFMA kernel when built) */
 #define NVFP4KV_VARIANT_VALU 1   /* fp32 vector-ALU dot products, one wave per work item */
 #define NVFP4KV_VARIANT_MFMA 2   /* f16 matrix-core products (gfx950 MFMA) */
+#define NVFP4KV_VARIANT_MFMA_LUT 3 /* as MFMA, E2M1 unpacked through a register lookup table
+                                      (byte permutes) instead of the gfx950 FP4 conversion;
+                                      identical results; FP8 caches run the MFMA kernel */
 
 typedef struct {
   int32_t num_pages;    /* pages in the pool */

@@ -24,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnvfp4kv.so")
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4, -5
-VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
+VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA, VARIANT_MFMA_LUT = 0, 1, 2, 3
 
 c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 

@@ -148,7 +148,8 @@ DecodeParams make_decode(const nvfp4kv_geom* g, const void* q, const uint8_t* kd
 }
 
 int check_variant(int32_t variant, const char* fn) {
-  if (variant != NVFP4KV_VARIANT_AUTO && variant != NVFP4KV_VARIANT_VALU && variant != NVFP4KV_VARIANT_MFMA)
+  if (variant != NVFP4KV_VARIANT_AUTO && variant != NVFP4KV_VARIANT_VALU && variant != NVFP4KV_VARIANT_MFMA &&
+      variant != NVFP4KV_VARIANT_MFMA_LUT)
     return fail(NVFP4KV_EINVAL, "%s: unknown variant %d", fn, variant);
   return NVFP4KV_OK;
 }
@@ -156,7 +157,7 @@ int check_variant(int32_t variant, const char* fn) {
 hipError_t run_partial(const DecodeParams& p, int head_dim, bool fp8, int32_t variant, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   if (variant == NVFP4KV_VARIANT_VALU) return launch_decode_valu(p, head_dim, fp8, s);
-  return launch_decode_mfma(p, head_dim, fp8, s);
+  return launch_decode_mfma(p, head_dim, fp8, variant == NVFP4KV_VARIANT_MFMA_LUT, s);
 }
 
 hipError_t run_merge(const DecodeParams& d, int head_dim, float out_scale, void* out, hipStream_t s) {

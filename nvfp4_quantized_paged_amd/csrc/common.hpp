@@ -151,7 +151,8 @@ hipError_t launch_nvfp4_quantize(const QuantizeParams& p, hipStream_t s);
 hipError_t launch_fp8_quantize(const QuantizeParams& p, hipStream_t s);
 hipError_t launch_nvfp4_dequant_ws(const WorkspaceParams& p, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, bool fp8, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, hipStream_t s);
+// lut: NVFP4 unpack through a register lookup table instead of the conversion instruction
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, bool lut, hipStream_t s);
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t s);
 
 }  // namespace nvfp4kv

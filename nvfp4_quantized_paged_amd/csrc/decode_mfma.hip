@@ -92,6 +92,31 @@ __device__ inline half8_t fp4x8_scaled(uint32_t w, half2_t s) {
   return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// The same with a register lookup table instead of the conversion instruction
+// (kept to compare the two; the conversion is faster). An E2M1 code's f16
+// encoding has a zero low byte, and its high byte is a function of the 3-bit
+// magnitude: a byte permute picks it from two LUT registers, a second permute
+// places the sign bits. Byte k of w holds elements 2k (low nibble) and 2k+1.
+constexpr uint32_t kE2m1F16HiLo = 0x3E3C3800u;   // magnitudes 0..3 -> 0, 0.5, 1, 1.5
+constexpr uint32_t kE2m1F16HiHi = 0x46444240u;   // magnitudes 4..7 -> 2, 3, 4, 6
+__device__ inline half8_t fp4x8_scaled_lut(uint32_t w, half2_t s) {
+  const uint32_t mlo = w & 0x07070707u;           // magnitude of element 2k in byte k
+  const uint32_t mhi = (w >> 4) & 0x07070707u;    // magnitude of element 2k+1 in byte k
+  const uint32_t slo = (w << 4) & 0x80808080u;    // sign of element 2k at bit 7 of byte k
+  const uint32_t shi = w & 0x80808080u;           // sign of element 2k+1 at bit 7 of byte k
+  half2_t h[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // bytes [zero, byte k of the low source, zero, byte k of the high source]
+    const uint32_t sel = 0x000C000Cu | (uint32_t)k << 8 | (uint32_t)(4 + k) << 24;
+    const uint32_t mags = __builtin_amdgcn_perm(mhi, mlo, sel);
+    const uint32_t bits = __builtin_amdgcn_perm(kE2m1F16HiHi, kE2m1F16HiLo, mags) |
+                          __builtin_amdgcn_perm(shi, slo, sel);
+    h[k] = __builtin_bit_cast(half2_t, bits) * s;
+  }
+  return half8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+}
+
 // Eight E4M3 bytes of two words -> eight f16 values.
 __device__ inline half8_t fp8x8(uint32_t w0, uint32_t w1) {
   const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
@@ -103,7 +128,7 @@ __device__ inline half8_t fp8x8(uint32_t w0, uint32_t w1) {
 
 // The lane's A-operand slice for QK step kk (or the transpose of V): eight
 // consecutive channels (g*D/4 + 8kk .. +7) of its token, dequantized to f16.
-template <int D, bool FP8, int T>
+template <int D, bool FP8, bool LUT>
 __device__ inline half8_t unpack(const uint32_t* words, uint32_t scale_bits, int kk) {
   if constexpr (FP8) {
     return fp8x8(words[2 * kk], words[2 * kk + 1]);
@@ -111,7 +136,7 @@ __device__ inline half8_t unpack(const uint32_t* words, uint32_t scale_bits, int
     // NVFP4: word kk holds the 8 channels; block scale byte(s) of the lane
     const half2_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scale_bits, 1.0f, false);
     const half2_t s = (D == 128 && kk >= 2) ? splat_hi(s2) : splat_lo(s2);
-    return fp4x8_scaled(words[kk], s);
+    return LUT ? fp4x8_scaled_lut(words[kk], s) : fp4x8_scaled(words[kk], s);
   }
 }
 
@@ -216,7 +241,7 @@ struct Acc {
 };
 
 // One chunk: QK, online softmax, PV. `cs` > 0 maps raw scores to base-2 logits.
-template <int D, bool FP8, int T>
+template <int D, bool FP8, int T, bool LUT>
 __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D, FP8> (&cur)[Cfg<D, FP8, T>::kTiles],
                                      const half8_t (&qb)[Cfg<D, FP8, T>::kKSteps], const half8_t (&sel)[2], float cs,
                                      Acc<D>& a) {
@@ -229,7 +254,7 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
   for (int t = 0; t < C::kTiles; ++t) {
     float4_t c4 = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < C::kKSteps; ++kk) c4 = mfma(unpack<D, FP8, T>(cur[t].k, cur[t].ks, kk), qb[kk], c4);
+    for (int kk = 0; kk < C::kKSteps; ++kk) c4 = mfma(unpack<D, FP8, LUT>(cur[t].k, cur[t].ks, kk), qb[kk], c4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[t][i] = c4[i];
   }
@@ -285,8 +310,8 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
                                   float4_t{sc[t + 1][0], sc[t + 1][1], sc[t + 1][2], sc[t + 1][3]});
 #pragma unroll
     for (int kk = 0; kk < C::kKSteps; ++kk) {
-      const half8_t va = unpack<D, FP8, T>(cur[t].v, cur[t].vs, kk);
-      const half8_t vb = unpack<D, FP8, T>(cur[t + 1].v, cur[t + 1].vs, kk);
+      const half8_t va = unpack<D, FP8, LUT>(cur[t].v, cur[t].vs, kk);
+      const half8_t vb = unpack<D, FP8, LUT>(cur[t + 1].v, cur[t + 1].vs, kk);
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         const float4_t zero = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -298,7 +323,7 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
   }
 }
 
-template <int D, bool FP8, int T, int W, bool PW>
+template <int D, bool FP8, int T, int W, bool PW, bool LUT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(W)))
 void decode_partial_mfma_kernel(DecodeParams p) {
   using C = Cfg<D, FP8, T>;
@@ -374,16 +399,16 @@ void decode_partial_mfma_kernel(DecodeParams p) {
     // compiler's wait before each chunk leaves the other two chunks in flight.
     int ts = t0;
     for (; ts + 2 * C::kChunk < it.t1; ts += 3 * C::kChunk) {
-      process_chunk<D, FP8, T>(it, ts, lane, b0, qb, sel, cs, a);
+      process_chunk<D, FP8, T, LUT>(it, ts, lane, b0, qb, sel, cs, a);
       load_chunk<D, FP8, T, PW>(p, it, ts + 3 * C::kChunk, lane, b0);
-      process_chunk<D, FP8, T>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
+      process_chunk<D, FP8, T, LUT>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
       load_chunk<D, FP8, T, PW>(p, it, ts + 4 * C::kChunk, lane, b1);
-      process_chunk<D, FP8, T>(it, ts + 2 * C::kChunk, lane, b2, qb, sel, cs, a);
+      process_chunk<D, FP8, T, LUT>(it, ts + 2 * C::kChunk, lane, b2, qb, sel, cs, a);
       load_chunk<D, FP8, T, PW>(p, it, ts + 5 * C::kChunk, lane, b2);
     }
     // at most two chunks remain, already loaded
-    if (ts < it.t1) process_chunk<D, FP8, T>(it, ts, lane, b0, qb, sel, cs, a);
-    if (ts + C::kChunk < it.t1) process_chunk<D, FP8, T>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
+    if (ts < it.t1) process_chunk<D, FP8, T, LUT>(it, ts, lane, b0, qb, sel, cs, a);
+    if (ts + C::kChunk < it.t1) process_chunk<D, FP8, T, LUT>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
   }
 
   // ---- partial results. The accumulators sit in lane (head col, channel group grp) order;
@@ -417,15 +442,15 @@ void decode_partial_mfma_kernel(DecodeParams p) {
   }
 }
 
-template <int D, bool FP8, int T, int W>
+template <int D, bool FP8, int T, int W, bool LUT = false>
 hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.num_splits, p.num_kv_heads, p.batch);
   // buffer offsets and bounds are 32-bit: whole-pool descriptors only below 2 GiB per array
   const int64_t pool_bytes = (int64_t)p.num_pages * p.num_kv_heads * p.page_size * Cfg<D, FP8, T>::kRowBytes;
   if (pool_bytes <= INT32_MAX)
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, true>), grid, dim3(64), 0, s, p);
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, true, LUT>), grid, dim3(64), 0, s, p);
   else
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, false>), grid, dim3(64), 0, s, p);
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, false, LUT>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -435,14 +460,16 @@ hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
 //  * NVFP4, splits of up to 2048 tokens: 32-token chunks, 3 waves per SIMD;
 //    longer splits: 64-token chunks, 2 waves per SIMD (fewer softmax passes).
 //  * FP8 (twice the bytes per token): 32-token chunks, 2 waves per SIMD.
-hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, bool lut, hipStream_t s) {
   const int64_t split_len = ((int64_t)p.max_pages * p.page_size + p.num_splits - 1) / p.num_splits;
   const bool short_split = split_len <= 2048;
   if (head_dim == 64) {
     if (fp8) return launch_mfma<64, true, 2, 2>(p, s);
+    if (lut) return short_split ? launch_mfma<64, false, 2, 3, true>(p, s) : launch_mfma<64, false, 4, 2, true>(p, s);
     return short_split ? launch_mfma<64, false, 2, 3>(p, s) : launch_mfma<64, false, 4, 2>(p, s);
   }
   if (fp8) return launch_mfma<128, true, 2, 2>(p, s);
+  if (lut) return short_split ? launch_mfma<128, false, 2, 3, true>(p, s) : launch_mfma<128, false, 4, 2, true>(p, s);
   return short_split ? launch_mfma<128, false, 2, 3>(p, s) : launch_mfma<128, false, 4, 2>(p, s);
 }
 

@@ -134,6 +134,8 @@ def test_partial_rejects_bad_variant_and_auto_splits(L):
     args = lambda S, variant: (ctypes.byref(g), FAKE, ctypes.byref(kc), ctypes.byref(vc), FAKE, 16, FAKE, 1, 4,
                                0.125, S, variant, FAKE, 1 << 20, None)
     assert f(*args(1, 7)) == L.EINVAL
+    assert f(*args(1, 4)) == L.EINVAL
+    assert f(*args(1, -1)) == L.EINVAL
     assert f(*args(0, 0)) == L.EINVAL      # the partial call needs an explicit split count
 
 

@@ -287,8 +287,8 @@ def test_decode_tiny_workload(nk):
     wl = synth.WORKLOADS[1]
     say(f"case decode tiny: {wl}")
     inp = synth.host_uniform_decode(wl)
-    decode_problem(nk, inp, splits_list=(1, 3, 16), variants=(None, nk.VARIANT_VALU, nk.VARIANT_MFMA),
-                   label="tiny")
+    decode_problem(nk, inp, splits_list=(1, 3, 16),
+                   variants=(None, nk.VARIANT_VALU, nk.VARIANT_MFMA, nk.VARIANT_MFMA_LUT), label="tiny")
 
 
 def test_decode_moderate_workload(nk):
@@ -314,6 +314,20 @@ def test_decode_group_and_shape_coverage(nk, shape):
     say(f"case decode shape: G {G} Hkv {H} d {d} P {P}")
     inp = synth.host_uniform_decode(wl)
     decode_problem(nk, inp, splits_list=(1, 3), variants=(None, nk.VARIANT_VALU), label=f"G{G}-H{H}-d{d}-P{P}")
+
+
+@pytest.mark.parametrize("shape", [(8, 128, 16, 4096), (4, 64, 32, 700), (5, 128, 64, 3000)])
+def test_decode_lut_unpack_matches_conversion(nk, shape):
+    """The register-LUT E2M1 unpack and the conversion-instruction unpack give
+    the same f16 operands, hence bit-identical partials; both match the oracle."""
+    G, d, P, L = shape
+    wl = synth.Workload(95, "lut", 2, 2 * G, 2, d, P, L, True, 0)
+    say(f"case decode lut vs cvt: G {G} d {d} P {P} L {L}")
+    inp = synth.host_uniform_decode(wl)
+    for S in (1, 7):
+        outs, _, _ = decode_problem(nk, inp, splits_list=(S,), variants=(nk.VARIANT_MFMA, nk.VARIANT_MFMA_LUT),
+                                    label=f"lut S={S}")
+        assert torch.equal(outs[0], outs[1]), "LUT unpack changed the result"
 
 
 def test_decode_global_scale_power_of_two(nk):
