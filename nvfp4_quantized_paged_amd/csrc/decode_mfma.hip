@@ -34,8 +34,8 @@
 //    goes into addressing. Pools below 2 GiB use one descriptor per array,
 //    built once per wave (bounds: the whole pool); larger pools build a
 //    descriptor per page slice (bounds: the slice), because buffer offsets
-//    are 32-bit. Registers hold three chunks (64 tokens NVFP4, 32 tokens
-//    FP8): one computing, two in flight.
+//    are 32-bit. Registers hold three chunks of 32 tokens: one computing,
+//    two in flight.
 #include "common.hpp"
 
 namespace nvfp4kv {
@@ -457,20 +457,17 @@ hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
 }  // namespace
 
 // Chunk shape per launch (measured on MI355X, three register chunks per wave):
-//  * NVFP4, splits of up to 2048 tokens: 32-token chunks, 3 waves per SIMD;
-//    longer splits: 64-token chunks, 2 waves per SIMD (fewer softmax passes).
+//  * NVFP4: 32-token chunks, 3 waves per SIMD. 64-token chunks at 2 waves per
+//    SIMD measured slower for every split length tried (1024 tokens: 298 vs
+//    312 us; 4096 tokens: 396 vs 403 us).
 //  * FP8 (twice the bytes per token): 32-token chunks, 2 waves per SIMD.
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, bool lut, hipStream_t s) {
-  const int64_t split_len = ((int64_t)p.max_pages * p.page_size + p.num_splits - 1) / p.num_splits;
-  const bool short_split = split_len <= 2048;
   if (head_dim == 64) {
     if (fp8) return launch_mfma<64, true, 2, 2>(p, s);
-    if (lut) return short_split ? launch_mfma<64, false, 2, 3, true>(p, s) : launch_mfma<64, false, 4, 2, true>(p, s);
-    return short_split ? launch_mfma<64, false, 2, 3>(p, s) : launch_mfma<64, false, 4, 2>(p, s);
+    return lut ? launch_mfma<64, false, 2, 3, true>(p, s) : launch_mfma<64, false, 2, 3>(p, s);
   }
   if (fp8) return launch_mfma<128, true, 2, 2>(p, s);
-  if (lut) return short_split ? launch_mfma<128, false, 2, 3, true>(p, s) : launch_mfma<128, false, 4, 2, true>(p, s);
-  return short_split ? launch_mfma<128, false, 2, 3>(p, s) : launch_mfma<128, false, 4, 2>(p, s);
+  return lut ? launch_mfma<128, false, 2, 3, true>(p, s) : launch_mfma<128, false, 2, 3>(p, s);
 }
 
 }  // namespace nvfp4kv
