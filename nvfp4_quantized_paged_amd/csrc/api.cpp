@@ -154,6 +154,13 @@ int check_variant(int32_t variant, const char* fn) {
   return NVFP4KV_OK;
 }
 
+int page_shift(int32_t page_size) {
+  if (page_size & (page_size - 1)) return -1;
+  int k = 0;
+  while ((1 << k) < page_size) ++k;
+  return k;
+}
+
 hipError_t run_partial(const DecodeParams& p, int head_dim, bool fp8, int32_t variant, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   if (variant == NVFP4KV_VARIANT_VALU) return launch_decode_valu(p, head_dim, fp8, s);
@@ -225,6 +232,7 @@ NVFP4KV_API int nvfp4_kv_quantize(const nvfp4kv_geom* geom, const void* k, const
   p.head_dim = geom->head_dim;
   p.page_size = geom->page_size;
   p.num_slots = (int64_t)geom->num_pages * geom->page_size;
+  p.page_shift = page_shift(geom->page_size);
   p.data[0] = k_cache->data;
   p.data[1] = v_cache->data;
   p.scale[0] = k_cache->scale;
@@ -255,6 +263,7 @@ NVFP4KV_API int fp8_kv_quantize(const nvfp4kv_geom* geom, const void* k, const v
   p.head_dim = geom->head_dim;
   p.page_size = geom->page_size;
   p.num_slots = (int64_t)geom->num_pages * geom->page_size;
+  p.page_shift = page_shift(geom->page_size);
   p.data[0] = k_cache->data;
   p.data[1] = v_cache->data;
   p.gscale[0] = k_cache->scale;

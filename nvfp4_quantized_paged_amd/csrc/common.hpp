@@ -107,6 +107,7 @@ struct QuantizeParams {
   const int64_t* slot_mapping;
   int32_t num_tokens, num_kv_heads, head_dim, page_size;
   int64_t num_slots;        // num_pages * page_size: slots at or past it are skipped like negative ones
+  int32_t page_shift;       // log2(page_size) if it is a power of two, else -1
   uint8_t* data[2];         // NVFP4 data or FP8 bytes
   uint8_t* scale[2];        // NVFP4 block scales (unused for FP8)
   float gscale[2];          // NVFP4 global scale / FP8 per-tensor scale

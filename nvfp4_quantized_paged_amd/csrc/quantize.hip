@@ -6,7 +6,7 @@
 // persistent paged NVFP4 pool) and section A3 (E2M1 elements with one E4M3
 // scale per 16 elements and an FP32 tensor scale).
 //
-// One thread encodes one 16-channel block of one (token, head): it reads 32
+// One lane encodes one 16-channel block of one (token, head): it reads 32
 // bytes of bf16 with two 128-bit loads and writes 8 packed bytes plus one
 // scale byte. The element codes come from exact threshold compares: with
 // block scale S (E4M3) and tensor scale gs, the E2M1 midpoints m*S*gs are
@@ -44,90 +44,116 @@ __device__ inline uint32_t e2m1_code(float a, const float t[7]) {
   return c;
 }
 
-__global__ __launch_bounds__(256) void nvfp4_quantize_kernel(QuantizeParams p) {
-  const int which = blockIdx.y;                       // 0 = K, 1 = V
-  const int nb = p.head_dim / kBlock;
-  const int64_t items = (int64_t)p.num_tokens * p.num_kv_heads * nb;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= items) return;
-  const int blk = (int)(i % nb);
-  const int64_t th = i / nb;
-  const int h = (int)(th % p.num_kv_heads);
-  const int64_t t = th / p.num_kv_heads;
-  const int64_t slot = p.slot_mapping[t];
-  if (slot < 0 || slot >= p.num_slots) return;
-
-  float x[16];
-  load_block16(p.src[which] + t * p.src_stride + (int64_t)h * p.head_dim + blk * kBlock, x);
-
-  float amax = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
-  const float gs = p.gscale[which];
-  const uint32_t sbyte = e4m3_encode_nonneg(amax / (6.0f * gs));
-  const float sg = e4m3_to_f32(sbyte) * gs;
-  const float t7[7] = {0.25f * sg, 0.75f * sg, 1.25f * sg, 1.75f * sg,
-                       2.5f * sg, 3.5f * sg, 5.0f * sg};
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t sign = (__float_as_uint(x[e]) >> 31) << 3;
-    const uint32_t mag = sg > 0.0f ? e2m1_code(fabsf(x[e]), t7) : 0u;
-    const uint32_t nib = sign | mag;
-    if (e < 8) lo |= nib << (4 * e);
-    else hi |= nib << (4 * (e - 8));
+// Page and in-page position of a slot (a shift and a mask for power-of-two pages).
+__device__ inline void slot_position(const QuantizeParams& p, int64_t slot, int64_t& page, int64_t& off) {
+  if (p.page_shift >= 0) {
+    page = slot >> p.page_shift;
+    off = slot & (p.page_size - 1);
+  } else {
+    page = slot / p.page_size;
+    off = slot - page * p.page_size;
   }
-  const int64_t page = slot / p.page_size, off = slot % p.page_size;
-  const int64_t row = (page * p.num_kv_heads + h) * p.page_size + off;
-  *reinterpret_cast<uint2*>(p.data[which] + row * (p.head_dim / 2) + blk * 8) = make_uint2(lo, hi);
-  p.scale[which][row * nb + blk] = (uint8_t)sbyte;
 }
 
-// FP8: one thread per 16 elements, one 128-bit store.
-__global__ __launch_bounds__(256) void fp8_quantize_kernel(QuantizeParams p) {
-  const int which = blockIdx.y;
-  const int nb = p.head_dim / kBlock;
-  const int64_t items = (int64_t)p.num_tokens * p.num_kv_heads * nb;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= items) return;
-  const int blk = (int)(i % nb);
-  const int64_t th = i / nb;
-  const int h = (int)(th % p.num_kv_heads);
-  const int64_t t = th / p.num_kv_heads;
-  const int64_t slot = p.slot_mapping[t];
-  if (slot < 0 || slot >= p.num_slots) return;
+// Work mapping of both kernels: a wave owns one KV head of kTokPerWave
+// consecutive tokens; lane = (token, 16-element block), so the lanes of one
+// token read its head row contiguously and, when consecutive tokens go to
+// consecutive slots, one store instruction writes whole rows of the page.
+// Indices come from the grid and compile-time block counts (no 64-bit
+// division by runtime values).
+constexpr int kTokPerWave = 16;
+constexpr int kWavesPerGroup = 4;
 
-  float x[16];
-  load_block16(p.src[which] + t * p.src_stride + (int64_t)h * p.head_dim + blk * kBlock, x);
-  const float s = p.gscale[which];
-  uint32_t w[4] = {0, 0, 0, 0};
+template <int D>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void nvfp4_quantize_kernel(QuantizeParams p) {
+  constexpr int nb = D / kBlock;                 // blocks per head row
+  constexpr int kTokPerPass = 64 / nb;
+  const int which = blockIdx.z, h = blockIdx.y;   // 0 = K, 1 = V
+  const int lane = threadIdx.x & 63, blk = lane % nb;
+  const int64_t tw = ((int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6)) * kTokPerWave;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float y = (s == 1.0f) ? x[e] : x[e] / s;
-    const uint32_t byte = e4m3_encode_nonneg(fabsf(y)) | ((__float_as_uint(y) >> 31) << 7);
-    w[e / 4] |= byte << (8 * (e % 4));
+  for (int k = 0; k < kTokPerWave / kTokPerPass; ++k) {
+    const int64_t t = tw + k * kTokPerPass + lane / nb;
+    if (t >= p.num_tokens) break;
+    const int64_t slot = p.slot_mapping[t];
+    if (slot < 0 || slot >= p.num_slots) continue;
+
+    float x[16];
+    load_block16(p.src[which] + t * p.src_stride + (int64_t)h * D + blk * kBlock, x);
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    const float gs = p.gscale[which];
+    const uint32_t sbyte = e4m3_encode_nonneg(amax / (6.0f * gs));
+    const float sg = e4m3_to_f32(sbyte) * gs;
+    const float t7[7] = {0.25f * sg, 0.75f * sg, 1.25f * sg, 1.75f * sg,
+                         2.5f * sg, 3.5f * sg, 5.0f * sg};
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t sign = (__float_as_uint(x[e]) >> 31) << 3;
+      const uint32_t mag = sg > 0.0f ? e2m1_code(fabsf(x[e]), t7) : 0u;
+      const uint32_t nib = sign | mag;
+      if (e < 8) lo |= nib << (4 * e);
+      else hi |= nib << (4 * (e - 8));
+    }
+    int64_t page, off;
+    slot_position(p, slot, page, off);
+    const int64_t row = (page * p.num_kv_heads + h) * p.page_size + off;
+    *reinterpret_cast<uint2*>(p.data[which] + row * (D / 2) + blk * 8) = make_uint2(lo, hi);
+    p.scale[which][row * nb + blk] = (uint8_t)sbyte;
   }
-  const int64_t page = slot / p.page_size, off = slot % p.page_size;
-  const int64_t row = (page * p.num_kv_heads + h) * p.page_size + off;
-  *reinterpret_cast<uint4*>(p.data[which] + row * p.head_dim + blk * kBlock) =
-      make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// FP8: the same mapping, one 128-bit store per block.
+template <int D>
+__global__ __launch_bounds__(64 * kWavesPerGroup) void fp8_quantize_kernel(QuantizeParams p) {
+  constexpr int nb = D / kBlock;
+  constexpr int kTokPerPass = 64 / nb;
+  const int which = blockIdx.z, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, blk = lane % nb;
+  const int64_t tw = ((int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6)) * kTokPerWave;
+#pragma unroll
+  for (int k = 0; k < kTokPerWave / kTokPerPass; ++k) {
+    const int64_t t = tw + k * kTokPerPass + lane / nb;
+    if (t >= p.num_tokens) break;
+    const int64_t slot = p.slot_mapping[t];
+    if (slot < 0 || slot >= p.num_slots) continue;
+
+    float x[16];
+    load_block16(p.src[which] + t * p.src_stride + (int64_t)h * D + blk * kBlock, x);
+    const float s = p.gscale[which];
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float y = (s == 1.0f) ? x[e] : x[e] / s;
+      const uint32_t byte = e4m3_encode_nonneg(fabsf(y)) | ((__float_as_uint(y) >> 31) << 7);
+      w[e / 4] |= byte << (8 * (e % 4));
+    }
+    int64_t page, off;
+    slot_position(p, slot, page, off);
+    const int64_t row = (page * p.num_kv_heads + h) * p.page_size + off;
+    *reinterpret_cast<uint4*>(p.data[which] + row * D + blk * kBlock) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_nvfp4_quantize(const QuantizeParams& p, hipStream_t s) {
-  const int64_t items = (int64_t)p.num_tokens * p.num_kv_heads * (p.head_dim / kBlock);
-  if (items == 0) return hipSuccess;
-  dim3 grid((unsigned)((items + 255) / 256), 2);
-  hipLaunchKernelGGL(nvfp4_quantize_kernel, grid, dim3(256), 0, s, p);
+  if (p.num_tokens == 0) return hipSuccess;
+  const int64_t per_group = kTokPerWave * kWavesPerGroup;
+  const dim3 grid((unsigned)((p.num_tokens + per_group - 1) / per_group), (unsigned)p.num_kv_heads, 2);
+  if (p.head_dim == 64) hipLaunchKernelGGL(nvfp4_quantize_kernel<64>, grid, dim3(64 * kWavesPerGroup), 0, s, p);
+  else hipLaunchKernelGGL(nvfp4_quantize_kernel<128>, grid, dim3(64 * kWavesPerGroup), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_fp8_quantize(const QuantizeParams& p, hipStream_t s) {
-  const int64_t items = (int64_t)p.num_tokens * p.num_kv_heads * (p.head_dim / kBlock);
-  if (items == 0) return hipSuccess;
-  dim3 grid((unsigned)((items + 255) / 256), 2);
-  hipLaunchKernelGGL(fp8_quantize_kernel, grid, dim3(256), 0, s, p);
+  if (p.num_tokens == 0) return hipSuccess;
+  const int64_t per_group = kTokPerWave * kWavesPerGroup;
+  const dim3 grid((unsigned)((p.num_tokens + per_group - 1) / per_group), (unsigned)p.num_kv_heads, 2);
+  if (p.head_dim == 64) hipLaunchKernelGGL(fp8_quantize_kernel<64>, grid, dim3(64 * kWavesPerGroup), 0, s, p);
+  else hipLaunchKernelGGL(fp8_quantize_kernel<128>, grid, dim3(64 * kWavesPerGroup), 0, s, p);
   return hipGetLastError();
 }
 
