@@ -88,12 +88,13 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void nvfp4_quantize_kernel(Qua
     const float sg = e4m3_to_f32(sbyte) * gs;
     const float t7[7] = {0.25f * sg, 0.75f * sg, 1.25f * sg, 1.75f * sg,
                          2.5f * sg, 3.5f * sg, 5.0f * sg};
+    // S = 0 (an all-zero block): every magnitude code is 0; computed without a branch
+    const uint32_t keep = sg > 0.0f ? 7u : 0u;
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const uint32_t sign = (__float_as_uint(x[e]) >> 31) << 3;
-      const uint32_t mag = sg > 0.0f ? e2m1_code(fabsf(x[e]), t7) : 0u;
-      const uint32_t nib = sign | mag;
+      const uint32_t nib = sign | (e2m1_code(fabsf(x[e]), t7) & keep);
       if (e < 8) lo |= nib << (4 * e);
       else hi |= nib << (4 * (e - 8));
     }
