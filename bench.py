@@ -17,6 +17,13 @@ before timing. Prints ONE JSON line on stdout; diagnostics go to stderr.
                   launch / mean launch time (HIP events on the launch stream)
   cpu_baseline    the CPU oracle (dequantize + fp64 attention) on a bounded
                   sample of (sequence, KV head) slices of the same workload
+  fp8, extreme_context_1m, agentic_prefix_reuse
+                  the same step over the FP8 pool, the 1M batch-2 step, and
+                  the agentic prefix-reuse step with per-kernel times
+  decode_figures  decode tokens/s of NVFP4 and FP8 at the batch sizes of the
+                  page's decode figures (Fig. 6 iso-concurrency: 44 / 10 / 1
+                  at 32K / 160K / 1M; Fig. 7 iso-capacity: NVFP4 70 / 15 / 2
+                  against FP8 44 / 10 / 1)
 """
 import argparse
 import hashlib
@@ -95,15 +102,16 @@ def ramp(fn, seconds=RAMP_S):
 
 
 class Bench:
-    def __init__(self, nk, wl, fp8, variant):
+    def __init__(self, nk, wl, fp8, variant, batch=None):
         import torch
         from synth.workload import build_uniform_workload
         self.torch = torch
         self.nk, self.wl, self.fp8, self.variant = nk, wl, fp8, variant
+        self.batch = B = wl.batch if batch is None else batch
         t = time.time()
-        self.w = build_uniform_workload(nk, wl, fp8=fp8)
-        log(f"[bench] built {'fp8' if fp8 else 'nvfp4'} {wl.name} in {time.time() - t:.1f}s")
-        B, H, d, P, L = wl.batch, wl.num_kv_heads, wl.head_dim, wl.page_size, wl.context
+        self.w = build_uniform_workload(nk, wl, fp8=fp8, batch=B)
+        log(f"[bench] built {'fp8' if fp8 else 'nvfp4'} {wl.name} batch {B} in {time.time() - t:.1f}s")
+        H, d, P, L = wl.num_kv_heads, wl.head_dim, wl.page_size, wl.context
         g = torch.Generator(device="cuda")
         g.manual_seed(wl.seed + 1000)
         self.k_new = torch.randn((B, H, d), generator=g, device="cuda").to(torch.bfloat16)
@@ -125,7 +133,7 @@ class Bench:
 
     def merge(self):
         scale = self.w.vp.scale if self.fp8 else self.w.vp.global_scale
-        self.nk.nvfp4kv_lse_merge(self.ws, self.wl.batch, self.wl.num_q_heads, self.wl.head_dim, self.S,
+        self.nk.nvfp4kv_lse_merge(self.ws, self.batch, self.wl.num_q_heads, self.wl.head_dim, self.S,
                                   scale, self.out)
 
     def step(self):
@@ -162,6 +170,40 @@ class Bench:
     def free(self):
         del self.w, self.ws, self.out
         self.torch.cuda.empty_cache()
+
+
+def decode_figures(nk, variant, steps, warmup, measured):
+    """Kernel-level decode throughput at the batch sizes of the NVFP4 page's
+    decode figures: iso-concurrency (Fig. 6, both caches at the same batch)
+    and iso-capacity (Fig. 7, each cache at the batch it fits in the same
+    memory), at 32K, 160K and 1M context. One step = quantize the new token
+    + decode partial + merge; decode tokens/s = batch / step time. Steps
+    already timed by the main benchmark are reused from `measured`."""
+    import synth
+
+    def run(idx, batch, fp8):
+        key = (idx, batch, fp8)
+        if key not in measured:
+            b = Bench(nk, synth.WORKLOADS[idx], fp8, variant, batch=batch)
+            measured[key] = (b.time_steps(steps, warmup), b.S)
+            b.free()
+        t, S = measured[key]
+        wl = synth.WORKLOADS[idx]
+        kv = 2 * batch * wl.context * wl.num_kv_heads * (wl.head_dim if fp8 else wl.head_dim // 2 + wl.head_dim // 16)
+        return {"batch": batch, "num_splits": S, "ms_per_step": round(t * 1e3, 4),
+                "decode_tokens_per_s": round(batch / t, 1), "kv_gbs": round(kv / t / 1e9, 1)}
+    out = {"iso_concurrency": {}, "iso_capacity": {}}
+    for name, (idx, batch) in synth.ISO_CONCURRENCY.items():
+        nv, f8 = run(idx, batch, False), run(idx, batch, True)
+        out["iso_concurrency"][name] = {"nvfp4": nv, "fp8": f8,
+                                        "nvfp4_over_fp8": round(nv["decode_tokens_per_s"] / f8["decode_tokens_per_s"], 3)}
+    for name, (idx, batches) in synth.ISO_CAPACITY.items():
+        nv, f8 = run(idx, batches["nvfp4"], False), run(idx, batches["fp8"], True)
+        out["iso_capacity"][name] = {"nvfp4": nv, "fp8": f8,
+                                     "nvfp4_over_fp8": round(nv["decode_tokens_per_s"] / f8["decode_tokens_per_s"], 3)}
+    log("[bench] decode figures: " + ", ".join(
+        f"{k} {n} x{v['nvfp4_over_fp8']}" for k in out for n, v in out[k].items()))
+    return out
 
 
 def agentic(nk, wl, steps, warmup):
@@ -366,6 +408,10 @@ def main():
         log(f"[bench] 1m step {t4 * 1e3:.3f} ms")
 
         result["agentic_prefix_reuse"] = agentic(nk, synth.WORKLOADS[5], max(5, args.steps // 2), args.warmup)
+
+        measured = {(3, wl.batch, False): (t_step, S), (3, wl.batch, True): (t8, S),
+                    (4, wl4.batch, False): (t4, wl4.num_splits)}
+        result["decode_figures"] = decode_figures(nk, variant, max(5, args.steps // 2), args.warmup, measured)
 
     if not args.no_cpu_baseline:
         t = time.time()

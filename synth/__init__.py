@@ -78,7 +78,16 @@ WORKLOADS = {
     4: Workload(4, "extreme-context-1m", 2, 40, 8, 128, 64, 1048576, False, 256),
     5: Workload(5, "agentic-prefix-reuse", 64, 32, 8, 128, 16, 0, False, 0,
                 len_min=3200, len_max=10000, shared_prefix=2800, chunk=500),
+    # the third context length of the synthetic benchmark (section A3, 160K), N(0,1) values
+    6: Workload(6, "long-context-160k", 10, 40, 8, 128, 64, 163840, False, 0),
 }
+
+# Decode batch sizes of the NVFP4 page's decode figures, per context length:
+# iso-concurrency (Fig. 6: the same batch for both caches) and iso-capacity
+# (Fig. 7: the batch each cache fits in the same memory).
+ISO_CONCURRENCY = {"32k": (3, 44), "160k": (6, 10), "1m": (4, 1)}
+ISO_CAPACITY = {"32k": (3, {"fp8": 44, "nvfp4": 70}), "160k": (6, {"fp8": 10, "nvfp4": 15}),
+                "1m": (4, {"fp8": 1, "nvfp4": 2})}
 
 
 # ---------------------------------------------------------------------------

@@ -578,6 +578,61 @@ def test_full_size_extreme_context_1m_sampled(nk):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("idx,batch,fp8", [(6, 15, False), (6, 10, True), (3, 70, False), (4, 1, True)],
+                         ids=["160k-b15-nvfp4", "160k-b10-fp8", "32k-b70-nvfp4", "1m-b1-fp8"])
+def test_full_size_decode_figure_shapes_sampled(nk, idx, batch, fp8):
+    """The other batch sizes of the page's decode figures (iso-concurrency and
+    iso-capacity), in the benchmark's launch configuration. Up to 160K the
+    sampled (sequence, KV head) outputs are checked whole against the oracle;
+    at 1M, sampled splits' normalised partials over their own tokens."""
+    from synth.workload import build_uniform_workload
+    wl = synth.WORKLOADS[idx]
+    G, d, P, L = wl.group, wl.head_dim, wl.page_size, wl.context
+    w = build_uniform_workload(nk, wl, keep_bf16=True, fp8=fp8, batch=batch)
+    S = wl.num_splits or nk.nvfp4_paged_decode_num_splits(batch, wl.num_kv_heads, w.bt.shape[1], P)
+    say(f"case full size {wl.name}: B {batch} L {L} splits {S} {'fp8' if fp8 else 'nvfp4'}")
+    partial = nk.fp8_paged_decode_partial if fp8 else nk.nvfp4_paged_decode_partial
+    ws = partial(w.q, w.kp, w.vp, w.bt, w.sl, wl.sm_scale, S)
+    out = torch.empty_like(w.q)
+    nk.nvfp4kv_lse_merge(ws, batch, wl.num_q_heads, d, S, 1.0, out)
+    torch.cuda.synchronize()
+    per = -(-(-(-L // S)) // P) * P
+    split_level = L > 200_000
+    if split_level:
+        po, pml = nk.split_partials(ws, batch, wl.num_q_heads, d, S)
+        po, pml = po.double().cpu().numpy(), pml.double().cpu().numpy()
+    rng = np.random.default_rng(17 + idx)
+    for b, g in [(0, 0), (batch - 1, wl.num_kv_heads - 1), (int(rng.integers(batch)), int(rng.integers(8)))]:
+        j = int(rng.integers(S)) if split_level else 0
+        t0, t1 = (j * per, min(L, (j + 1) * per)) if split_level else (0, L)
+        say(f"  sample b {b} g {g}" + (f" split {j} tokens [{t0}, {t1})" if split_level else ""))
+        kb, vb = _sample_rows(w, b, g, t0, t1)
+        t = np.arange(t0, t1)
+        pages = torch.from_numpy(w.bt[b].cpu().numpy()[t // P].astype(np.int64)).cuda()
+        offs = torch.from_numpy(t % P).cuda()
+        if fp8:
+            kr, vr = of8.quantize_rows(kb), of8.quantize_rows(vb)
+            assert np.array_equal(w.kp.data[pages, g, offs].cpu().numpy(), kr[:, 0]), "sampled K bytes"
+            khat, vhat = of8.dequant_cache(kr), of8.dequant_cache(vr)
+        else:
+            rd, rs = onv.quantize_rows(kb)
+            _check_sampled_bytes(w, b, g, t0, t1, rd, rs)
+            vd_, vs_ = onv.quantize_rows(vb)
+            khat, vhat = onv.dequant_rows(rd, rs), onv.dequant_rows(vd_, vs_)
+        qb = synth.bf16_tensor_bits(w.q[b, g * G:(g + 1) * G])
+        ref, mass = oatt.decode_heads(onv.bf16_to_f64(qb), khat, vhat, wl.sm_scale)
+        if split_level:
+            hs = slice(g * G, (g + 1) * G)
+            part = po[b, hs, j] / pml[b, hs, j, 1:2]
+            e = np.abs(part - ref) / np.maximum(1.0, mass)
+            say(f"    partial max e {e.max():.3e} mean e {e.mean():.3e}")
+            assert e.max() <= TOL_MAX and e.mean() <= TOL_MEAN
+        else:
+            check_out(out[b, g * G:(g + 1) * G], ref, mass, f"{wl.name} B{batch} b{b} g{g}")
+    del w, ws
+    torch.cuda.empty_cache()
+
+
 def test_full_size_agentic_sampled(nk):
     """64 sequences, L_b ~ U[3200, 10000], a 2,800-token prefix on 175 shared
     pages, 500-token chunks: the whole step at full size, then sampled
