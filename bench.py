@@ -261,7 +261,21 @@ def agentic(nk, wl, steps, warmup):
                    "kv_gbs_unique": round(by["decode_read_unique"] / per["decode"] / 1e9, 1)},
         "bytes": by,
     }
-    log(f"[bench] agentic step {t_step * 1e3:.3f} ms: " + ", ".join(f"{k} {v * 1e3:.3f} ms" for k, v in per.items()))
+    # global-scale calibration of the chunk (absmax of K and V), not part of the step
+    amax = torch.zeros(2, dtype=torch.float32, device="cuda")
+    cal = lambda: (nk.nvfp4_kv_absmax(w.k_chunk, amax[0:1]), nk.nvfp4_kv_absmax(w.v_chunk, amax[1:2]))
+    for _ in range(warmup):
+        cal()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        cal()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_cal = e0.elapsed_time(e1) / steps / 1e3
+    res["absmax_calibration"] = {"ms": round(t_cal * 1e3, 4), "gbs": round(by["quant_read"] / t_cal / 1e9, 1)}
+    log(f"[bench] agentic step {t_step * 1e3:.3f} ms: " + ", ".join(f"{k} {v * 1e3:.3f} ms" for k, v in per.items())
+        + f"; absmax calibration {t_cal * 1e3:.3f} ms")
     del w, ws, out
     torch.cuda.empty_cache()
     return res

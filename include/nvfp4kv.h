@@ -118,8 +118,12 @@ typedef struct {
  *   S = E4M3(amax / (6 * global_scale)), rounded to nearest even, saturating
  *   at 448; each element gets the E2M1 code nearest to |x| / (S * global_scale),
  *   ties to the even code, saturating at 6 (S == 0 gives magnitude 0); the
- *   sign bit is always kept. For a global_scale that is a power of two the
- *   result is bit-exact against that definition.
+ *   sign bit is always kept. The arithmetic is FP32: S is encoded from
+ *   fl32(amax / fl32(6 * global_scale)), and the element codes come from
+ *   comparing |x| with fl32(m * fl32(S * global_scale)) for the E2M1 midpoints
+ *   m (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; ties at 0.75, 1.75 and 3.5 round
+ *   up). For a power-of-two global_scale every step is exact, so this is the
+ *   real-number definition above.
  * Nothing outside the addressed slots is written; shared (aliased) pages are
  * never touched unless a slot names them.
  */
@@ -237,6 +241,33 @@ int fp8_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,
                              const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
                              float sm_scale, int32_t num_splits, int32_t variant,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_kv_absmax -- calibration of the FP32 tensor-level scale (section A3:
+ * NVFP4's per-tensor scale, fixed to 1.0 in the pages' runs, section A7).
+ *
+ *   x            device bf16; element (t, h, c) at [t * token_stride + h * head_dim + c]
+ *   token_stride elements between tokens (>= num_kv_heads * head_dim, multiple of 8)
+ *   num_tokens   T >= 0 (0 is a no-op)
+ *   amax_inout   device float, caller-initialised (0.0f, or the running value of
+ *                earlier calls); on completion it holds max(*amax_inout, max |x|).
+ *                NaN elements are ignored. Must be >= 0 on entry.
+ *
+ * Stream-ordered; the caller reads the result back (or keeps folding chunks
+ * into it) and derives the pool's global_scale with
+ * nvfp4_global_scale_from_absmax. Calls that fold into the same float may
+ * run concurrently (the update is an atomic maximum).
+ */
+int nvfp4_kv_absmax(const void* x, int64_t token_stride, int32_t num_tokens, int32_t num_kv_heads,
+                    int32_t head_dim, float* amax_inout, void* stream);
+
+/*
+ * nvfp4_global_scale_from_absmax -- host helper: the global scale that maps a
+ * tensor's absolute maximum onto the top of both grids, amax / (448 * 6) in
+ * FP32 (largest block scale 448, largest element 6); 1.0 when amax is 0,
+ * negative, NaN or infinite.
+ */
+float nvfp4_global_scale_from_absmax(float amax);
 
 /* Text of the last non-zero return on the calling thread ("" if none). */
 const char* nvfp4kv_last_error(void);

@@ -61,6 +61,8 @@ _SIGNATURES = {
     "fp8_paged_decode_partial": (ctypes.c_int, [P_GEOM, c_vp, P_F8, P_F8, c_vp, c_i32, c_vp, c_i32, c_i32,
                                                 c_f32, c_i32, c_i32, c_vp, c_size, c_vp]),
     "nvfp4kv_lse_merge": (ctypes.c_int, [c_vp, c_size, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_vp]),
+    "nvfp4_kv_absmax": (ctypes.c_int, [c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "nvfp4_global_scale_from_absmax": (c_f32, [c_f32]),
 }
 
 _lib_handle = None
@@ -203,6 +205,26 @@ def nvfp4_kv_quantize(k, v, slot_mapping, k_pool: NVFP4Pool, v_pool: NVFP4Pool, 
 
 def fp8_kv_quantize(k, v, slot_mapping, k_pool: FP8Pool, v_pool: FP8Pool, stream=None):
     _quantize(lib().fp8_kv_quantize, k, v, slot_mapping, k_pool, v_pool, stream)
+
+
+def nvfp4_kv_absmax(x, amax, stream=None):
+    """Fold max |x| of x [T][Hkv][d] (bf16, dense heads) into amax (float32 device tensor of
+    one element, caller-initialised, >= 0)."""
+    _need(amax, torch.float32, "amax")
+    if amax.numel() != 1:
+        raise ValueError("amax must hold one float")
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 3:
+        raise TypeError("x must be a bf16 device tensor [T][Hkv][d]")
+    if x.shape[0] > 0 and (x.stride(2) != 1 or x.stride(1) != x.shape[2]):
+        raise ValueError("x must be [T][Hkv][d] with dense heads")
+    stride = x.stride(0) if x.shape[0] > 0 else x.shape[1] * x.shape[2]
+    _check(lib().nvfp4_kv_absmax(x.data_ptr(), stride, x.shape[0], x.shape[1], x.shape[2], amax.data_ptr(),
+                                 _stream(stream)))
+
+
+def nvfp4_global_scale_from_absmax(amax: float) -> float:
+    """amax / (448 * 6) in FP32 (1.0 for amax 0, negative or non-finite)."""
+    return float(lib().nvfp4_global_scale_from_absmax(float(amax)))
 
 
 def nvfp4_kv_dequant_workspace(k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables, prefix_lens,

@@ -189,6 +189,32 @@ hipError_t run_merge(const DecodeParams& d, int head_dim, float out_scale, void*
 
 NVFP4KV_API int nvfp4kv_abi_version(void) { return NVFP4KV_ABI_VERSION; }
 
+NVFP4KV_API int nvfp4_kv_absmax(const void* x, int64_t token_stride, int32_t num_tokens, int32_t num_kv_heads,
+                                int32_t head_dim, float* amax_inout, void* stream) {
+  const char* fn = "nvfp4_kv_absmax";
+  if (num_tokens < 0) return fail(NVFP4KV_EINVAL, "%s: num_tokens %d < 0", fn, num_tokens);
+  if (num_kv_heads <= 0) return fail(NVFP4KV_EINVAL, "%s: num_kv_heads %d <= 0", fn, num_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(NVFP4KV_EUNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
+  if (num_tokens == 0) return launched(hipSuccess, fn);
+  if (!x || !amax_inout) return fail(NVFP4KV_EINVAL, "%s: x and amax must be non-NULL", fn);
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (row > 0x7FFFFFFFLL) return fail(NVFP4KV_EINVAL, "%s: num_kv_heads * head_dim too large", fn);
+  if (token_stride < row)
+    return fail(NVFP4KV_EINVAL, "%s: token_stride %lld < num_kv_heads * head_dim", fn, (long long)token_stride);
+  if (!aligned16(x) || token_stride % 8 != 0 || reinterpret_cast<uintptr_t>(amax_inout) % 4 != 0)
+    return fail(NVFP4KV_EALIGN, "%s: x must be 16-byte aligned, token_stride a multiple of 8, amax 4-byte aligned",
+                fn);
+  return launched(launch_absmax(static_cast<const uint16_t*>(x), token_stride, num_tokens, (int32_t)row,
+                                amax_inout, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+NVFP4KV_API float nvfp4_global_scale_from_absmax(float amax) {
+  if (!(amax > 0.0f) || !isfinite(amax)) return 1.0f;
+  return amax / (448.0f * 6.0f);
+}
+
 NVFP4KV_API const char* nvfp4kv_last_error(void) { return g_error; }
 
 NVFP4KV_API int32_t nvfp4_paged_decode_num_splits(int32_t batch, int32_t num_kv_heads,

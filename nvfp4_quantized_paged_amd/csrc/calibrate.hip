@@ -1,0 +1,91 @@
+// Tensor absolute maximum for a calibrated NVFP4 global scale.
+//
+// "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
+// section A3: besides the per-16-element E4M3 block scales, NVFP4 carries one
+// FP32 scale per tensor; it is fixed to 1.0 in the pages' experiments and is
+// named there as the lever for accuracy. Calibrating it from the tensor's
+// absolute maximum maps the largest block onto the top of both grids (block
+// scale 448, element 6), so no block scale saturates and small blocks keep
+// their resolution.
+//
+// The kernel folds max |x| of a [tokens][kv_heads][head_dim] bf16 tensor into
+// a running maximum in device memory. Grid-stride over token rows; threads
+// take 16-byte pieces of a row, so every load instruction reads contiguous
+// row bytes, with eight independent loads in flight per thread; one atomic
+// per workgroup (same-address atomics serialise, so the grid is small). Non-negative floats order like
+// their bit patterns, so the fold is an integer atomic max on the bits.
+// NaN inputs are ignored (fmaxf), like the block-scale amax of the encoder.
+#include "common.hpp"
+
+namespace nvfp4kv {
+
+namespace {
+
+constexpr int kAbsmaxThreads = 256;
+constexpr int kAbsmaxMaxGroups = 512;       // one atomic per workgroup: few workgroups, each with more loads in flight
+constexpr int kAbsmaxUnroll = 8;             // independent 16-byte loads in flight per thread
+
+__device__ inline float absmax8(uint4 w, float m) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m = fmaxf(m, fabsf(__uint_as_float(ww[e] << 16)));
+    m = fmaxf(m, fabsf(__uint_as_float(ww[e] & 0xFFFF0000u)));
+  }
+  return m;
+}
+
+// A workgroup pass covers `tpp` whole token rows (row_chunks <= 256: thread =
+// (row in the pass, 16-byte piece)); longer rows are walked piece by piece.
+__global__ __launch_bounds__(kAbsmaxThreads) void absmax_kernel(const uint16_t* x, int64_t stride,
+                                                               int32_t num_tokens, int32_t row_chunks,
+                                                               uint32_t* amax_bits) {
+  __shared__ float red[kAbsmaxThreads / 64];
+  float m = 0.0f;
+  if (row_chunks <= kAbsmaxThreads) {
+    const int tpp = kAbsmaxThreads / row_chunks;
+    const int lt = threadIdx.x / row_chunks, c = threadIdx.x % row_chunks;
+    if (lt < tpp) {
+      const int64_t step = (int64_t)gridDim.x * tpp;
+      for (int64_t t0 = (int64_t)blockIdx.x * tpp + lt; t0 < num_tokens; t0 += kAbsmaxUnroll * step) {
+        uint4 w[kAbsmaxUnroll];
+#pragma unroll
+        for (int k = 0; k < kAbsmaxUnroll; ++k) {
+          const int64_t t = t0 + k * step;
+          w[k] = t < num_tokens ? reinterpret_cast<const uint4*>(x + t * stride)[c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < kAbsmaxUnroll; ++k) m = absmax8(w[k], m);
+      }
+    }
+  } else {
+    for (int64_t t = blockIdx.x; t < num_tokens; t += gridDim.x) {
+      const uint4* row = reinterpret_cast<const uint4*>(x + t * stride);
+      for (int c = threadIdx.x; c < row_chunks; c += kAbsmaxThreads) m = absmax8(row[c], m);
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kAbsmaxThreads / 64; ++w) m = fmaxf(m, red[w]);
+    atomicMax(amax_bits, __float_as_uint(m));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_absmax(const uint16_t* x, int64_t stride, int32_t num_tokens, int32_t row_elems,
+                         float* amax, hipStream_t s) {
+  if (num_tokens == 0) return hipSuccess;
+  const int chunks = row_elems / 8;
+  const int64_t tpp = chunks <= kAbsmaxThreads ? kAbsmaxThreads / chunks : 1;
+  const int64_t want = (num_tokens + tpp * kAbsmaxUnroll - 1) / (tpp * kAbsmaxUnroll);
+  const int groups = (int)(want < kAbsmaxMaxGroups ? want : kAbsmaxMaxGroups);
+  hipLaunchKernelGGL(absmax_kernel, dim3(groups), dim3(kAbsmaxThreads), 0, s, x, stride, num_tokens,
+                     row_elems / 8, reinterpret_cast<uint32_t*>(amax));
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4kv

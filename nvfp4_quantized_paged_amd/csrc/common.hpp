@@ -155,5 +155,8 @@ hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, bool fp8, hip
 // lut: NVFP4 unpack through a register lookup table instead of the conversion instruction
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, bool lut, hipStream_t s);
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t s);
+// running max |x| of a [tokens][row_elems] bf16 tensor (rows `stride` elements apart) into *amax
+hipError_t launch_absmax(const uint16_t* x, int64_t stride, int32_t num_tokens, int32_t row_elems,
+                         float* amax, hipStream_t s);
 
 }  // namespace nvfp4kv

@@ -90,14 +90,19 @@ def f64_to_bf16_exact(x: np.ndarray) -> np.ndarray:
 
 def dequant_workspace(cache_hat: np.ndarray, block_tables: np.ndarray,
                       prefix_lens: np.ndarray, ws_row_offsets: np.ndarray,
-                      rows: int, fill: int = 0) -> np.ndarray:
+                      rows: int, fill: int = 0, cache_bits: np.ndarray = None) -> np.ndarray:
     """Extend-path workspace: rows [off_b, off_b + prefix_len_b) hold the
     dequantized tokens [0, prefix_len_b) of sequence b as bf16 bits
-    [rows][Hkv][d]; other rows keep ``fill``."""
+    [rows][Hkv][d]; other rows keep ``fill``. The values are cache_hat
+    (exact in bf16), or, when given, the bf16 bits ``cache_bits`` of every
+    cache element (a calibrated global scale rounds them)."""
     _, Hkv, _, d = cache_hat.shape
     ws = np.full((rows, Hkv, d), fill, dtype=np.uint16)
     for b in range(len(prefix_lens)):
         n = int(prefix_lens[b])
         off = int(ws_row_offsets[b])
-        ws[off:off + n] = f64_to_bf16_exact(gather_tokens(cache_hat, block_tables[b], n))
+        if cache_bits is None:
+            ws[off:off + n] = f64_to_bf16_exact(gather_tokens(cache_hat, block_tables[b], n))
+        else:
+            ws[off:off + n] = gather_tokens(cache_bits, block_tables[b], n)
     return ws

@@ -59,6 +59,64 @@ def encode_blocks(x: np.ndarray, gs: float = 1.0):
     return codes.astype(np.uint8), s_byte
 
 
+# E2M1 magnitude midpoints, and whether a value exactly on one rounds up
+# (the upper neighbour has the even code: 0.75 -> 1, 1.75 -> 2, 3.5 -> 4)
+MIDPOINTS = ((0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False), (3.5, True), (5.0, False))
+
+
+def is_power_of_two(gs: float) -> bool:
+    m, _ = np.frexp(np.float64(gs))
+    return bool(gs > 0 and m == 0.5)
+
+
+def encode_blocks_fp32(x: np.ndarray, gs: float):
+    """Encode with a calibrated global scale, in the FP32 arithmetic of the
+    NVFP4 recipe (reading A12 of this build; the pages fix only that the
+    tensor scale is FP32):
+
+      S     = E4M3(fl32(amax / fl32(6 * gs)))        nearest even, saturating
+      S_eff = fl32(S * gs)
+      code  = number of E2M1 midpoints m with |x| > fl32(m * S_eff), counting
+              |x| == fl32(m * S_eff) as passing where a tie rounds up
+              (S_eff == 0: code 0)
+
+    For a power-of-two gs every product and quotient is exact and this is
+    encode_blocks (pinned by the tests). x: float64 [..., 16] of bf16 values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] == BLOCK
+    a = np.abs(x).astype(np.float32)                     # exact: bf16 values
+    amax = a.max(axis=-1)
+    g = np.float32(gs)
+    s_byte = e4m3_encode_nonneg((amax / (np.float32(6.0) * g)).astype(np.float64))
+    s_eff = (E4M3_VALUES[s_byte].astype(np.float32) * g)[..., None]
+    mag = np.zeros(x.shape, dtype=np.int64)
+    for m, tie_up in MIDPOINTS:
+        t = np.float32(m) * s_eff
+        mag += (a > t) | ((a == t) & tie_up)
+    mag = np.where(s_eff > 0, mag, 0)
+    sign = np.signbit(x).astype(np.int64)
+    return ((sign << 3) | mag).astype(np.uint8), s_byte
+
+
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """bf16 bits (uint16) of float32 values, rounded to nearest even (finite values)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def workspace_bits(data: np.ndarray, scale: np.ndarray, gs: float = 1.0) -> np.ndarray:
+    """bf16 bits of dequantized values as a bf16 workspace holds them:
+    bf16(fl32(e2m1 * fl32(S * gs))). For a power-of-two gs both roundings are
+    exact (every E2M1 x E4M3 product is a bf16 value), so this is the exact value."""
+    codes = unpack_nibbles(data)
+    vals = E2M1_VALUES[codes.astype(np.int64)].astype(np.float32)
+    s = E4M3_VALUES[np.asarray(scale, dtype=np.int64)].astype(np.float32) * np.float32(gs)
+    d = vals.shape[-1]
+    prod = vals.reshape(vals.shape[:-1] + (d // BLOCK, BLOCK)) * s[..., None]
+    return f32_to_bf16_rne(prod.reshape(vals.shape))
+
+
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:
     """[..., 2n] 4-bit codes -> [..., n] bytes, element 2i in the low nibble."""
     c = np.asarray(codes, dtype=np.uint8)
@@ -74,11 +132,13 @@ def unpack_nibbles(data: np.ndarray) -> np.ndarray:
 
 
 def quantize_rows(x_bits: np.ndarray, gs: float = 1.0):
-    """Quantize token rows [T][H][d] (bf16 bits) to (data [T][H][d/2], scale [T][H][d/16])."""
+    """Quantize token rows [T][H][d] (bf16 bits) to (data [T][H][d/2], scale [T][H][d/16]).
+    Power-of-two gs: the real-number encode; any other gs: its FP32 recipe."""
     x = bf16_to_f64(x_bits)
     T, H, d = x.shape
     assert d % BLOCK == 0
-    codes, s = encode_blocks(x.reshape(T, H, d // BLOCK, BLOCK), gs)
+    enc = encode_blocks if is_power_of_two(gs) else encode_blocks_fp32
+    codes, s = enc(x.reshape(T, H, d // BLOCK, BLOCK), gs)
     data = pack_nibbles(codes.reshape(T, H, d))
     return data, s.reshape(T, H, d // BLOCK)
 

@@ -26,13 +26,14 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^(?:const\s+char\s*\*|int32_t|int|size_t)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:const\s+char\s*\*|int32_t|int|size_t|float)\s+(\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("nvfp4_kv_quantize", "nvfp4_kv_dequant_workspace", "nvfp4_paged_decode_attn",
-                     "fp8_paged_decode_attn", "fp8_kv_quantize", "nvfp4kv_lse_merge"):
+                     "fp8_paged_decode_attn", "fp8_kv_quantize", "nvfp4kv_lse_merge", "nvfp4_kv_absmax",
+                     "nvfp4_global_scale_from_absmax"):
         assert required in names
 
 
@@ -181,3 +182,28 @@ def test_fp8_entry_points_validate(L):
     d = L.lib().fp8_paged_decode_attn
     assert d(ctypes.byref(g), FAKE, ctypes.byref(kc), ctypes.byref(kc), FAKE, 16, FAKE, 1, 4, 0.125, 1, FAKE, 8,
              FAKE, None) == L.EWORKSPACE
+
+
+def test_absmax_rejects_bad_arguments(L):
+    f = L.lib().nvfp4_kv_absmax
+    FAKE16, FAKE4 = 1 << 20, (1 << 20) + 4
+    assert f(FAKE16, 1024, 0, 8, 128, None, None) == L.OK            # no tokens: nothing to do
+    assert f(FAKE16, 1024, -1, 8, 128, FAKE4, None) == L.EINVAL
+    assert f(FAKE16, 1024, 4, 0, 128, FAKE4, None) == L.EINVAL
+    assert f(FAKE16, 1024, 4, 8, 96, FAKE4, None) == L.EUNSUPPORTED
+    assert f(None, 1024, 4, 8, 128, FAKE4, None) == L.EINVAL
+    assert f(FAKE16, 1024, 4, 8, 128, None, None) == L.EINVAL
+    assert f(FAKE16, 1000, 4, 8, 128, FAKE4, None) == L.EINVAL     # stride below a token row
+    assert f(FAKE16 + 2, 1024, 4, 8, 128, FAKE4, None) == L.EALIGN
+    assert f(FAKE16, 1028, 4, 8, 128, FAKE4, None) == L.EALIGN
+    assert f(FAKE16, 1024, 4, 8, 128, FAKE4 + 1, None) == L.EALIGN
+
+
+def test_global_scale_from_absmax(L):
+    g = L.nvfp4_global_scale_from_absmax
+    assert g(2688.0) == 1.0                       # 448 * 6: the largest block maps onto scale 448, element 6
+    assert g(1344.0) == 0.5
+    assert g(0.0) == 1.0 and g(-3.0) == 1.0 and g(float("inf")) == 1.0 and g(float("nan")) == 1.0
+    import numpy as np
+    for a in (1.0, 3.14159, 1e-20, 6.5e4, 1e30):
+        assert g(a) == float(np.float32(a) / np.float32(2688.0))

@@ -170,7 +170,10 @@ def _crafted_rows(rng, T, H, d):
     return flat.reshape(T, H, d)
 
 
-@pytest.mark.parametrize("gs", [1.0, 2.0, 0.5])
+GS_THIRD = float(np.float32(1.0 / 3.0))     # a calibrated (non-power-of-two) global scale
+
+
+@pytest.mark.parametrize("gs", [1.0, 2.0, 0.5, GS_THIRD])
 def test_quantize_crafted_values_and_skipped_slots(nk, gs):
     rng = np.random.default_rng(11)
     T, H, P, d, pages = 1536, 2, 32, 64, 64
@@ -253,16 +256,16 @@ def test_fp8_quantize_every_bf16_value(nk):
 # dequantize-to-workspace
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape", [(8, 128, 16), (1, 64, 16), (3, 64, 32)])
+@pytest.mark.parametrize("shape", [(8, 128, 16, 1.0), (1, 64, 16, 1.0), (3, 64, 32, 1.0), (8, 128, 16, GS_THIRD)])
 def test_dequant_workspace_agentic_small(nk, shape):
-    H0, d0, P0 = shape
+    H0, d0, P0, gs = shape
     wl = synth.Workload(95, "ws", 7, 2 * H0, H0, d0, P0, 0, False, 0, len_min=48, len_max=131,
                         shared_prefix=32, chunk=9)
     a = synth.host_agentic(wl)
     H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
-    say(f"case workspace small agentic: B 7 pages {a.num_pages}")
-    kp, vp = gpu_quantize_nv(nk, a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached)
-    kd, ks, vd, vs = oracle_nv(a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached)
+    say(f"case workspace small agentic: B 7 pages {a.num_pages} gs {gs}")
+    kp, vp = gpu_quantize_nv(nk, a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached, gs)
+    kd, ks, vd, vs = oracle_nv(a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached, gs)
     prefix = a.cached_lens.copy()
     prefix[3] = 0                                         # an empty prefix
     prefix[5] = 17                                        # a ragged partial page
@@ -273,8 +276,10 @@ def test_dequant_workspace_agentic_small(nk, shape):
                                   synth.to_device(a.ws_row_offsets), kws, vws)
     torch.cuda.synchronize()
     fill = int(synth.bf16_tensor_bits(torch.tensor([-7.0], dtype=torch.bfloat16))[0])
-    kref = oatt.dequant_workspace(onv.dequant_cache(kd, ks), a.block_tables, prefix, a.ws_row_offsets, rows, fill)
-    vref = oatt.dequant_workspace(onv.dequant_cache(vd, vs), a.block_tables, prefix, a.ws_row_offsets, rows, fill)
+    kref = oatt.dequant_workspace(onv.dequant_cache(kd, ks, gs), a.block_tables, prefix, a.ws_row_offsets, rows, fill,
+                                  cache_bits=onv.workspace_bits(kd, ks, gs))
+    vref = oatt.dequant_workspace(onv.dequant_cache(vd, vs, gs), a.block_tables, prefix, a.ws_row_offsets, rows, fill,
+                                  cache_bits=onv.workspace_bits(vd, vs, gs))
     assert np.array_equal(synth.bf16_tensor_bits(kws), kref)
     assert np.array_equal(synth.bf16_tensor_bits(vws), vref)
 
@@ -330,11 +335,68 @@ def test_decode_lut_unpack_matches_conversion(nk, shape):
         assert torch.equal(outs[0], outs[1]), "LUT unpack changed the result"
 
 
-def test_decode_global_scale_power_of_two(nk):
+@pytest.mark.parametrize("gs", [2.0, GS_THIRD])
+def test_decode_global_scale(nk, gs):
     wl = synth.Workload(92, "gs", 2, 8, 2, 128, 16, 300, True, 2)
     inp = synth.host_uniform_decode(wl)
-    say("case decode global scale 2.0")
-    decode_problem(nk, inp, splits_list=(2,), variants=(None,), gs=2.0, label="gs2")
+    say(f"case decode global scale {gs}")
+    decode_problem(nk, inp, splits_list=(2,), variants=(None,), gs=gs, label=f"gs{gs:.4g}")
+
+
+@pytest.mark.parametrize("mag", [3.0e4, 1.0e-5])
+def test_calibrated_global_scale_end_to_end(nk, mag):
+    """Calibration on the GPU: the absmax kernel folds two chunks (one with a
+    strided source and a NaN, which is ignored) into a running maximum; the
+    global scale derived from it keeps a tensor far outside the E4M3 range
+    quantizable; bytes bit-exact against the oracle's FP32 recipe, decode
+    within tolerance."""
+    wl = synth.Workload(96, "calibrated", 2, 8, 2, 128, 16, 200, False, 3)
+    inp = synth.host_uniform_decode(wl)
+    scale = lambda b: synth.f32_to_bf16_bits((synth.bf16_bits_to_f64(b) * mag).astype(np.float32))
+    k_bits, v_bits = scale(inp.k), scale(inp.v)
+    say(f"case calibrated global scale: magnitude {mag}")
+    amax = torch.zeros(2, dtype=torch.float32, device="cuda")
+    refs = []
+    for i, x in enumerate((k_bits, v_bits)):
+        half = x.shape[0] // 2
+        wide = np.zeros((half, x.shape[1] * 3, x.shape[2]), np.uint16)     # fused-QKV-like stride
+        wide[:, :x.shape[1]] = x[:half]
+        wide[0, x.shape[1] + 1, 5] = 0x7FC0                              # NaN outside the K/V heads: not read
+        t = synth.to_device_bf16(wide)[:, :x.shape[1]]
+        rest = x[half:].copy()
+        rest[3, 0, 7] = 0x7FC0                                           # NaN inside: ignored
+        nk.nvfp4_kv_absmax(t, amax[i:i + 1])
+        nk.nvfp4_kv_absmax(synth.to_device_bf16(rest), amax[i:i + 1])
+        refs.append(max(np.abs(synth.bf16_bits_to_f64(x[:half])).max(), np.nanmax(np.abs(synth.bf16_bits_to_f64(rest)))))
+    torch.cuda.synchronize()
+    got = amax.cpu().numpy()
+    for i in range(2):
+        assert got[i] == np.float32(refs[i]), (got[i], refs[i])
+    gk, gv = nk.nvfp4_global_scale_from_absmax(got[0]), nk.nvfp4_global_scale_from_absmax(got[1])
+    assert gk == float(np.float32(got[0]) / np.float32(2688.0))
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    kp = nk.NVFP4Pool.empty(inp.num_pages, H, P, d, global_scale=gk)
+    vp = nk.NVFP4Pool.empty(inp.num_pages, H, P, d, global_scale=gv)
+    for t in (kp.data, kp.scale, vp.data, vp.scale):
+        t.fill_(SENT)
+    nk.nvfp4_kv_quantize(synth.to_device_bf16(k_bits), synth.to_device_bf16(v_bits), synth.to_device(inp.slot_mapping),
+                         kp, vp)
+    kd, ks = onv.empty_cache(inp.num_pages, H, P, d, fill=SENT)
+    vd, vs = onv.empty_cache(inp.num_pages, H, P, d, fill=SENT)
+    onv.write_cache(kd, ks, k_bits, inp.slot_mapping, gk)
+    onv.write_cache(vd, vs, v_bits, inp.slot_mapping, gv)
+    torch.cuda.synchronize()
+    assert_pool_equal(kp.data, kd, "calibrated K data")
+    assert_pool_equal(kp.scale, ks, "calibrated K scale")
+    assert_pool_equal(vp.data, vd, "calibrated V data")
+    assert_pool_equal(vp.scale, vs, "calibrated V scale")
+    q = synth.to_device_bf16(inp.q)
+    out = nk.nvfp4_paged_decode_attn(q, kp, vp, synth.to_device(inp.block_tables), synth.to_device(inp.seq_lens),
+                                     wl.sm_scale, num_splits=3)
+    torch.cuda.synchronize()
+    ref, mass = oatt.paged_decode(inp.q, onv.dequant_cache(kd, ks, gk), onv.dequant_cache(vd, vs, gv),
+                                  inp.block_tables, inp.seq_lens, wl.sm_scale)
+    check_out(out, ref, mass, f"calibrated x{mag}")
 
 
 def test_decode_invariants(nk):

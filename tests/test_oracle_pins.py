@@ -382,3 +382,81 @@ def test_workspace_is_exact_bf16_of_dequantized_prefix():
     # every E2M1 * E4M3 product is exact in bf16
     prod = np.outer(formats.E2M1_VALUES, formats.E4M3_VALUES[:127]).reshape(-1)
     attention.f64_to_bf16_exact(prod)
+
+
+# ---------------------------------------------------------------------------
+# calibrated global scale: the FP32 recipe
+# ---------------------------------------------------------------------------
+
+def _test_blocks(rng, n=4000):
+    """bf16-valued blocks over many magnitudes, plus blocks built from exact midpoints."""
+    mags = 2.0 ** rng.integers(-12, 14, size=(n, 1))
+    x = (rng.standard_normal((n, 16)) * mags).astype(np.float32)
+    x = nvfp4.bf16_to_f64(nvfp4.f32_to_bf16_rne(x))
+    ties = np.array([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75, -1.75, -3.5, 0.0, 6.0, 3.0, 2.0, 1.0])
+    return np.concatenate([x, ties[None, :] * 2.0 ** np.arange(-6, 7)[:, None]])
+
+
+@pytest.mark.parametrize("gs", [1.0, 2.0, 0.5, 2.0 ** -8, 2.0 ** 6])
+def test_fp32_recipe_is_the_exact_encode_at_power_of_two_scales(gs):
+    """Two formulations: FP32 threshold compares vs division and nearest-even
+    rounding in float64. At a power-of-two gs they must agree everywhere."""
+    x = _test_blocks(np.random.default_rng(31))
+    c1, s1 = nvfp4.encode_blocks(x, gs)
+    c2, s2 = nvfp4.encode_blocks_fp32(x, gs)
+    assert np.array_equal(s1, s2) and np.array_equal(c1, c2)
+
+
+@pytest.mark.parametrize("gs", [float(np.float32(1.0 / 3.0)), float(np.float32(0.1))])
+def test_fp32_recipe_differs_from_real_arithmetic_only_at_rounding_boundaries(gs):
+    """At a calibrated (non-power-of-two) gs the FP32 recipe rounds 6*gs, the
+    scale quotient, S*gs and the thresholds. Wherever it disagrees with the
+    real-number encode, the real quantity must sit within a few FP32 ulps of
+    the boundary that decided it; anything else would be an arithmetic slip."""
+    rng = np.random.default_rng(32)
+    x = _test_blocks(rng, 20000)
+    c_real, s_real = nvfp4.encode_blocks(x, gs)
+    c_f32, s_f32 = nvfp4.encode_blocks_fp32(x, gs)
+    # block scales: a disagreement means amax / (6 gs) is within 4 ulps of an E4M3 rounding boundary
+    bad_s = np.nonzero(s_real != s_f32)[0]
+    grid = formats.E4M3_VALUES[:127]
+    mids = (grid[1:] + grid[:-1]) / 2
+    for i in bad_s:
+        q = np.abs(x[i]).max() / (6.0 * gs)
+        dist = np.min(np.abs(mids - q))
+        assert dist <= 4 * np.spacing(np.float32(q)), (i, q, dist)
+    # element codes (same scale byte): a disagreement means |x| is within 4 ulps of a midpoint m * S * gs
+    same = s_real == s_f32
+    diff = np.argwhere((c_real != c_f32) & same[:, None])
+    for i, e in diff:
+        s = formats.E4M3_VALUES[s_real[i]] * gs
+        a = abs(x[i, e])
+        dist = min(abs(a - m * s) for m, _ in nvfp4.MIDPOINTS)
+        assert dist <= 4 * np.spacing(np.float32(a)), (i, e, a, dist)
+    assert 0 < len(bad_s) + len(diff) < 0.01 * x.size     # the rounding does matter, and only rarely
+
+
+def test_calibrated_global_scale_recovers_the_dynamic_range():
+    """The accuracy lever of the tensor scale: with gs = 1 a tensor whose
+    blocks exceed 448 * 6 saturates and one below the E4M3 range flushes to
+    zero; gs = amax / 2688 brings both back to NVFP4's ordinary error."""
+    rng = np.random.default_rng(33)
+    for mag in (3.0e4, 1.0e-5):
+        x = rng.standard_normal((512, 16)) * mag
+        x = nvfp4.bf16_to_f64(nvfp4.f32_to_bf16_rne(x.astype(np.float32)))
+        gs_cal = float(np.float32(np.abs(x).max()) / np.float32(2688.0))
+        errs = {}
+        for gs in (1.0, gs_cal):
+            c, s = (nvfp4.encode_blocks if gs == 1.0 else nvfp4.encode_blocks_fp32)(x, gs)
+            xh = formats.E2M1_VALUES[c.astype(np.int64)] * (formats.E4M3_VALUES[s] * gs)[:, None]
+            errs[gs] = np.sqrt(np.mean((xh - x) ** 2) / np.mean(x ** 2))
+        assert errs[1.0] > 0.5, errs          # saturated or flushed
+        assert errs[gs_cal] < 0.15, errs      # NVFP4's usual relative error
+
+
+def test_workspace_bits_are_exact_at_power_of_two_scales():
+    rng = np.random.default_rng(34)
+    xb = nvfp4.f32_to_bf16_rne(rng.standard_normal((64, 2, 128)).astype(np.float32) * 3)
+    for gs in (1.0, 0.25, 8.0):
+        d, s = nvfp4.quantize_rows(xb, gs)
+        assert np.array_equal(nvfp4.workspace_bits(d, s, gs), attention.f64_to_bf16_exact(nvfp4.dequant_rows(d, s, gs)))
