@@ -206,26 +206,10 @@ def decode_figures(nk, variant, steps, warmup, measured):
     return out
 
 
-def agentic(nk, wl, steps, warmup):
-    """The prefix-reuse step (quantize the new chunk, dequantize every cached
-    prefix into the workspace, decode all sequences): whole-step time and
-    each kernel's mean duration from HIP events on the launch stream."""
+def time_calls(calls, steps, warmup):
+    """Whole-sequence time of `calls` per step (wall clock, synchronised) and each
+    call's mean duration from HIP events on the launch stream."""
     import torch
-    from synth.workload import agentic_bytes, build_agentic_workload
-    t = time.time()
-    w = build_agentic_workload(nk, wl)
-    log(f"[bench] built agentic workload in {time.time() - t:.1f}s")
-    B, Hq, d = wl.batch, wl.num_q_heads, wl.head_dim
-    S = nk.nvfp4_paged_decode_num_splits(B, wl.num_kv_heads, w.bt.shape[1], wl.page_size)
-    ws = nk.decode_workspace(B, Hq, d, S)
-    out = torch.empty_like(w.q)
-    calls = [
-        ("quantize", lambda: nk.nvfp4_kv_quantize(w.k_chunk, w.v_chunk, w.slot_chunk, w.kp, w.vp)),
-        ("dequant_workspace", lambda: nk.nvfp4_kv_dequant_workspace(w.kp, w.vp, w.bt, w.cached_lens,
-                                                                    w.ws_row_offsets, w.k_ws, w.v_ws)),
-        ("decode", lambda: nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale,
-                                                      num_splits=S, workspace=ws, out=out)),
-    ]
     ramp(lambda: [f() for _, f in calls], seconds=0.2)
     for _ in range(warmup):
         for _, f in calls:
@@ -247,6 +231,35 @@ def agentic(nk, wl, steps, warmup):
             b.record(stream)
         torch.cuda.synchronize()
         per[name] = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+    return t_step, per
+
+
+def agentic(nk, wl, steps, warmup):
+    """The prefix-reuse step (quantize the new chunk, dequantize every cached
+    prefix into the workspace, decode all sequences): whole-step time and
+    each kernel's mean duration from HIP events on the launch stream. Run
+    twice: with bf16 chunk and workspace (the workload definition) and with
+    the pages' FP8 types (FP8 chunk quantized to NVFP4 and copied into an FP8
+    workspace in one pass, FP8 workspace)."""
+    import numpy as np
+    import torch
+    from synth.workload import agentic_bytes, build_agentic_workload
+    t = time.time()
+    w = build_agentic_workload(nk, wl)
+    log(f"[bench] built agentic workload in {time.time() - t:.1f}s")
+    B, Hq, d, H, C = wl.batch, wl.num_q_heads, wl.head_dim, wl.num_kv_heads, wl.chunk
+    S = nk.nvfp4_paged_decode_num_splits(B, H, w.bt.shape[1], wl.page_size)
+    ws = nk.decode_workspace(B, Hq, d, S)
+    out = torch.empty_like(w.q)
+    decode = ("decode", lambda: nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale,
+                                                           num_splits=S, workspace=ws, out=out))
+    calls = [
+        ("quantize", lambda: nk.nvfp4_kv_quantize(w.k_chunk, w.v_chunk, w.slot_chunk, w.kp, w.vp)),
+        ("dequant_workspace", lambda: nk.nvfp4_kv_dequant_workspace(w.kp, w.vp, w.bt, w.cached_lens,
+                                                                    w.ws_row_offsets, w.k_ws, w.v_ws)),
+        decode,
+    ]
+    t_step, per = time_calls(calls, steps, warmup)
     by = agentic_bytes(w)
     res = {
         "ms_per_step": round(t_step * 1e3, 4), "steps_per_s": round(1.0 / t_step, 2), "num_splits": S,
@@ -261,7 +274,42 @@ def agentic(nk, wl, steps, warmup):
                    "kv_gbs_unique": round(by["decode_read_unique"] / per["decode"] / 1e9, 1)},
         "bytes": by,
     }
+    log(f"[bench] agentic step {t_step * 1e3:.3f} ms: " + ", ".join(f"{k} {v * 1e3:.3f} ms" for k, v in per.items()))
+
+    # the pages' path-2 types: FP8 chunk and FP8 workspace
+    k8 = w.k_chunk.to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = w.v_chunk.to(torch.float8_e4m3fn).view(torch.uint8)
+    rows = int(w.ws_row_offsets[-1].item())
+    kws8 = torch.empty((rows, H, d), dtype=torch.uint8, device="cuda")
+    vws8 = torch.empty((rows, H, d), dtype=torch.uint8, device="cuda")
+    offs = w.ws_row_offsets.cpu().numpy()
+    chunk_rows = np.concatenate([offs[b] + w.host_cached_lens[b] + np.arange(C) for b in range(B)]).astype(np.int64)
+    ws_rows = torch.from_numpy(chunk_rows).cuda()
+    calls8 = [
+        ("quantize", lambda: nk.nvfp4_kv_quantize_fp8(k8, v8, w.slot_chunk, w.kp, w.vp, 1.0, 1.0, ws_rows, kws8, vws8)),
+        ("dequant_workspace", lambda: nk.nvfp4_kv_dequant_workspace_fp8(w.kp, w.vp, w.bt, w.cached_lens,
+                                                                        w.ws_row_offsets, kws8, vws8)),
+        decode,
+    ]
+    t8, per8 = time_calls(calls8, steps, warmup)
+    q_rd = by["quant_read"] // 2                        # FP8 chunk: one byte per element
+    q_wr = by["quant_write"] + q_rd                     # NVFP4 + the chunk copied into the workspace
+    dq_wr = by["dequant_write"] // 2
+    res["fp8_path2"] = {
+        "ms_per_step": round(t8 * 1e3, 4), "steps_per_s": round(1.0 / t8, 2),
+        "quantize_with_chunk_copy": {"ms": round(per8["quantize"] * 1e3, 4),
+                                     "gbs": round((q_rd + q_wr) / per8["quantize"] / 1e9, 1)},
+        "dequant_workspace_fp8": {"ms": round(per8["dequant_workspace"] * 1e3, 4),
+                                  "gbs_unique": round((by["dequant_read_unique"] + dq_wr)
+                                                      / per8["dequant_workspace"] / 1e9, 1),
+                                  "write_gbs": round(dq_wr / per8["dequant_workspace"] / 1e9, 1)},
+        "decode": {"ms": round(per8["decode"] * 1e3, 4)},
+    }
+    log(f"[bench] agentic fp8 path-2 step {t8 * 1e3:.3f} ms: "
+        + ", ".join(f"{k} {v * 1e3:.3f} ms" for k, v in per8.items()))
+
     # global-scale calibration of the chunk (absmax of K and V), not part of the step
+    stream = torch.cuda.current_stream()
     amax = torch.zeros(2, dtype=torch.float32, device="cuda")
     cal = lambda: (nk.nvfp4_kv_absmax(w.k_chunk, amax[0:1]), nk.nvfp4_kv_absmax(w.v_chunk, amax[1:2]))
     for _ in range(warmup):
@@ -274,9 +322,8 @@ def agentic(nk, wl, steps, warmup):
     torch.cuda.synchronize()
     t_cal = e0.elapsed_time(e1) / steps / 1e3
     res["absmax_calibration"] = {"ms": round(t_cal * 1e3, 4), "gbs": round(by["quant_read"] / t_cal / 1e9, 1)}
-    log(f"[bench] agentic step {t_step * 1e3:.3f} ms: " + ", ".join(f"{k} {v * 1e3:.3f} ms" for k, v in per.items())
-        + f"; absmax calibration {t_cal * 1e3:.3f} ms")
-    del w, ws, out
+    log(f"[bench] absmax calibration {t_cal * 1e3:.3f} ms")
+    del w, ws, out, kws8, vws8
     torch.cuda.empty_cache()
     return res
 

@@ -133,6 +133,30 @@ int nvfp4_kv_quantize(const nvfp4kv_geom* geom, const void* k, const void* v,
                       const nvfp4kv_cache* v_cache, void* stream);
 
 /*
+ * nvfp4_kv_quantize_fp8 -- quantize-on-write from FP8-E4M3 K/V, the source
+ * type of the pages' paths 1 and 2 (section A2: the projected K/V are FP8 and
+ * are quantized from FP8 to NVFP4 into the pool), with the current chunk
+ * optionally copied into an FP8 workspace in the same pass (path 2: the
+ * chunk's K/V sit next to the dequantized prefix).
+ *
+ *   k, v          device FP8-E4M3 bytes; element (t, h, c) at [t * src_token_stride + h * d + c]
+ *   src_token_stride  bytes between tokens (>= Hkv * d, multiple of 16)
+ *   k_src_scale, v_src_scale  FP32 per-tensor scales of the sources (> 0):
+ *                 element value = fl32(e4m3(byte) * src_scale)
+ *   slot_mapping, k_cache, v_cache  as nvfp4_kv_quantize; the encode is the
+ *                 same (FP32 recipe) applied to the element values
+ *   ws_rows       NULL, or device int64 [T]: token t's source bytes are also
+ *                 copied unchanged to row ws_rows[t] of k_ws / v_ws
+ *                 ([rows][Hkv][d] bytes, 16-byte aligned); rows < 0 are not copied
+ * FP8 NaN bytes in the source are outside the contract.
+ */
+int nvfp4_kv_quantize_fp8(const nvfp4kv_geom* geom, const void* k, const void* v,
+                          int64_t src_token_stride, int32_t num_tokens, const int64_t* slot_mapping,
+                          float k_src_scale, float v_src_scale, const nvfp4kv_cache* k_cache,
+                          const nvfp4kv_cache* v_cache, const int64_t* ws_rows, void* k_ws, void* v_ws,
+                          void* stream);
+
+/*
  * nvfp4_kv_dequant_workspace -- gather and dequantize cached prefixes into a
  * bf16 workspace for extend / chunked-prefill attention (section A2, path 2).
  *
@@ -152,6 +176,22 @@ int nvfp4_kv_dequant_workspace(const nvfp4kv_geom* geom, const nvfp4kv_cache* k_
                                int32_t max_pages_per_seq, const int32_t* prefix_lens,
                                const int64_t* ws_row_offsets, int32_t batch, void* k_ws,
                                void* v_ws, void* stream);
+
+/*
+ * nvfp4_kv_dequant_workspace_fp8 -- the same gather into the pages' FP8-E4M3
+ * workspace (section A2, path 2: a preallocated FP8 workspace shared across
+ * layers). Arguments as nvfp4_kv_dequant_workspace, plus
+ *   k_ws_scale, v_ws_scale  FP32 per-tensor scales of the workspaces (> 0)
+ *   k_ws, v_ws      device bytes [ws_row_offsets[batch]][Hkv][d]
+ * Element byte = E4M3(fl32(fl32(e2m1 * fl32(S * global_scale)) / ws_scale)),
+ * nearest even, saturating at +-448, sign kept. Lossy: 275 of the 1016
+ * products e2m1 * S (gs = ws_scale = 1) are not E4M3 values.
+ */
+int nvfp4_kv_dequant_workspace_fp8(const nvfp4kv_geom* geom, const nvfp4kv_cache* k_cache,
+                                   const nvfp4kv_cache* v_cache, const int32_t* block_tables,
+                                   int32_t max_pages_per_seq, const int32_t* prefix_lens,
+                                   const int64_t* ws_row_offsets, int32_t batch, float k_ws_scale,
+                                   float v_ws_scale, void* k_ws, void* v_ws, void* stream);
 
 /*
  * Split-KV decode. Each (sequence b, KV head g, split j) item attends the G =

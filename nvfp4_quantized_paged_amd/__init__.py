@@ -62,6 +62,10 @@ _SIGNATURES = {
                                                 c_f32, c_i32, c_i32, c_vp, c_size, c_vp]),
     "nvfp4kv_lse_merge": (ctypes.c_int, [c_vp, c_size, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_vp]),
     "nvfp4_kv_absmax": (ctypes.c_int, [c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "nvfp4_kv_quantize_fp8": (ctypes.c_int, [P_GEOM, c_vp, c_vp, c_i64, c_i32, c_vp, c_f32, c_f32, P_NV, P_NV,
+                                             c_vp, c_vp, c_vp, c_vp]),
+    "nvfp4_kv_dequant_workspace_fp8": (ctypes.c_int, [P_GEOM, P_NV, P_NV, c_vp, c_i32, c_vp, c_vp, c_i32,
+                                                      c_f32, c_f32, c_vp, c_vp, c_vp]),
     "nvfp4_global_scale_from_absmax": (c_f32, [c_f32]),
 }
 
@@ -225,6 +229,45 @@ def nvfp4_kv_absmax(x, amax, stream=None):
 def nvfp4_global_scale_from_absmax(amax: float) -> float:
     """amax / (448 * 6) in FP32 (1.0 for amax 0, negative or non-finite)."""
     return float(lib().nvfp4_global_scale_from_absmax(float(amax)))
+
+
+def nvfp4_kv_quantize_fp8(k, v, slot_mapping, k_pool: NVFP4Pool, v_pool: NVFP4Pool, k_src_scale=1.0,
+                          v_src_scale=1.0, ws_rows=None, k_ws=None, v_ws=None, stream=None):
+    """Quantize-on-write from FP8-E4M3 k, v [T][Hkv][d] (uint8 bytes) into the NVFP4 pools; with ws_rows
+    ([T] int64) the source bytes are also copied to those rows of k_ws, v_ws ([rows][Hkv][d] uint8)."""
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 3:
+            raise TypeError(f"{name} must be a uint8 (FP8-E4M3) device tensor [T][Hkv][d]")
+        if t.shape[0] > 0 and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
+            raise ValueError(f"{name} must be [T][Hkv][d] with dense heads")
+    g = k_pool.geom
+    if k.shape[0] > 0 and k.stride(0) != v.stride(0):
+        raise ValueError("k and v must share a token stride")
+    stride = k.stride(0) if k.shape[0] > 0 else g.num_kv_heads * g.head_dim
+    if ws_rows is not None:
+        _need(ws_rows, torch.int64, "ws_rows")
+        _need(k_ws, torch.uint8, "k_ws")
+        _need(v_ws, torch.uint8, "v_ws")
+    _check(lib().nvfp4_kv_quantize_fp8(
+        ctypes.byref(g), k.data_ptr(), v.data_ptr(), stride, k.shape[0], slot_mapping.data_ptr(),
+        float(k_src_scale), float(v_src_scale), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()),
+        _ptr(ws_rows), _ptr(k_ws), _ptr(v_ws), _stream(stream)))
+
+
+def nvfp4_kv_dequant_workspace_fp8(k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables, prefix_lens,
+                                   ws_row_offsets, k_ws, v_ws, k_ws_scale=1.0, v_ws_scale=1.0, stream=None):
+    """As nvfp4_kv_dequant_workspace, into FP8-E4M3 workspaces ([rows][Hkv][d] uint8)."""
+    _need(block_tables, torch.int32, "block_tables")
+    _need(prefix_lens, torch.int32, "prefix_lens")
+    _need(ws_row_offsets, torch.int64, "ws_row_offsets")
+    _need(k_ws, torch.uint8, "k_ws")
+    _need(v_ws, torch.uint8, "v_ws")
+    g = k_pool.geom
+    _check(lib().nvfp4_kv_dequant_workspace_fp8(
+        ctypes.byref(g), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()), block_tables.data_ptr(),
+        block_tables.shape[1], prefix_lens.data_ptr(), ws_row_offsets.data_ptr(), prefix_lens.shape[0],
+        float(k_ws_scale), float(v_ws_scale), k_ws.data_ptr(), v_ws.data_ptr(), _stream(stream)))
 
 
 def nvfp4_kv_dequant_workspace(k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables, prefix_lens,

@@ -270,6 +270,51 @@ NVFP4KV_API int nvfp4_kv_quantize(const nvfp4kv_geom* geom, const void* k, const
   return launched(launch_nvfp4_quantize(p, static_cast<hipStream_t>(stream)), fn);
 }
 
+NVFP4KV_API int nvfp4_kv_quantize_fp8(const nvfp4kv_geom* geom, const void* k, const void* v,
+                                      int64_t src_token_stride, int32_t num_tokens, const int64_t* slot_mapping,
+                                      float k_src_scale, float v_src_scale, const nvfp4kv_cache* k_cache,
+                                      const nvfp4kv_cache* v_cache, const int64_t* ws_rows, void* k_ws, void* v_ws,
+                                      void* stream) {
+  const char* fn = "nvfp4_kv_quantize_fp8";
+  int rc;
+  if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
+      (rc = check_nvfp4_cache(v_cache, "V", fn)) ||
+      (rc = check_quantize_src(geom, k, v, src_token_stride, num_tokens, slot_mapping, fn)))
+    return rc;
+  if (!(isfinite(k_src_scale) && k_src_scale > 0.0f && isfinite(v_src_scale) && v_src_scale > 0.0f))
+    return fail(NVFP4KV_EINVAL, "%s: source scales must be finite and > 0", fn);
+  if (num_tokens == 0) return launched(hipSuccess, fn);
+  if (src_token_stride % 16 != 0)
+    return fail(NVFP4KV_EALIGN, "%s: src_token_stride must be a multiple of 16 (bytes of FP8)", fn);
+  if (ws_rows && (!k_ws || !v_ws)) return fail(NVFP4KV_EINVAL, "%s: ws_rows given without k_ws and v_ws", fn);
+  if (ws_rows && (!aligned16(k_ws) || !aligned16(v_ws)))
+    return fail(NVFP4KV_EALIGN, "%s: workspaces must be 16-byte aligned", fn);
+  QuantizeParams p{};
+  p.src[0] = k;
+  p.src[1] = v;
+  p.src_stride = src_token_stride;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = geom->num_kv_heads;
+  p.head_dim = geom->head_dim;
+  p.page_size = geom->page_size;
+  p.num_slots = (int64_t)geom->num_pages * geom->page_size;
+  p.page_shift = page_shift(geom->page_size);
+  p.data[0] = k_cache->data;
+  p.data[1] = v_cache->data;
+  p.scale[0] = k_cache->scale;
+  p.scale[1] = v_cache->scale;
+  p.gscale[0] = k_cache->global_scale;
+  p.gscale[1] = v_cache->global_scale;
+  p.src_fp8 = 1;
+  p.src_scale[0] = k_src_scale;
+  p.src_scale[1] = v_src_scale;
+  p.ws_rows = ws_rows;
+  p.ws[0] = static_cast<uint8_t*>(k_ws);
+  p.ws[1] = static_cast<uint8_t*>(v_ws);
+  return launched(launch_nvfp4_quantize(p, static_cast<hipStream_t>(stream)), fn);
+}
+
 NVFP4KV_API int fp8_kv_quantize(const nvfp4kv_geom* geom, const void* k, const void* v,
                                 int64_t src_token_stride, int32_t num_tokens,
                                 const int64_t* slot_mapping, const fp8kv_cache* k_cache,
@@ -299,17 +344,17 @@ NVFP4KV_API int fp8_kv_quantize(const nvfp4kv_geom* geom, const void* k, const v
   return launched(launch_fp8_quantize(p, static_cast<hipStream_t>(stream)), fn);
 }
 
-NVFP4KV_API int nvfp4_kv_dequant_workspace(const nvfp4kv_geom* geom, const nvfp4kv_cache* k_cache,
-                                           const nvfp4kv_cache* v_cache, const int32_t* block_tables,
-                                           int32_t max_pages_per_seq, const int32_t* prefix_lens,
-                                           const int64_t* ws_row_offsets, int32_t batch, void* k_ws,
-                                           void* v_ws, void* stream) {
-  const char* fn = "nvfp4_kv_dequant_workspace";
+int dequant_workspace(const char* fn, const nvfp4kv_geom* geom, const nvfp4kv_cache* k_cache,
+                      const nvfp4kv_cache* v_cache, const int32_t* block_tables, int32_t max_pages_per_seq,
+                      const int32_t* prefix_lens, const int64_t* ws_row_offsets, int32_t batch, bool fp8_out,
+                      float k_ws_scale, float v_ws_scale, void* k_ws, void* v_ws, void* stream) {
   int rc;
   if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
       (rc = check_nvfp4_cache(v_cache, "V", fn)))
     return rc;
   if (batch < 0 || batch > kGridYZ) return fail(NVFP4KV_EINVAL, "%s: batch %d out of range [0, %d]", fn, batch, kGridYZ);
+  if (!(isfinite(k_ws_scale) && k_ws_scale > 0.0f && isfinite(v_ws_scale) && v_ws_scale > 0.0f))
+    return fail(NVFP4KV_EINVAL, "%s: workspace scales must be finite and > 0", fn);
   if (batch == 0) return launched(hipSuccess, fn);
   if (!block_tables || !prefix_lens || !ws_row_offsets || !k_ws || !v_ws)
     return fail(NVFP4KV_EINVAL, "%s: block_tables, prefix_lens, ws_row_offsets, k_ws and v_ws must be non-NULL", fn);
@@ -331,9 +376,31 @@ NVFP4KV_API int nvfp4_kv_dequant_workspace(const nvfp4kv_geom* geom, const nvfp4
   p.head_dim = geom->head_dim;
   p.page_size = geom->page_size;
   p.num_pages = geom->num_pages;
-  p.ws[0] = static_cast<uint16_t*>(k_ws);
-  p.ws[1] = static_cast<uint16_t*>(v_ws);
+  p.ws[0] = k_ws;
+  p.ws[1] = v_ws;
+  p.out_fp8 = fp8_out ? 1 : 0;
+  p.ws_scale[0] = k_ws_scale;
+  p.ws_scale[1] = v_ws_scale;
   return launched(launch_nvfp4_dequant_ws(p, static_cast<hipStream_t>(stream)), fn);
+}
+
+NVFP4KV_API int nvfp4_kv_dequant_workspace(const nvfp4kv_geom* geom, const nvfp4kv_cache* k_cache,
+                                           const nvfp4kv_cache* v_cache, const int32_t* block_tables,
+                                           int32_t max_pages_per_seq, const int32_t* prefix_lens,
+                                           const int64_t* ws_row_offsets, int32_t batch, void* k_ws,
+                                           void* v_ws, void* stream) {
+  return dequant_workspace("nvfp4_kv_dequant_workspace", geom, k_cache, v_cache, block_tables, max_pages_per_seq,
+                           prefix_lens, ws_row_offsets, batch, false, 1.0f, 1.0f, k_ws, v_ws, stream);
+}
+
+NVFP4KV_API int nvfp4_kv_dequant_workspace_fp8(const nvfp4kv_geom* geom, const nvfp4kv_cache* k_cache,
+                                               const nvfp4kv_cache* v_cache, const int32_t* block_tables,
+                                               int32_t max_pages_per_seq, const int32_t* prefix_lens,
+                                               const int64_t* ws_row_offsets, int32_t batch, float k_ws_scale,
+                                               float v_ws_scale, void* k_ws, void* v_ws, void* stream) {
+  return dequant_workspace("nvfp4_kv_dequant_workspace_fp8", geom, k_cache, v_cache, block_tables,
+                           max_pages_per_seq, prefix_lens, ws_row_offsets, batch, true, k_ws_scale, v_ws_scale,
+                           k_ws, v_ws, stream);
 }
 
 NVFP4KV_API int nvfp4_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,

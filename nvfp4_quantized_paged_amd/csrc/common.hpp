@@ -82,6 +82,18 @@ __device__ inline void fp8x4_to_f32(uint32_t w, float out[4]) {
   out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
 }
 
+// Four floats -> four OCP E4M3 bytes (element i in byte i), nearest even,
+// saturating at +-448, sign of zero kept. The conversion instruction rounds to
+// nearest even but turns magnitudes that round past 448 into NaN, so the
+// inputs are clamped first; checked on MI355X against the exact encoder for
+// every finite bf16 value, every E2M1 x E4M3 product and 1M random floats.
+__device__ inline uint32_t f32x4_to_fp8(float a, float b, float c, float d) {
+  const auto clamp = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(a), clamp(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(c), clamp(d), w, true);
+  return (uint32_t)w;
+}
+
 // ---------------------------------------------------------------------------
 // wave64 reductions
 // ---------------------------------------------------------------------------
@@ -102,7 +114,7 @@ __device__ inline float wave_sum(float v) {
 // ---------------------------------------------------------------------------
 
 struct QuantizeParams {
-  const uint16_t* src[2];   // K, V (bf16)
+  const void* src[2];       // K, V: bf16, or FP8-E4M3 bytes (src_fp8)
   int64_t src_stride;       // elements between tokens
   const int64_t* slot_mapping;
   int32_t num_tokens, num_kv_heads, head_dim, page_size;
@@ -111,6 +123,10 @@ struct QuantizeParams {
   uint8_t* data[2];         // NVFP4 data or FP8 bytes
   uint8_t* scale[2];        // NVFP4 block scales (unused for FP8)
   float gscale[2];          // NVFP4 global scale / FP8 per-tensor scale
+  int32_t src_fp8;          // source elements are FP8-E4M3 bytes, value = e4m3 * src_scale
+  float src_scale[2];
+  const int64_t* ws_rows;   // optional: workspace row of each token (< 0: not copied)
+  uint8_t* ws[2];           // workspace [rows][Hkv][head_dim] of source elements, copied unchanged
 };
 
 struct WorkspaceParams {
@@ -122,7 +138,9 @@ struct WorkspaceParams {
   const int64_t* row_offsets;
   int32_t max_pages, batch, num_kv_heads, head_dim, page_size;
   int32_t num_pages;        // page indices are clamped into [0, num_pages)
-  uint16_t* ws[2];
+  void* ws[2];              // bf16, or FP8-E4M3 bytes (out_fp8)
+  int32_t out_fp8;          // FP8 workspace: byte = E4M3(value / ws_scale), nearest even, saturating
+  float ws_scale[2];
 };
 
 struct DecodeParams {

@@ -1,12 +1,12 @@
-// Dequantize cached prefixes into a bf16 workspace (extend / chunked-prefill
-// path).
+// Dequantize cached prefixes into a workspace (extend / chunked-prefill path).
 //
 // "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
 // section A2, path 2: the scattered NVFP4 entries of the cached prefix are
 // gathered through the page table, dequantized and written into a workspace
 // that is shared by all layers; the current chunk's K/V occupy the rows after
-// the prefix. The pages use an FP8 workspace; this library writes bf16, in
-// which every E2M1 x E4M3 product is exact.
+// the prefix. Two workspace types: bf16, in which every E2M1 x E4M3 product
+// (times a power-of-two global scale) is exact, and the pages' FP8-E4M3, which
+// rounds some of them (nearest even, saturating) and halves the bytes written.
 //
 // The kernel is write-bound: per 8 channels it reads 4 bytes (plus a shared
 // scale byte) and writes 16 bytes, for each of K and V. Grid: (row groups,
@@ -30,6 +30,9 @@ constexpr int kWsRowsPerWave = 2;    // rows handled by one wave
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool FP8OUT>
 __global__ __launch_bounds__(64 * kWsWaves) void nvfp4_dequant_ws_kernel(WorkspaceParams p) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -73,10 +76,24 @@ __global__ __launch_bounds__(64 * kWsWaves) void nvfp4_dequant_ws_kernel(Workspa
           const float s = e4m3_to_f32(sb[r][which]) * p.gscale[which];
           float f[8];
           fp4x8_to_f32(w[r][which], f);
-          const u32x4 v = {pack_bf16x2(f[0] * s, f[1] * s), pack_bf16x2(f[2] * s, f[3] * s),
-                           pack_bf16x2(f[4] * s, f[5] * s), pack_bf16x2(f[6] * s, f[7] * s)};
-          __builtin_nontemporal_store(
-              v, reinterpret_cast<u32x4*>(p.ws[which] + dst_row + h * p.head_dim + blk * kBlock + half * 8));
+          const int64_t e0 = dst_row + h * p.head_dim + blk * kBlock + half * 8;   // first element
+          if constexpr (FP8OUT) {
+            // FP8 workspace (the pages' type): byte = E4M3(fl32(e2m1 * S * gs) / ws_scale); lossy
+            const float ws = p.ws_scale[which];
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = f[e] * s;
+            if (ws != 1.0f) {      // correctly rounded division only where the scale needs it
+#pragma unroll
+              for (int e = 0; e < 8; ++e) y[e] = y[e] / ws;
+            }
+            const u32x2 v = {f32x4_to_fp8(y[0], y[1], y[2], y[3]), f32x4_to_fp8(y[4], y[5], y[6], y[7])};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.ws[which]) + e0));
+          } else {
+            const u32x4 v = {pack_bf16x2(f[0] * s, f[1] * s), pack_bf16x2(f[2] * s, f[3] * s),
+                             pack_bf16x2(f[4] * s, f[5] * s), pack_bf16x2(f[6] * s, f[7] * s)};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.ws[which]) + e0));
+          }
         }
       }
     }
@@ -89,7 +106,8 @@ hipError_t launch_nvfp4_dequant_ws(const WorkspaceParams& p, hipStream_t s) {
   const int64_t max_rows = (int64_t)p.max_pages * p.page_size;
   const int64_t per_block = (int64_t)kWsWaves * kWsRowsPerWave;
   dim3 grid((unsigned)((max_rows + per_block - 1) / per_block), (unsigned)p.batch);
-  hipLaunchKernelGGL(nvfp4_dequant_ws_kernel, grid, dim3(64 * kWsWaves), 0, s, p);
+  if (p.out_fp8) hipLaunchKernelGGL(nvfp4_dequant_ws_kernel<true>, grid, dim3(64 * kWsWaves), 0, s, p);
+  else hipLaunchKernelGGL(nvfp4_dequant_ws_kernel<false>, grid, dim3(64 * kWsWaves), 0, s, p);
   return hipGetLastError();
 }
 

@@ -64,7 +64,46 @@ __device__ inline void slot_position(const QuantizeParams& p, int64_t slot, int6
 constexpr int kTokPerWave = 16;
 constexpr int kWavesPerGroup = 4;
 
-template <int D>
+// Source block of 16 elements as floats: bf16 (two 128-bit loads) or
+// FP8-E4M3 bytes times the source scale (one 128-bit load). With ws_rows the
+// source bytes also go, unchanged, to the token's workspace row (the current
+// chunk of the extend path next to the dequantized prefix).
+template <int D, bool FP8SRC>
+__device__ inline void load_source_block(const QuantizeParams& p, int which, int64_t t, int h, int blk, float x[16]) {
+  constexpr int kEsize = FP8SRC ? 1 : 2;
+  const int64_t elem = t * p.src_stride + (int64_t)h * D + blk * kBlock;
+  const uint8_t* src = static_cast<const uint8_t*>(p.src[which]) + elem * kEsize;
+  uint4 raw[kEsize];
+#pragma unroll
+  for (int i = 0; i < kEsize; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+  if (p.ws_rows) {
+    const int64_t r = p.ws_rows[t];
+    if (r >= 0) {
+      uint4* dst = reinterpret_cast<uint4*>(p.ws[which] + ((r * p.num_kv_heads + h) * D + blk * kBlock) * kEsize);
+#pragma unroll
+      for (int i = 0; i < kEsize; ++i) dst[i] = raw[i];
+    }
+  }
+  if constexpr (FP8SRC) {
+    const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+    const float ss = p.src_scale[which];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fp8x4_to_f32(w[i], x + 4 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * i + e] *= ss;
+    }
+  } else {
+    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <int D, bool FP8SRC>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void nvfp4_quantize_kernel(QuantizeParams p) {
   constexpr int nb = D / kBlock;                 // blocks per head row
   constexpr int kTokPerPass = 64 / nb;
@@ -75,11 +114,11 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void nvfp4_quantize_kernel(Qua
   for (int k = 0; k < kTokPerWave / kTokPerPass; ++k) {
     const int64_t t = tw + k * kTokPerPass + lane / nb;
     if (t >= p.num_tokens) break;
+    float x[16];
+    load_source_block<D, FP8SRC>(p, which, t, h, blk, x);
     const int64_t slot = p.slot_mapping[t];
     if (slot < 0 || slot >= p.num_slots) continue;
 
-    float x[16];
-    load_block16(p.src[which] + t * p.src_stride + (int64_t)h * D + blk * kBlock, x);
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
@@ -122,7 +161,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void fp8_quantize_kernel(Quant
     if (slot < 0 || slot >= p.num_slots) continue;
 
     float x[16];
-    load_block16(p.src[which] + t * p.src_stride + (int64_t)h * D + blk * kBlock, x);
+    load_block16(static_cast<const uint16_t*>(p.src[which]) + t * p.src_stride + (int64_t)h * D + blk * kBlock, x);
     const float s = p.gscale[which];
     uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -144,8 +183,14 @@ hipError_t launch_nvfp4_quantize(const QuantizeParams& p, hipStream_t s) {
   if (p.num_tokens == 0) return hipSuccess;
   const int64_t per_group = kTokPerWave * kWavesPerGroup;
   const dim3 grid((unsigned)((p.num_tokens + per_group - 1) / per_group), (unsigned)p.num_kv_heads, 2);
-  if (p.head_dim == 64) hipLaunchKernelGGL(nvfp4_quantize_kernel<64>, grid, dim3(64 * kWavesPerGroup), 0, s, p);
-  else hipLaunchKernelGGL(nvfp4_quantize_kernel<128>, grid, dim3(64 * kWavesPerGroup), 0, s, p);
+  const dim3 block(64 * kWavesPerGroup);
+  if (p.head_dim == 64) {
+    if (p.src_fp8) hipLaunchKernelGGL((nvfp4_quantize_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((nvfp4_quantize_kernel<64, false>), grid, block, 0, s, p);
+  } else {
+    if (p.src_fp8) hipLaunchKernelGGL((nvfp4_quantize_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((nvfp4_quantize_kernel<128, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

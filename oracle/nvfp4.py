@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import (E2M1_VALUES, E4M3_VALUES, e2m1_magnitude_code,
+from .formats import (E2M1_VALUES, E4M3_VALUES, e2m1_magnitude_code, e4m3_encode,
                       e4m3_encode_nonneg)
 
 BLOCK = 16
@@ -85,8 +85,8 @@ def encode_blocks_fp32(x: np.ndarray, gs: float):
     """
     x = np.asarray(x, dtype=np.float64)
     assert x.shape[-1] == BLOCK
-    a = np.abs(x).astype(np.float32)                     # exact: bf16 values
-    amax = a.max(axis=-1)
+    a = np.abs(x).astype(np.float32)                     # exact: bf16 or FP32 values
+    amax = np.fmax.reduce(a, axis=-1, initial=np.float32(0.0))   # NaN elements ignored
     g = np.float32(gs)
     s_byte = e4m3_encode_nonneg((amax / (np.float32(6.0) * g)).astype(np.float64))
     s_eff = (E4M3_VALUES[s_byte].astype(np.float32) * g)[..., None]
@@ -115,6 +115,28 @@ def workspace_bits(data: np.ndarray, scale: np.ndarray, gs: float = 1.0) -> np.n
     d = vals.shape[-1]
     prod = vals.reshape(vals.shape[:-1] + (d // BLOCK, BLOCK)) * s[..., None]
     return f32_to_bf16_rne(prod.reshape(vals.shape))
+
+
+def quantize_rows_fp8(x_bytes: np.ndarray, src_scale: float = 1.0, gs: float = 1.0):
+    """Quantize FP8-E4M3 token rows [T][H][d] (bytes) to NVFP4 (the pages' source
+    type, section A2 paths 1-2): element value fl32(e4m3 * src_scale), then the
+    FP32 recipe (for src_scale = 1 and a power-of-two gs every step is exact)."""
+    x = (E4M3_VALUES[np.asarray(x_bytes, dtype=np.int64)].astype(np.float32) * np.float32(src_scale))
+    T, H, d = x.shape
+    codes, s = encode_blocks_fp32(x.astype(np.float64).reshape(T, H, d // BLOCK, BLOCK), gs)
+    return pack_nibbles(codes.reshape(T, H, d)), s.reshape(T, H, d // BLOCK)
+
+
+def workspace_fp8_bytes(data: np.ndarray, scale: np.ndarray, gs: float = 1.0, ws_scale: float = 1.0) -> np.ndarray:
+    """E4M3 bytes of dequantized values in the pages' FP8 workspace (section A2,
+    path 2): E4M3(fl32(fl32(e2m1 * fl32(S * gs)) / ws_scale)), nearest even,
+    saturating at +-448, sign kept. Lossy: some products are not E4M3 values."""
+    codes = unpack_nibbles(data)
+    vals = E2M1_VALUES[codes.astype(np.int64)].astype(np.float32)
+    s = E4M3_VALUES[np.asarray(scale, dtype=np.int64)].astype(np.float32) * np.float32(gs)
+    d = vals.shape[-1]
+    prod = (vals.reshape(vals.shape[:-1] + (d // BLOCK, BLOCK)) * s[..., None]).reshape(vals.shape)
+    return e4m3_encode((prod / np.float32(ws_scale)).astype(np.float64))
 
 
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:

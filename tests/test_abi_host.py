@@ -207,3 +207,34 @@ def test_global_scale_from_absmax(L):
     import numpy as np
     for a in (1.0, 3.14159, 1e-20, 6.5e4, 1e30):
         assert g(a) == float(np.float32(a) / np.float32(2688.0))
+
+
+def test_fp8_path2_entry_points_validate(L):
+    g = _geom(L)
+    kc, vc = _nv(L), _nv(L)
+    q = L.lib().nvfp4_kv_quantize_fp8
+    ok = dict(k=FAKE, v=FAKE, stride=64, T=4, slots=FAKE, ks=1.0, vs=1.0, rows=None, kw=None, vw=None)
+
+    def quant(**kw):
+        a = dict(ok, **kw)
+        return q(ctypes.byref(g), a["k"], a["v"], a["stride"], a["T"], a["slots"], a["ks"], a["vs"],
+                 ctypes.byref(kc), ctypes.byref(vc), a["rows"], a["kw"], a["vw"], None)
+
+    assert quant(T=0, k=None, v=None, slots=None) == L.OK
+    assert quant(ks=0.0) == L.EINVAL and quant(vs=float("nan")) == L.EINVAL
+    assert quant(stride=72) == L.EALIGN                 # FP8 rows are read 16 bytes at a time
+    assert quant(stride=32) == L.EINVAL                 # below a token row (1 x 64)
+    assert quant(rows=FAKE) == L.EINVAL                 # a copy needs both workspaces
+    assert quant(rows=FAKE, kw=FAKE + 8, vw=FAKE) == L.EALIGN
+    d = L.lib().nvfp4_kv_dequant_workspace_fp8
+    okd = dict(bt=FAKE, maxp=16, pl=FAKE, offs=FAKE, B=2, ks=1.0, vs=1.0, kw=FAKE, vw=FAKE)
+
+    def deq(**kw):
+        a = dict(okd, **kw)
+        return d(ctypes.byref(g), ctypes.byref(kc), ctypes.byref(vc), a["bt"], a["maxp"], a["pl"], a["offs"],
+                 a["B"], a["ks"], a["vs"], a["kw"], a["vw"], None)
+
+    assert deq(ks=-1.0) == L.EINVAL and deq(vs=float("inf")) == L.EINVAL
+    assert deq(bt=None) == L.EINVAL
+    assert deq(kw=FAKE + 8) == L.EALIGN
+    assert deq(B=0, bt=None, pl=None, offs=None, kw=None, vw=None) == L.OK

@@ -284,6 +284,84 @@ def test_dequant_workspace_agentic_small(nk, shape):
     assert np.array_equal(synth.bf16_tensor_bits(vws), vref)
 
 
+def _fp8_bytes(rng, shape):
+    """Random FP8-E4M3 bytes over the whole finite range (NaN bytes replaced)."""
+    b = rng.integers(0, 256, size=shape).astype(np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x3A
+    return b
+
+
+@pytest.mark.parametrize("src_scale,gs", [(1.0, 1.0), (1.0, GS_THIRD), (0.37, 1.0)])
+def test_quantize_fp8_source_and_fused_chunk_copy(nk, src_scale, gs):
+    """The pages' path-2 types: FP8 K/V (strided, fused-QKV-like source) are
+    quantized to NVFP4 bit-exactly against the oracle, and in the same pass
+    copied unchanged into FP8 workspace rows (rows < 0 not copied)."""
+    rng = np.random.default_rng(41)
+    T, H, d, P, pages = 150, 2, 128, 16, 24
+    say(f"case quantize fp8 source: T {T} src_scale {src_scale} gs {gs}")
+    kb, vb = _fp8_bytes(rng, (T, H, d)), _fp8_bytes(rng, (T, H, d))
+    kb[:4, 0, :16] = 0                                                    # zero blocks
+    kb[4, 1, :16] = 0x80                                                  # -0.0 block
+    slots = rng.permutation(pages * P)[:T].astype(np.int64)
+    slots[7] = -1
+    rows = rng.permutation(T + 20)[:T].astype(np.int64)
+    rows[11] = -5
+    wide = np.zeros((T, 3 * H, d), np.uint8)                              # token stride 3 * H * d bytes
+    wide[:, :H], wide[:, H:2 * H] = kb, vb
+    wt = torch.from_numpy(wide).cuda()
+    kt, vt = wt[:, :H], wt[:, H:2 * H]
+    kp, vp = nv_pools(nk, pages, H, P, d, gs)
+    kws = torch.full((T + 20, H, d), SENT, dtype=torch.uint8, device="cuda")
+    vws = torch.full((T + 20, H, d), SENT, dtype=torch.uint8, device="cuda")
+    nk.nvfp4_kv_quantize_fp8(kt, vt, synth.to_device(slots), kp, vp, src_scale, src_scale,
+                             synth.to_device(rows), kws, vws)
+    torch.cuda.synchronize()
+    kd, ks = onv.empty_cache(pages, H, P, d, fill=SENT)
+    vd, vs = onv.empty_cache(pages, H, P, d, fill=SENT)
+    keep = slots >= 0
+    for (dd, ss), x in (((kd, ks), kb), ((vd, vs), vb)):
+        rd, rs = onv.quantize_rows_fp8(x, src_scale, gs)
+        dd[slots[keep] // P, :, slots[keep] % P] = rd[keep]
+        ss[slots[keep] // P, :, slots[keep] % P] = rs[keep]
+    assert_pool_equal(kp.data, kd, "fp8-source K data")
+    assert_pool_equal(kp.scale, ks, "fp8-source K scale")
+    assert_pool_equal(vp.data, vd, "fp8-source V data")
+    assert_pool_equal(vp.scale, vs, "fp8-source V scale")
+    for ws_t, x in ((kws, kb), (vws, vb)):
+        ref = np.full((T + 20, H, d), SENT, np.uint8)
+        ok = rows >= 0
+        ref[rows[ok]] = x[ok]
+        assert_pool_equal(ws_t, ref, "fused chunk copy")
+
+
+@pytest.mark.parametrize("gs,ws_scale", [(1.0, 1.0), (GS_THIRD, 1.0), (1.0, 0.5), (1.0, 0.3)])
+def test_dequant_workspace_fp8(nk, gs, ws_scale):
+    """The pages' FP8 workspace: bytes bit-exact against the oracle's E4M3
+    rounding of the dequantized prefix; rows past each prefix untouched."""
+    wl = synth.Workload(97, "wsfp8", 7, 16, 8, 128, 16, 0, False, 0, len_min=48, len_max=131,
+                        shared_prefix=32, chunk=9)
+    a = synth.host_agentic(wl)
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    say(f"case fp8 workspace: gs {gs} ws_scale {ws_scale}")
+    kp, vp = gpu_quantize_nv(nk, a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached, gs)
+    kd, ks, vd, vs = oracle_nv(a.num_pages, H, P, d, a.k_cached, a.v_cached, a.slot_cached, gs)
+    prefix = a.cached_lens.copy()
+    prefix[2] = 0
+    rows = int(a.ws_row_offsets[-1])
+    kws = torch.full((rows, H, d), SENT, dtype=torch.uint8, device="cuda")
+    vws = torch.full((rows, H, d), SENT, dtype=torch.uint8, device="cuda")
+    nk.nvfp4_kv_dequant_workspace_fp8(kp, vp, synth.to_device(a.block_tables), synth.to_device(prefix),
+                                      synth.to_device(a.ws_row_offsets), kws, vws, ws_scale, ws_scale)
+    torch.cuda.synchronize()
+    for ws_t, (dd, ss) in ((kws, (kd, ks)), (vws, (vd, vs))):
+        cache_b = onv.workspace_fp8_bytes(dd, ss, gs, ws_scale)
+        ref = np.full((rows, H, d), SENT, np.uint8)
+        for b in range(len(prefix)):
+            n, off = int(prefix[b]), int(a.ws_row_offsets[b])
+            ref[off:off + n] = oatt.gather_tokens(cache_b, a.block_tables[b], n)
+        assert_pool_equal(ws_t, ref, "fp8 workspace")
+
+
 # ---------------------------------------------------------------------------
 # decode attention
 # ---------------------------------------------------------------------------

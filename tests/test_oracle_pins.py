@@ -460,3 +460,45 @@ def test_workspace_bits_are_exact_at_power_of_two_scales():
     for gs in (1.0, 0.25, 8.0):
         d, s = nvfp4.quantize_rows(xb, gs)
         assert np.array_equal(nvfp4.workspace_bits(d, s, gs), attention.f64_to_bf16_exact(nvfp4.dequant_rows(d, s, gs)))
+
+
+# ---------------------------------------------------------------------------
+# the pages' FP8 path-2 types: FP8 source, FP8 workspace
+# ---------------------------------------------------------------------------
+
+def test_fp8_workspace_rounds_exactly_the_non_e4m3_products():
+    """Every product e2m1 * S (gs = ws_scale = 1) either is an E4M3 value and
+    is stored exactly, or is stored as its nearest E4M3 value (ties to the
+    even byte, saturating at 448). Checked against rational arithmetic and a
+    linear search; 275 of the 1016 products are rounded, 63 of them saturate."""
+    from fractions import Fraction
+    grid = [(Fraction(formats.E4M3_VALUES[b]), b) for b in range(127)]
+    codes = np.arange(8, dtype=np.uint8)
+    data = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)            # the 8 magnitudes, one block half
+    data = np.concatenate([data, data])                                  # 16 elements
+    rounded = saturated = 0
+    for sb in range(127):
+        got = nvfp4.workspace_fp8_bytes(data[None, :], np.array([[sb]], np.uint8))[0]
+        for c in range(8):
+            exact = Fraction(formats.E2M1_VALUES[c]) * Fraction(formats.E4M3_VALUES[sb])
+            if exact > 448:
+                want, saturated = 0x7E, saturated + 1
+            else:
+                best = min(grid, key=lambda g: (abs(g[0] - exact), g[1] & 1))
+                want = best[1]
+            if Fraction(formats.E4M3_VALUES[want]) != exact:
+                rounded += 1
+            assert got[c] == want, (sb, c, got[c], want)
+    assert (rounded, saturated) == (275, 63)
+
+
+def test_fp8_source_rows_equal_the_bf16_route():
+    """FP8 values are bf16 values (4 significant bits), so quantizing FP8 bytes
+    at source scale 1 must equal quantizing their bf16 images."""
+    rng = np.random.default_rng(35)
+    b = rng.integers(0, 256, size=(64, 2, 128)).astype(np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x41                                          # no NaN bytes
+    d1, s1 = nvfp4.quantize_rows_fp8(b)
+    vals = formats.E4M3_VALUES[b.astype(np.int64)].astype(np.float32)
+    d2, s2 = nvfp4.quantize_rows((vals.view(np.uint32) >> 16).astype(np.uint16))
+    assert np.array_equal(d1, d2) and np.array_equal(s1, s2)
