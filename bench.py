@@ -308,8 +308,36 @@ def agentic(nk, wl, steps, warmup):
     log(f"[bench] agentic fp8 path-2 step {t8 * 1e3:.3f} ms: "
         + ", ".join(f"{k} {v * 1e3:.3f} ms" for k, v in per8.items()))
 
-    # global-scale calibration of the chunk (absmax of K and V), not part of the step
+    # extend attention of the chunk over the bf16 workspace (path 2's consumer), not part of the step:
+    # the chunk's K/V go to the workspace rows after each prefix, then its queries attend causally
+    crow = torch.from_numpy(np.concatenate([offs[b] + w.host_cached_lens[b] + np.arange(C)
+                                            for b in range(B)]).astype(np.int64)).cuda()
+    w.k_ws[crow] = w.k_chunk
+    w.v_ws[crow] = w.v_chunk
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 2000)
+    qx = torch.randn((B * C, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    q_offs = torch.arange(0, B * C + 1, C, dtype=torch.int64, device="cuda")
+    ox = torch.empty_like(qx)
+    ext = lambda: nk.nvfp4_extend_attn(qx, q_offs, w.k_ws, w.v_ws, w.ws_row_offsets, w.cached_lens, wl.sm_scale,
+                                       max_chunk=C, out=ox)
     stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        ext()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        ext()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_ext = e0.elapsed_time(e1) / steps / 1e3
+    Lc = w.host_cached_lens.astype(np.float64)
+    flops = 4.0 * d * Hq * float(np.sum(C * Lc + C * (C + 1) / 2.0))
+    res["extend_attention"] = {"ms": round(t_ext * 1e3, 4), "tflops": round(flops / t_ext / 1e12, 1),
+                               "bf16_mfma_peak_frac": round(flops / t_ext / 2.5e15, 4), "flops": flops}
+    log(f"[bench] extend attention {t_ext * 1e3:.3f} ms, {flops / t_ext / 1e12:.1f} TFLOP/s")
+
+    # global-scale calibration of the chunk (absmax of K and V), not part of the step
     amax = torch.zeros(2, dtype=torch.float32, device="cuda")
     cal = lambda: (nk.nvfp4_kv_absmax(w.k_chunk, amax[0:1]), nk.nvfp4_kv_absmax(w.v_chunk, amax[1:2]))
     for _ in range(warmup):
@@ -323,7 +351,7 @@ def agentic(nk, wl, steps, warmup):
     t_cal = e0.elapsed_time(e1) / steps / 1e3
     res["absmax_calibration"] = {"ms": round(t_cal * 1e3, 4), "gbs": round(by["quant_read"] / t_cal / 1e9, 1)}
     log(f"[bench] absmax calibration {t_cal * 1e3:.3f} ms")
-    del w, ws, out, kws8, vws8
+    del w, ws, out, kws8, vws8, qx, ox
     torch.cuda.empty_cache()
     return res
 

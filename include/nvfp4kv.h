@@ -309,6 +309,32 @@ int nvfp4_kv_absmax(const void* x, int64_t token_stride, int32_t num_tokens, int
  */
 float nvfp4_global_scale_from_absmax(float amax);
 
+/*
+ * nvfp4_extend_attn -- chunked-prefill / extend attention over the workspace
+ * (section A2, path 2: the chunk's queries attend to the dequantized cached
+ * prefix and, causally, to the chunk itself). bf16 operands on the matrix
+ * cores, fp32 softmax and accumulation, bf16 output.
+ *
+ *   q               device bf16 [q rows][num_q_heads][head_dim]; sequence b's
+ *                   chunk queries are rows [q_row_offsets[b], q_row_offsets[b+1])
+ *   q_row_offsets   device int64 [batch + 1], non-decreasing
+ *   k_ws, v_ws      device bf16 [rows][num_kv_heads][head_dim]: sequence b's keys
+ *                   are rows ws_row_offsets[b] + j, j < prefix_lens[b] + chunk_b
+ *                   (the prefix from nvfp4_kv_dequant_workspace, then the chunk)
+ *   ws_row_offsets  device int64 [batch + 1]
+ *   prefix_lens     device int32 [batch]
+ *   max_chunk       >= every chunk length (sizes the grid); 0 is a no-op
+ *   sm_scale        logit scale (finite)
+ *   out             device bf16 [q rows][num_q_heads][head_dim]
+ * Query i of sequence b sits at position prefix_lens[b] + i and attends to keys
+ * j <= prefix_lens[b] + i; query head h reads KV head h / (num_q_heads /
+ * num_kv_heads), a group of 1, 2, 4, 8 or 16.
+ */
+int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, const void* k_ws, const void* v_ws,
+                      const int64_t* ws_row_offsets, const int32_t* prefix_lens, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_chunk,
+                      float sm_scale, void* out, void* stream);
+
 /* Text of the last non-zero return on the calling thread ("" if none). */
 const char* nvfp4kv_last_error(void);
 

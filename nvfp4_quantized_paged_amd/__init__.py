@@ -62,6 +62,8 @@ _SIGNATURES = {
                                                 c_f32, c_i32, c_i32, c_vp, c_size, c_vp]),
     "nvfp4kv_lse_merge": (ctypes.c_int, [c_vp, c_size, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_vp]),
     "nvfp4_kv_absmax": (ctypes.c_int, [c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "nvfp4_extend_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                         c_f32, c_vp, c_vp]),
     "nvfp4_kv_quantize_fp8": (ctypes.c_int, [P_GEOM, c_vp, c_vp, c_i64, c_i32, c_vp, c_f32, c_f32, P_NV, P_NV,
                                              c_vp, c_vp, c_vp, c_vp]),
     "nvfp4_kv_dequant_workspace_fp8": (ctypes.c_int, [P_GEOM, P_NV, P_NV, c_vp, c_i32, c_vp, c_vp, c_i32,
@@ -224,6 +226,29 @@ def nvfp4_kv_absmax(x, amax, stream=None):
     stride = x.stride(0) if x.shape[0] > 0 else x.shape[1] * x.shape[2]
     _check(lib().nvfp4_kv_absmax(x.data_ptr(), stride, x.shape[0], x.shape[1], x.shape[2], amax.data_ptr(),
                                  _stream(stream)))
+
+
+def nvfp4_extend_attn(q, q_row_offsets, k_ws, v_ws, ws_row_offsets, prefix_lens, sm_scale, max_chunk=None,
+                      out=None, stream=None):
+    """Extend attention of chunk queries q [rows][Hq][d] (bf16) over workspaces k_ws, v_ws ([rows][Hkv][d] bf16):
+    sequence b's queries are rows q_row_offsets[b].. (int64 [B+1]); its keys are workspace rows
+    ws_row_offsets[b] + j, j < prefix_lens[b] + chunk_b, attended causally. Returns out."""
+    _need(q, torch.bfloat16, "q")
+    _need(k_ws, torch.bfloat16, "k_ws")
+    _need(v_ws, torch.bfloat16, "v_ws")
+    _need(q_row_offsets, torch.int64, "q_row_offsets")
+    _need(ws_row_offsets, torch.int64, "ws_row_offsets")
+    _need(prefix_lens, torch.int32, "prefix_lens")
+    if max_chunk is None:
+        max_chunk = int((q_row_offsets[1:] - q_row_offsets[:-1]).max().item()) if prefix_lens.numel() else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.bfloat16, "out")
+    _check(lib().nvfp4_extend_attn(q.data_ptr(), q_row_offsets.data_ptr(), k_ws.data_ptr(), v_ws.data_ptr(),
+                                   ws_row_offsets.data_ptr(), prefix_lens.data_ptr(), prefix_lens.shape[0],
+                                   q.shape[1], k_ws.shape[1], q.shape[2], int(max_chunk), float(sm_scale),
+                                   out.data_ptr(), _stream(stream)))
+    return out
 
 
 def nvfp4_global_scale_from_absmax(amax: float) -> float:

@@ -210,6 +210,43 @@ NVFP4KV_API int nvfp4_kv_absmax(const void* x, int64_t token_stride, int32_t num
                   fn);
 }
 
+NVFP4KV_API int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, const void* k_ws,
+                                  const void* v_ws, const int64_t* ws_row_offsets, const int32_t* prefix_lens,
+                                  int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_chunk, float sm_scale, void* out, void* stream) {
+  const char* fn = "nvfp4_extend_attn";
+  if (batch < 0 || batch > kGridYZ) return fail(NVFP4KV_EINVAL, "%s: batch %d out of range [0, %d]", fn, batch, kGridYZ);
+  if (num_kv_heads <= 0 || num_kv_heads > kGridYZ || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(NVFP4KV_EINVAL, "%s: heads %d / %d (num_q_heads must be a multiple of num_kv_heads)", fn,
+                num_q_heads, num_kv_heads);
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group > kMaxGroup || (group & (group - 1)) != 0)
+    return fail(NVFP4KV_EUNSUPPORTED, "%s: query heads per KV head %d (1, 2, 4, 8 or 16)", fn, group);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(NVFP4KV_EUNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
+  if (max_chunk < 0) return fail(NVFP4KV_EINVAL, "%s: max_chunk %d < 0", fn, max_chunk);
+  if (!isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "%s: sm_scale must be finite", fn);
+  if (batch == 0 || max_chunk == 0) return launched(hipSuccess, fn);
+  if (!q || !q_row_offsets || !k_ws || !v_ws || !ws_row_offsets || !prefix_lens || !out)
+    return fail(NVFP4KV_EINVAL, "%s: pointers must be non-NULL", fn);
+  if (!aligned16(q) || !aligned16(k_ws) || !aligned16(v_ws) || !aligned16(out))
+    return fail(NVFP4KV_EALIGN, "%s: q, k_ws, v_ws and out must be 16-byte aligned", fn);
+  ExtendParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_row_offsets = q_row_offsets;
+  p.k = static_cast<const uint16_t*>(k_ws);
+  p.v = static_cast<const uint16_t*>(v_ws);
+  p.ws_row_offsets = ws_row_offsets;
+  p.prefix_lens = prefix_lens;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.max_chunk = max_chunk;
+  p.qk_scale = sm_scale * 1.4426950408889634f;
+  p.out = static_cast<uint16_t*>(out);
+  return launched(launch_extend_attn(p, head_dim, static_cast<hipStream_t>(stream)), fn);
+}
+
 NVFP4KV_API float nvfp4_global_scale_from_absmax(float amax) {
   if (!(amax > 0.0f) || !isfinite(amax)) return 1.0f;
   return amax / (448.0f * 6.0f);

@@ -158,6 +158,18 @@ struct DecodeParams {
   float qk_scale;           // sm_scale * K global scale * log2(e)
 };
 
+struct ExtendParams {
+  const uint16_t* q;            // [q rows][Hq][D] bf16
+  const int64_t* q_row_offsets; // [B + 1]
+  const uint16_t* k;            // workspace [rows][Hkv][D] bf16
+  const uint16_t* v;
+  const int64_t* ws_row_offsets;  // [B + 1]
+  const int32_t* prefix_lens;   // [B]
+  int32_t batch, num_q_heads, num_kv_heads, max_chunk;
+  float qk_scale;               // sm_scale * log2(e)
+  uint16_t* out;                // [q rows][Hq][D] bf16
+};
+
 struct MergeParams {
   const float* part_o;
   const float* part_ml;
@@ -173,6 +185,7 @@ hipError_t launch_decode_valu(const DecodeParams& p, int head_dim, bool fp8, hip
 // lut: NVFP4 unpack through a register lookup table instead of the conversion instruction
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, bool lut, hipStream_t s);
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_extend_attn(const ExtendParams& p, int head_dim, hipStream_t s);
 // running max |x| of a [tokens][row_elems] bf16 tensor (rows `stride` elements apart) into *amax
 hipError_t launch_absmax(const uint16_t* x, int64_t stride, int32_t num_tokens, int32_t row_elems,
                          float* amax, hipStream_t s);

@@ -106,3 +106,25 @@ def dequant_workspace(cache_hat: np.ndarray, block_tables: np.ndarray,
         else:
             ws[off:off + n] = gather_tokens(cache_bits, block_tables[b], n)
     return ws
+
+
+def extend_attention(q: np.ndarray, k_ws: np.ndarray, v_ws: np.ndarray, q_row_offsets: np.ndarray,
+                     ws_row_offsets: np.ndarray, prefix_lens: np.ndarray, sm_scale: float):
+    """Extend (chunked-prefill) attention, "Accelerating Long-Context and Agentic
+    Inference with NVFP4 KV Cache" section A2 path 2: the chunk's queries
+    attend to the cached prefix and causally to the chunk. Query i of sequence
+    b (q row q_row_offsets[b] + i) sits at position prefix_lens[b] + i and sees
+    workspace rows ws_row_offsets[b] + j for j <= prefix_lens[b] + i.
+
+    q [rows][Hq][d], k_ws / v_ws [rows][Hkv][d] (float64). Returns (out, mass)
+    shaped like q: the plain softmax attention per query and the tolerance
+    weight sum_t p_t |v_t| (decode_heads per query)."""
+    out = np.zeros(q.shape, dtype=np.float64)
+    mass = np.zeros(q.shape, dtype=np.float64)
+    for b in range(len(prefix_lens)):
+        L, w0 = int(prefix_lens[b]), int(ws_row_offsets[b])
+        for r in range(int(q_row_offsets[b]), int(q_row_offsets[b + 1])):
+            i = r - int(q_row_offsets[b])
+            keys = slice(w0, w0 + L + i + 1)
+            out[r], mass[r] = decode_heads(q[r], k_ws[keys], v_ws[keys], sm_scale)
+    return out, mass

@@ -362,6 +362,54 @@ def test_dequant_workspace_fp8(nk, gs, ws_scale):
         assert_pool_equal(ws_t, ref, "fp8 workspace")
 
 
+@pytest.mark.parametrize("G,Hkv,d,P", [(4, 2, 128, 16), (1, 2, 64, 32), (8, 1, 128, 16), (16, 1, 64, 16)])
+def test_extend_attention_over_workspace(nk, G, Hkv, d, P):
+    """Path 2 end to end at a small size: the prefix is quantized into the
+    pool and dequantized into the bf16 workspace by the library, the chunk's
+    K/V follow it in the workspace, and the chunk's queries attend (causally
+    within the chunk) through nvfp4_extend_attn; against the oracle. Ragged
+    chunks, an empty prefix, a one-token chunk and an empty chunk included."""
+    rng = np.random.default_rng(42)
+    B = 6
+    prefix = np.array([37, 0, 120, 64, 5, 90], np.int32)
+    chunk = np.array([33, 17, 1, 48, 0, 40], np.int32)
+    Hq = G * Hkv
+    say(f"case extend attention: G {G} Hkv {Hkv} d {d} P {P}")
+    pages_per = -(-(prefix + chunk).max() // P)
+    num_pages = B * pages_per
+    bt = rng.permutation(num_pages).astype(np.int32).reshape(B, pages_per)
+    kb = synth.host_values(rng, (int(prefix.sum()), Hkv, d))
+    vb = synth.host_values(rng, (int(prefix.sum()), Hkv, d))
+    slots = np.concatenate([bt[b, np.arange(prefix[b]) // P].astype(np.int64) * P + np.arange(prefix[b]) % P
+                            for b in range(B)])
+    kp, vp = gpu_quantize_nv(nk, num_pages, Hkv, P, d, kb, vb, slots)
+    ws_offs = np.zeros(B + 1, np.int64)
+    ws_offs[1:] = np.cumsum(prefix + chunk + 3)                  # 3 spare rows per sequence
+    rows = int(ws_offs[-1])
+    kws = torch.zeros((rows, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    vws = torch.zeros((rows, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    nk.nvfp4_kv_dequant_workspace(kp, vp, synth.to_device(bt), synth.to_device(prefix), synth.to_device(ws_offs),
+                                  kws, vws)
+    # the chunk's own K/V go to the rows after each prefix
+    kc = synth.host_values(rng, (int(chunk.sum()), Hkv, d))
+    vc = synth.host_values(rng, (int(chunk.sum()), Hkv, d))
+    crow = np.concatenate([ws_offs[b] + prefix[b] + np.arange(chunk[b]) for b in range(B)]).astype(np.int64)
+    idx = torch.from_numpy(crow).cuda()
+    kws[idx] = synth.to_device_bf16(kc)
+    vws[idx] = synth.to_device_bf16(vc)
+    q_offs = np.zeros(B + 1, np.int64)
+    q_offs[1:] = np.cumsum(chunk)
+    qb = synth.host_values(rng, (int(chunk.sum()), Hq, d))
+    sm = 1.0 / math.sqrt(d)
+    out = nk.nvfp4_extend_attn(synth.to_device_bf16(qb), synth.to_device(q_offs), kws, vws, synth.to_device(ws_offs),
+                               synth.to_device(prefix), sm, max_chunk=int(chunk.max()) + 5)
+    torch.cuda.synchronize()
+    kw = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(kws))
+    vw = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(vws))
+    ref, mass = oatt.extend_attention(synth.bf16_bits_to_f64(qb), kw, vw, q_offs, ws_offs, prefix, sm)
+    check_out(out, ref, mass, f"extend G{G} d{d}")
+
+
 # ---------------------------------------------------------------------------
 # decode attention
 # ---------------------------------------------------------------------------

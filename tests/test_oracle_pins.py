@@ -502,3 +502,39 @@ def test_fp8_source_rows_equal_the_bf16_route():
     vals = formats.E4M3_VALUES[b.astype(np.int64)].astype(np.float32)
     d2, s2 = nvfp4.quantize_rows((vals.view(np.uint32) >> 16).astype(np.uint16))
     assert np.array_equal(d1, d2) and np.array_equal(s1, s2)
+
+
+# ---------------------------------------------------------------------------
+# extend attention (path 2)
+# ---------------------------------------------------------------------------
+
+def test_extend_attention_pins():
+    """A one-query chunk is decode over the prefix plus itself; later chunk
+    keys never change earlier queries (causality); explicit loops on a tiny
+    case agree with the vectorised routine."""
+    rng = np.random.default_rng(36)
+    Hq, Hkv, d, sm = 4, 2, 16, 0.25
+    L, C = 5, 3
+    q = rng.standard_normal((C, Hq, d))
+    k = rng.standard_normal((L + C, Hkv, d))
+    v = rng.standard_normal((L + C, Hkv, d))
+    qo, wo, pl = np.array([0, C]), np.array([0, L + C]), np.array([L])
+    out, _ = attention.extend_attention(q, k, v, qo, wo, pl, sm)
+    # query 0 = decode over keys [0, L]
+    ref0, _ = attention.decode_heads(q[0], k[:L + 1], v[:L + 1], sm)
+    assert np.allclose(out[0], ref0, rtol=1e-13, atol=1e-13)
+    # causality: perturb the last chunk key; queries 0 .. C-2 unchanged
+    k2, v2 = k.copy(), v.copy()
+    k2[-1] += 5.0
+    v2[-1] -= 3.0
+    out2, _ = attention.extend_attention(q, k2, v2, qo, wo, pl, sm)
+    assert np.array_equal(out2[:C - 1], out[:C - 1]) and not np.allclose(out2[C - 1], out[C - 1])
+    # explicit loops
+    for i in range(C):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            s = [sm * sum(q[i, h, c] * k[j, g, c] for c in range(d)) for j in range(L + i + 1)]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            o = [sum(w[j] * v[j, g, c] for j in range(L + i + 1)) / sum(w) for c in range(d)]
+            assert np.allclose(out[i, h], o, rtol=1e-12, atol=1e-12)
