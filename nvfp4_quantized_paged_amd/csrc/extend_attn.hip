@@ -11,14 +11,17 @@
 //
 // Compute-bound (4 * Hq * d flops per query-key pair), so the products run on
 // the bf16 matrix cores (v_mfma_f32_16x16x32_bf16), laid out like the decode
-// kernel: each wave computes S^T = K Q^T for 16 queries of one head (queries
-// are the 16 MFMA columns), keeps the online softmax per column, and reuses
-// the softmax output in its C layout as the B operand of O^T = V^T P^T. A
-// workgroup holds the G query heads of one KV head times WQ blocks of 16
-// queries (8 waves); each 64-key block of K and V is staged once in LDS and
-// read by all of them: K row-major, V transposed, so the A operand of the PV
-// product is two 8-byte LDS reads and no transpose runs on the matrix unit.
-// Row pitches are padded so the lanes of one read hit distinct LDS banks.
+// kernel: a wave computes S^T = K Q^T for two 16-column tiles (queries or heads
+// are the MFMA columns, and each K operand read from LDS feeds both), keeps the
+// online softmax per column, and reuses the softmax output in its C layout as
+// the B operand of O^T = V^T P^T. A workgroup (8 waves) holds the G query heads
+// of one KV head times enough query tiles; each 64-key block of K and V is
+// staged once in LDS and read by all of them: K row-major, V transposed, so the
+// A operand of the PV product is two 8-byte LDS reads and no transpose runs on
+// the matrix unit. The next block is loaded into registers while the current
+// one is computed and written to the second of two LDS buffers (one barrier
+// per block). Row pitches are padded so the lanes of one read spread over the
+// LDS banks.
 #include "common.hpp"
 
 namespace nvfp4kv {
@@ -28,146 +31,290 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kKB = 64;                    // keys per LDS block
+constexpr int kRsrcWord3 = 0x00020000;     // gfx9 raw buffer descriptor, 32-bit data format
 
 __device__ inline float4_t mfma_bf16(const bf16x8_t& a, const bf16x8_t& b, const float4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// A wave computes two 16-column tiles that share every K operand: two 16-query tiles of one
+// head, or (16 heads per KV head) one 16-query tile of two heads. A workgroup has 8 waves:
+// the group's heads times enough query tiles.
 template <int D, int G>
 struct ExtCfg {
-  static constexpr int kWQ = G >= 8 ? 1 : 8 / G;     // 16-query blocks per workgroup
-  static constexpr int kWaves = G * kWQ;
-  static constexpr int kQPerGroup = 16 * kWQ;
+  static constexpr int kNT = 2;                             // 16-column tiles per wave
+  static constexpr int kHPW = G >= 16 ? 2 : 1;              // heads per wave
+  static constexpr int kQT = kNT / kHPW;                    // 16-query tiles per wave
+  static constexpr int kHeadWaves = G / kHPW;               // waves covering the group's heads
+  static constexpr int kWQ = kHeadWaves >= 8 ? 1 : 8 / kHeadWaves;   // query groups per workgroup
+  static constexpr int kWaves = kHeadWaves * kWQ;
+  static constexpr int kQPerWave = 16 * kQT;
+  static constexpr int kQPerGroup = kQPerWave * kWQ;
   static constexpr int kKPitch = D + 8;             // K row pitch (bf16): 16-byte reads of 16 rows spread over banks
   static constexpr int kVPitch = kKB + 4;           // V^T row pitch (bf16)
   static constexpr int kKSteps = D / 32;
   static constexpr int kCTiles = D / 16;
 };
 
+// The running max of a query is raised only when a block's max exceeds it by
+// more than this (log2 units), so the softmax numerators stay below 2^8 and
+// the accumulator rescale is skipped for most blocks; the normalised result is
+// the same up to rounding.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D, int G>
-__global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kernel(ExtendParams p) {
+__global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kernel(ExtendParams p, int num_qblocks) {
   using C = ExtCfg<D, G>;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kKB * C::kKPitch];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[D * C::kVPitch];
-  const int b = blockIdx.z, g = blockIdx.y;
+  constexpr int NT = C::kNT;
+  // two LDS buffers: block j is read from buffer j % 2 while block j + 1 is written to the other
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kKB * C::kKPitch];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * C::kVPitch];
+  // Workgroup w runs on XCD w % 8; tiles are renumbered so that the query blocks of
+  // one (sequence, KV head), which read the same keys, are consecutive on one XCD.
+  const int nwg = (int)gridDim.x;
+  const int wg = (int)blockIdx.x;
+  const int per = nwg / 8, rem = nwg % 8, x = wg % 8;
+  const int tile = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + wg / 8;
+  const int qb_idx = tile % num_qblocks;
+  const int g = (tile / num_qblocks) % p.num_kv_heads;
+  const int b = tile / (num_qblocks * p.num_kv_heads);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int h = g * G + wave % G;
   const int64_t q_begin = p.q_row_offsets[b];
   const int chunk = (int)__builtin_amdgcn_readfirstlane((int)(p.q_row_offsets[b + 1] - q_begin));
-  const int qblk = blockIdx.x * C::kQPerGroup;
+  const int qblk = qb_idx * C::kQPerGroup;
   if (qblk >= chunk) return;                                   // uniform over the workgroup
   const int L = __builtin_amdgcn_readfirstlane(p.prefix_lens[b]);
   const int64_t kv0 = p.ws_row_offsets[b];
   const int nkeys = L + min(chunk, qblk + C::kQPerGroup);       // keys any query of this workgroup sees
-  const int qi = qblk + (wave / G) * 16 + col;                  // this lane's query (chunk index)
-  const int qe = min(qi, chunk - 1);                            // past the chunk: a valid stand-in, not written
+  const int qw = qblk + (wave / C::kHeadWaves) * C::kQPerWave;  // first query of this wave
+  const int h0 = g * G + (wave % C::kHeadWaves) * C::kHPW;      // first head of this wave
+  // a negative logit scale moves its sign into q (exact in bf16), so the scale used below is positive
+  const uint32_t qsign = p.qk_scale < 0.0f ? 0x80008000u : 0u;
+  const float cs = fabsf(p.qk_scale);                           // |sm_scale| * log2(e)
 
-  // Q^T as the B operand: lane (query col, grp), step kk: channels 32kk + 8grp .. +7
-  bf16x8_t qb[C::kKSteps];
-  {
-    const uint16_t* qrow = p.q + ((q_begin + qe) * p.num_q_heads + h) * D;
+  // Q^T as the B operand of tile n (head h0 + n % kHPW, queries qw + 16 (n / kHPW) ..):
+  // lane (query col, grp), step kk: channels 32kk + 8grp .. +7
+  bf16x8_t qb[NT][C::kKSteps];
+  int causal[NT];                                               // last key each of the lane's queries sees
 #pragma unroll
-    for (int kk = 0; kk < C::kKSteps; ++kk)
-      qb[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * grp);
+  for (int n = 0; n < NT; ++n) {
+    const int qe = min(qw + 16 * (n / C::kHPW) + col, chunk - 1);  // past the chunk: a valid stand-in, not written
+    causal[n] = L + qe;
+    const uint16_t* qrow = p.q + ((q_begin + qe) * p.num_q_heads + h0 + n % C::kHPW) * D;
+#pragma unroll
+    for (int kk = 0; kk < C::kKSteps; ++kk) {
+      uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * grp);
+      w.x ^= qsign; w.y ^= qsign; w.z ^= qsign; w.w ^= qsign;
+      qb[n][kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
   }
-  const float cs = p.qk_scale;                                  // sm_scale * log2(e)
+  // blocks ending at or before this key need no causal mask for any query of the wave
+  const int unmasked_end = L + min(qw, chunk - 1);
 
-  float4_t o[C::kCTiles];
+  // o: O^T tiles; lsum: the softmax denominators, accumulated on the matrix unit as the
+  // product of an all-ones A operand with the same numerators (every lane of a query
+  // column holds the column's full sum)
+  float4_t o[NT][C::kCTiles], lsum[NT];
+  float m[NT];
 #pragma unroll
-  for (int c = 0; c < C::kCTiles; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.0f;
-  const int causal = L + qe;                                    // last key this query sees
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int c = 0; c < C::kCTiles; ++c) o[n][c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    lsum[n] = float4_t{0.f, 0.f, 0.f, 0.f};
+    m[n] = -INFINITY;
+  }
+  const bf16x8_t ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                         (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 
-  for (int k0 = 0; k0 < nkeys; k0 += kKB) {
-    __syncthreads();                                            // the previous block's LDS reads are done
-    // stage keys [k0, k0 + 64): K row-major, V transposed (rows past nkeys repeat the last key; masked)
-    for (int piece = threadIdx.x; piece < kKB * (D / 8); piece += 64 * C::kWaves) {
-      const int kr = piece / (D / 8), c8 = piece % (D / 8);
-      const int64_t row = kv0 + min(k0 + kr, nkeys - 1);
-      const int64_t off = (row * p.num_kv_heads + g) * D + c8 * 8;
-      const uint4 kv = *reinterpret_cast<const uint4*>(p.k + off);
-      const uint4 vv = *reinterpret_cast<const uint4*>(p.v + off);
-      *reinterpret_cast<uint4*>(&k_lds[kr * C::kKPitch + c8 * 8]) = kv;
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  // Staging of a 64-key block through registers: K in 16-byte pieces (8 channels of one key),
+  // stored row-major; V in quads of 4 keys x 4 channels (four 8-byte loads, consecutive quads
+  // along the channels so that a wave reads whole rows), transposed with byte permutes and
+  // stored as four 8-byte pieces of V^T rows.
+  constexpr int kThreads = 64 * C::kWaves;
+  constexpr int kKPieces = kKB * D / 8, kVQuads = kKB / 4 * D / 4;
+  constexpr int kKPer = (kKPieces + kThreads - 1) / kThreads;
+  constexpr int kVPer = (kVQuads + kThreads - 1) / kThreads;
+  u32x4_t kreg[kKPer];
+  u32x2_t vreg[kVPer][4];
+  // A block's rows are read through a buffer descriptor based at its first row (head g) that
+  // covers only the block's keys below nkeys: rows past them read as zeros (and are masked).
+  // The per-thread offsets within a block are fixed.
+  const uint32_t rs_bytes = (uint32_t)(p.num_kv_heads * D * 2);  // bytes between workspace rows
+  const char* kseq = reinterpret_cast<const char*>(p.k + (kv0 * p.num_kv_heads + g) * D);
+  const char* vseq = reinterpret_cast<const char*>(p.v + (kv0 * p.num_kv_heads + g) * D);
+  uint32_t koff[kKPer], voff[kVPer];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt_lds[(c8 * 8 + 2 * e) * C::kVPitch + kr] = __builtin_bit_cast(__bf16, (uint16_t)(w[e] & 0xFFFFu));
-        vt_lds[(c8 * 8 + 2 * e + 1) * C::kVPitch + kr] = __builtin_bit_cast(__bf16, (uint16_t)(w[e] >> 16));
+  for (int i = 0; i < kKPer; ++i) {
+    const uint32_t piece = threadIdx.x + i * kThreads;
+    koff[i] = piece / (D / 8) * rs_bytes + piece % (D / 8) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < kVPer; ++i) {
+    const uint32_t quad = threadIdx.x + i * kThreads;
+    voff[i] = 4 * (quad / (D / 4)) * rs_bytes + quad % (D / 4) * 8;
+  }
+  auto load_block = [&](int k0) {
+    const int nrec = (int)(min(nkeys - k0, kKB) * rs_bytes);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kseq + (int64_t)k0 * rs_bytes), (short)0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vseq + (int64_t)k0 * rs_bytes), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < kKPer; ++i)
+      if (kKPieces % kThreads == 0 || (int)threadIdx.x + i * kThreads < kKPieces)
+        kreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff[i], 0, 0));
+#pragma unroll
+    for (int i = 0; i < kVPer; ++i)
+      if (kVQuads % kThreads == 0 || (int)threadIdx.x + i * kThreads < kVQuads)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vreg[i][j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(voff[i] + j * rs_bytes), 0, 0));
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kKPer; ++i) {
+      const int piece = threadIdx.x + i * kThreads;
+      if (kKPieces % kThreads == 0 || piece < kKPieces) {
+        const int kr = piece / (D / 8), c8 = piece % (D / 8);
+        *reinterpret_cast<u32x4_t*>(&k_lds[buf][kr * C::kKPitch + c8 * 8]) = kreg[i];
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kVPer; ++i) {
+      const int quad = threadIdx.x + i * kThreads;
+      if (kVQuads % kThreads == 0 || quad < kVQuads) {
+        const int c4 = quad % (D / 4), kq = quad / (D / 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          // channel 4c4 + c of keys 4kq .. 4kq + 3: 16-bit half (c & 1) of word c / 2 of each key's piece
+          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          const int wd = c >> 1;
+          const u32x2_t out = {__builtin_amdgcn_perm(vreg[i][1][wd], vreg[i][0][wd], sel),
+                               __builtin_amdgcn_perm(vreg[i][3][wd], vreg[i][2][wd], sel)};
+          *reinterpret_cast<u32x2_t*>(&vt_lds[buf][(4 * c4 + c) * C::kVPitch + 4 * kq]) = out;
+        }
+      }
+    }
+  };
 
-    // ---- S^T = K Q^T: lane (query col, grp) holds keys 16t + 4grp + i of key tile t
-    float sc[4][4];
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < nkeys; k0 += kKB, buf ^= 1) {
+    const bool more = k0 + kKB < nkeys;                         // uniform over the workgroup
+    if (more) load_block(k0 + kKB);                             // lands during this block's products
+    const __bf16* kl = k_lds[buf];
+    const __bf16* vl = vt_lds[buf];
+
+    // ---- S^T = K Q^T: lane (query col, grp) of tile n holds keys 16t + 4grp + i of key tile t;
+    // each K operand read from LDS feeds the NT query tiles
+    float sc[NT][4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      float4_t c4 = float4_t{0.f, 0.f, 0.f, 0.f};
+      float4_t acc[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < C::kKSteps; ++kk) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&k_lds[(16 * t + col) * C::kKPitch + 32 * kk + 8 * grp]);
-        c4 = mfma_bf16(a, qb[kk], c4);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&kl[(16 * t + col) * C::kKPitch + 32 * kk + 8 * grp]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = mfma_bf16(a, qb[n][kk], acc[n]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[t][i] = (k0 + 16 * t + 4 * grp + i <= causal) ? c4[i] : -INFINITY;
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[n][t][i] = acc[n][i];
+    }
+    if (k0 + kKB - 1 > unmasked_end) {                          // the block crosses some query's diagonal
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + 16 * t + 4 * grp + i > causal[n]) sc[n][t][i] = -INFINITY;
     }
 
-    // ---- online softmax (base 2) per query column
-    float cmax = -INFINITY;
+    // ---- online softmax (base 2) per query column, lazily rescaled
+    float cmax[NT];
+    bool grow = false;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int n = 0; n < NT; ++n) {
+      float v = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[t][i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float mnew = fmaxf(m, cmax * cs);                     // finite: key 0 is in every query's range
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
-    float psum = 0.0f;
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+        for (int i = 0; i < 4; ++i) v = fmaxf(v, sc[n][t][i]);
+      v = fmaxf(v, __shfl_xor(v, 16, 64));
+      v = fmaxf(v, __shfl_xor(v, 32, 64));
+      cmax[n] = v * cs;                                         // finite in the first block: key 0 is in every query's range
+      grow |= cmax[n] > m[n] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {               // wave-uniform
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[t][i] = __builtin_amdgcn_exp2f(fmaf(sc[t][i], cs, -mnew));
-        psum += sc[t][i];
+      for (int n = 0; n < NT; ++n) {
+        const float mnew = fmaxf(m[n], cmax[n]);
+        const float alpha = __builtin_amdgcn_exp2f(m[n] - mnew);
+        m[n] = mnew;
+        lsum[n] *= alpha;
+#pragma unroll
+        for (int c = 0; c < C::kCTiles; ++c) o[n][c] *= alpha;
       }
-    l = l * alpha + psum;
+    }
 #pragma unroll
-    for (int c = 0; c < C::kCTiles; ++c) o[c] *= alpha;
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[n][t][i] = __builtin_amdgcn_exp2f(fmaf(sc[n][t][i], cs, -m[n]));
 
     // ---- O^T += V^T P^T over key-tile pairs: k-slot (grp, e) is key 16t + 4grp + e (e < 4)
-    // or 16(t + 1) + 4grp + e - 4, the same keys the lane holds in sc[t], sc[t + 1]
+    // or 16(t + 1) + 4grp + e - 4, the same keys the lane holds in sc[n][t], sc[n][t + 1]
 #pragma unroll
     for (int t = 0; t < 4; t += 2) {
-      bf16x8_t pb;
+      bf16x8_t pb[NT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = (__bf16)sc[t][i];
-        pb[4 + i] = (__bf16)sc[t + 1][i];
+      for (int n = 0; n < NT; ++n) {
+        const u32x4_t w = {pack_bf16x2(sc[n][t][0], sc[n][t][1]), pack_bf16x2(sc[n][t][2], sc[n][t][3]),
+                           pack_bf16x2(sc[n][t + 1][0], sc[n][t + 1][1]), pack_bf16x2(sc[n][t + 1][2], sc[n][t + 1][3])};
+        pb[n] = __builtin_bit_cast(bf16x8_t, w);
+        lsum[n] = mfma_bf16(ones, pb[n], lsum[n]);
       }
 #pragma unroll
       for (int c = 0; c < C::kCTiles; ++c) {
-        const __bf16* vrow = &vt_lds[(16 * c + col) * C::kVPitch];
+        const __bf16* vrow = &vl[(16 * c + col) * C::kVPitch];
         const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * t + 4 * grp);
         const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * (t + 1) + 4 * grp);
         const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[c] = mfma_bf16(a, pb, o[c]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) o[n][c] = mfma_bf16(a, pb[n], o[n][c]);
       }
     }
+    // the other buffer was last read in the previous block, before the barrier that ended it
+    if (more) store_block(buf ^ 1);
+    __syncthreads();
   }
 
-  // ---- output: lane (query col, grp) holds channels 16c + 4grp .. +3 of its query
-  float lt = l + __shfl_xor(l, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  if (qi < chunk) {
-    const float inv = 1.0f / lt;
-    uint16_t* orow = p.out + ((q_begin + qi) * p.num_q_heads + h) * D;
+  // ---- output: lane (query col, grp) of tile n holds channels 16c + 4grp .. +3 of its query
 #pragma unroll
-    for (int c = 0; c < C::kCTiles; ++c) {
-      const uint2 v = make_uint2(pack_bf16x2(o[c][0] * inv, o[c][1] * inv), pack_bf16x2(o[c][2] * inv, o[c][3] * inv));
-      *reinterpret_cast<uint2*>(orow + 16 * c + 4 * grp) = v;
+  for (int n = 0; n < NT; ++n) {
+    const float lt = lsum[n][0];
+    const int qi = qw + 16 * (n / C::kHPW) + col;
+    if (qi < chunk) {
+      const float inv = 1.0f / lt;
+      uint16_t* orow = p.out + ((q_begin + qi) * p.num_q_heads + h0 + n % C::kHPW) * D;
+#pragma unroll
+      for (int c = 0; c < C::kCTiles; ++c) {
+        const uint2 v = make_uint2(pack_bf16x2(o[n][c][0] * inv, o[n][c][1] * inv),
+                                   pack_bf16x2(o[n][c][2] * inv, o[n][c][3] * inv));
+        *reinterpret_cast<uint2*>(orow + 16 * c + 4 * grp) = v;
+      }
     }
   }
 }
@@ -175,9 +322,11 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
 template <int D, int G>
 hipError_t launch_ext(const ExtendParams& p, hipStream_t s) {
   using C = ExtCfg<D, G>;
-  const dim3 grid((unsigned)((p.max_chunk + C::kQPerGroup - 1) / C::kQPerGroup), (unsigned)p.num_kv_heads,
-                  (unsigned)p.batch);
-  hipLaunchKernelGGL((extend_attn_kernel<D, G>), grid, dim3(64 * C::kWaves), 0, s, p);
+  const int64_t nqb = (p.max_chunk + C::kQPerGroup - 1) / C::kQPerGroup;
+  const int64_t tiles = nqb * p.num_kv_heads * p.batch;
+  // grid size, and a 64-row block's byte extent for its buffer descriptor
+  if (tiles > INT32_MAX || (int64_t)p.num_kv_heads * D * 2 * kKB > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((extend_attn_kernel<D, G>), dim3((unsigned)tiles), dim3(64 * C::kWaves), 0, s, p, (int)nqb);
   return hipGetLastError();
 }
 

@@ -410,6 +410,39 @@ def test_extend_attention_over_workspace(nk, G, Hkv, d, P):
     check_out(out, ref, mass, f"extend G{G} d{d}")
 
 
+@pytest.mark.parametrize("G,d,sm_sign", [(4, 128, 1.0), (2, 64, -1.0), (16, 128, -1.0), (1, 128, 1.0)])
+def test_extend_attention_long_prefix(nk, G, d, sm_sign):
+    """Prefixes spanning many 64-key blocks and chunks spanning several query
+    blocks of one KV head, with key magnitudes that grow along each sequence so
+    that the running max of most queries rises many times over the keys; a
+    negative logit scale included. The workspace is filled directly; against
+    the oracle."""
+    rng = np.random.default_rng(7)
+    Hkv = 2
+    Hq = G * Hkv
+    prefix = np.array([700, 0, 1290], np.int32)
+    chunk = np.array([150, 203, 75], np.int32)
+    B = len(prefix)
+    say(f"case extend long prefix: G {G} d {d} sm sign {sm_sign:+.0f}")
+    ws_offs = np.zeros(B + 1, np.int64)
+    ws_offs[1:] = np.cumsum(prefix + chunk)
+    rows = int(ws_offs[-1])
+    gain = np.concatenate([0.5 + 5.5 * np.arange(n) / n for n in prefix + chunk])
+    kx = rng.standard_normal((rows, Hkv, d)) * gain[:, None, None]
+    kb = synth.f32_to_bf16_bits(kx.astype(np.float32))
+    vb = synth.host_values(rng, (rows, Hkv, d))
+    q_offs = np.zeros(B + 1, np.int64)
+    q_offs[1:] = np.cumsum(chunk)
+    qb = synth.host_values(rng, (int(chunk.sum()), Hq, d))
+    sm = sm_sign / math.sqrt(d)
+    out = nk.nvfp4_extend_attn(synth.to_device_bf16(qb), synth.to_device(q_offs), synth.to_device_bf16(kb),
+                               synth.to_device_bf16(vb), synth.to_device(ws_offs), synth.to_device(prefix), sm)
+    torch.cuda.synchronize()
+    ref, mass = oatt.extend_attention(synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb),
+                                      synth.bf16_bits_to_f64(vb), q_offs, ws_offs, prefix, sm)
+    check_out(out, ref, mass, f"extend long G{G} d{d} sm{sm:+.3f}")
+
+
 # ---------------------------------------------------------------------------
 # decode attention
 # ---------------------------------------------------------------------------
