@@ -10,15 +10,14 @@
 //
 // The kernel is write-bound: per 8 channels it reads 4 bytes (plus a shared
 // scale byte) and writes 16 bytes, for each of K and V. Grid: (row groups,
-// sequence). Each wave owns two workspace rows (one token of one sequence,
-// all KV heads): the sequence comes from the grid and the page from one
-// scalar block-table load per row, so nothing is searched. Lane i handles
-// 8-channel half-block i of the row, so every 128-bit store instruction
-// writes 1 KB of contiguous bf16 (whole cache lines); all of a wave's loads
-// are issued before its conversions and stores. Stores are non-temporal: the
-// workspace (gigabytes) is written once. Measured on MI355X (agentic
-// workload, 1.7 GB written): 361 us, against 787 us for one lane per 16-channel
-// block with half-line stores.
+// sequence). Each wave owns one (bf16) or two (FP8) workspace rows (a row is
+// one token of one sequence, all KV heads): the sequence comes from the grid
+// and the page from one scalar block-table load per row, so nothing is
+// searched. Lane i handles 8-channel half-block i of the row, so every 128-bit
+// store instruction writes 1 KB of contiguous bf16 (whole cache lines); all of
+// a wave's loads (its rows, two 64-lane chunks of each) are issued before its
+// conversions and stores. Stores are non-temporal: the workspace (gigabytes)
+// is written once.
 #include "common.hpp"
 
 namespace nvfp4kv {
@@ -26,7 +25,12 @@ namespace nvfp4kv {
 namespace {
 
 constexpr int kWsWaves = 8;          // waves per workgroup
-constexpr int kWsRowsPerWave = 2;    // rows handled by one wave
+constexpr int kChunks = 2;           // 64-lane chunks of a row whose loads are issued together
+
+// rows handled by one wave (measured on the agentic workload: bf16 one row,
+// FP8 two rows)
+template <bool FP8OUT>
+constexpr int rows_per_wave() { return FP8OUT ? 2 : 1; }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -42,57 +46,64 @@ __global__ __launch_bounds__(64 * kWsWaves) void nvfp4_dequant_ws_kernel(Workspa
   const int prefix = __builtin_amdgcn_readfirstlane(p.prefix_lens[b]);
   const int64_t row0 = p.row_offsets[b];
   const int P = p.page_size;
+  constexpr int kWsRowsPerWave = rows_per_wave<FP8OUT>();
   const int t_first = (blockIdx.x * kWsWaves + wave) * kWsRowsPerWave;
   if (t_first >= prefix) return;
   const int32_t* bt = p.block_tables + (int64_t)b * p.max_pages;
 
-  for (int i0 = 0; i0 < items; i0 += 64) {
-    const int i = i0 + lane;
-    const bool on = i < items;
-    const int hb = on ? i >> 1 : 0, half = i & 1;
-    const int h = hb / nb, blk = hb % nb;
-    uint32_t w[kWsRowsPerWave][2], sb[kWsRowsPerWave][2];
+  // every load of the wave's rows and chunks is issued before any conversion or store
+  for (int i0 = 0; i0 < items; i0 += 64 * kChunks) {
+    uint32_t w[kWsRowsPerWave][kChunks][2], sb[kWsRowsPerWave][kChunks][2];
 #pragma unroll
     for (int r = 0; r < kWsRowsPerWave; ++r) {
       const int t = t_first + r;
-      if (t < prefix && on) {
-        const int32_t page = min(max(__builtin_amdgcn_readfirstlane(bt[t / P]), 0), p.num_pages - 1);
-        const int64_t src_row = ((int64_t)page * p.num_kv_heads + h) * P + t % P;
+      const int32_t page = t < prefix ? min(max(__builtin_amdgcn_readfirstlane(bt[t / P]), 0), p.num_pages - 1) : 0;
 #pragma unroll
-        for (int which = 0; which < 2; ++which) {
-          w[r][which] = *reinterpret_cast<const uint32_t*>(p.data[which] + src_row * (p.head_dim / 2) + blk * 8 +
-                                                           half * 4);
-          sb[r][which] = p.scale[which][src_row * nb + blk];
+      for (int j = 0; j < kChunks; ++j) {
+        const int i = i0 + 64 * j + lane;
+        const int hb = i >> 1, half = i & 1;
+        const int h = hb / nb, blk = hb % nb;
+        if (t < prefix && i < items) {
+          const int64_t src_row = ((int64_t)page * p.num_kv_heads + h) * P + t % P;
+#pragma unroll
+          for (int which = 0; which < 2; ++which) {
+            w[r][j][which] = *reinterpret_cast<const uint32_t*>(p.data[which] + src_row * (p.head_dim / 2) + blk * 8 + half * 4);
+            sb[r][j][which] = p.scale[which][src_row * nb + blk];
+          }
         }
       }
     }
 #pragma unroll
     for (int r = 0; r < kWsRowsPerWave; ++r) {
       const int t = t_first + r;
-      if (t < prefix && on) {
-        const int64_t dst_row = (row0 + t) * p.num_kv_heads * p.head_dim;
 #pragma unroll
-        for (int which = 0; which < 2; ++which) {
-          const float s = e4m3_to_f32(sb[r][which]) * p.gscale[which];
-          float f[8];
-          fp4x8_to_f32(w[r][which], f);
-          const int64_t e0 = dst_row + h * p.head_dim + blk * kBlock + half * 8;   // first element
-          if constexpr (FP8OUT) {
-            // FP8 workspace (the pages' type): byte = E4M3(fl32(e2m1 * S * gs) / ws_scale); lossy
-            const float ws = p.ws_scale[which];
-            float y[8];
+      for (int j = 0; j < kChunks; ++j) {
+        const int i = i0 + 64 * j + lane;
+        if (t < prefix && i < items) {
+          const int64_t e0 = (row0 + t) * p.num_kv_heads * p.head_dim + (int64_t)i * 8;   // first element
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = f[e] * s;
-            if (ws != 1.0f) {      // correctly rounded division only where the scale needs it
+          for (int which = 0; which < 2; ++which) {
+            // block scale: the E4M3 byte decoded by the conversion instruction (exact)
+            const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb[r][j][which], 1.0f, false)[0] * p.gscale[which];
+            float f[8];
+            fp4x8_to_f32(w[r][j][which], f);
+            if constexpr (FP8OUT) {
+              // FP8 workspace (the pages' type): byte = E4M3(fl32(e2m1 * S * gs) / ws_scale); lossy
+              const float ws = p.ws_scale[which];
+              float y[8];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) y[e] = y[e] / ws;
+              for (int e = 0; e < 8; ++e) y[e] = f[e] * s;
+              if (ws != 1.0f) {      // correctly rounded division only where the scale needs it
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = y[e] / ws;
+              }
+              const u32x2 v = {f32x4_to_fp8(y[0], y[1], y[2], y[3]), f32x4_to_fp8(y[4], y[5], y[6], y[7])};
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.ws[which]) + e0));
+            } else {
+              const u32x4 v = {pack_bf16x2(f[0] * s, f[1] * s), pack_bf16x2(f[2] * s, f[3] * s),
+                               pack_bf16x2(f[4] * s, f[5] * s), pack_bf16x2(f[6] * s, f[7] * s)};
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.ws[which]) + e0));
             }
-            const u32x2 v = {f32x4_to_fp8(y[0], y[1], y[2], y[3]), f32x4_to_fp8(y[4], y[5], y[6], y[7])};
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.ws[which]) + e0));
-          } else {
-            const u32x4 v = {pack_bf16x2(f[0] * s, f[1] * s), pack_bf16x2(f[2] * s, f[3] * s),
-                             pack_bf16x2(f[4] * s, f[5] * s), pack_bf16x2(f[6] * s, f[7] * s)};
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.ws[which]) + e0));
           }
         }
       }
@@ -104,10 +115,15 @@ __global__ __launch_bounds__(64 * kWsWaves) void nvfp4_dequant_ws_kernel(Workspa
 
 hipError_t launch_nvfp4_dequant_ws(const WorkspaceParams& p, hipStream_t s) {
   const int64_t max_rows = (int64_t)p.max_pages * p.page_size;
-  const int64_t per_block = (int64_t)kWsWaves * kWsRowsPerWave;
-  dim3 grid((unsigned)((max_rows + per_block - 1) / per_block), (unsigned)p.batch);
-  if (p.out_fp8) hipLaunchKernelGGL(nvfp4_dequant_ws_kernel<true>, grid, dim3(64 * kWsWaves), 0, s, p);
-  else hipLaunchKernelGGL(nvfp4_dequant_ws_kernel<false>, grid, dim3(64 * kWsWaves), 0, s, p);
+  if (p.out_fp8) {
+    const int64_t per_block = (int64_t)kWsWaves * rows_per_wave<true>();
+    dim3 grid((unsigned)((max_rows + per_block - 1) / per_block), (unsigned)p.batch);
+    hipLaunchKernelGGL(nvfp4_dequant_ws_kernel<true>, grid, dim3(64 * kWsWaves), 0, s, p);
+  } else {
+    const int64_t per_block = (int64_t)kWsWaves * rows_per_wave<false>();
+    dim3 grid((unsigned)((max_rows + per_block - 1) / per_block), (unsigned)p.batch);
+    hipLaunchKernelGGL(nvfp4_dequant_ws_kernel<false>, grid, dim3(64 * kWsWaves), 0, s, p);
+  }
   return hipGetLastError();
 }
 

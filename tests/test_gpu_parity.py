@@ -284,6 +284,65 @@ def test_dequant_workspace_agentic_small(nk, shape):
     assert np.array_equal(synth.bf16_tensor_bits(vws), vref)
 
 
+@pytest.mark.parametrize("fp8_ws", [False, True])
+def test_dequant_workspace_every_scale_byte(nk, fp8_ws):
+    """Pools written directly with every finite E4M3 scale byte (both signs,
+    subnormals included) against random data bytes (every nibble), read back
+    through the page table into the bf16 or the FP8 workspace; bit-exact
+    against the oracle."""
+    rng = np.random.default_rng(23)
+    H, P, d, pages = 2, 16, 128, 40
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    say(f"case workspace every scale byte: fp8 {fp8_ws}")
+    pools, ref_bytes = [], []
+    for _ in range(2):
+        data = rng.integers(0, 256, size=(pages, H, P, d // 2)).astype(np.uint8)
+        scale = np.resize(rng.permutation(finite), pages * H * P * (d // 16)).reshape(pages, H, P, d // 16)
+        pool = nk.NVFP4Pool.empty(pages, H, P, d)
+        pool.data.copy_(torch.from_numpy(data))
+        pool.scale.copy_(torch.from_numpy(scale))
+        pools.append(pool)
+        ref_bytes.append((data, scale))
+    B = 3
+    prefix = np.array([pages * P // 2, 37, pages * P // 2 - 37], np.int32)
+    bt = rng.permutation(pages).astype(np.int32)
+    tables = np.zeros((B, pages), np.int32)
+    tables[0, :pages // 2] = bt[:pages // 2]
+    tables[1, :3] = bt[pages // 2:pages // 2 + 3]
+    tables[2, :pages // 2] = bt[pages // 2:]
+    offs = np.zeros(B + 1, np.int64)
+    offs[1:] = np.cumsum(prefix + 5)
+    rows = int(offs[-1])
+    if fp8_ws:
+        kws = torch.full((rows, H, d), 0xA5, dtype=torch.uint8, device="cuda")
+        vws = torch.full((rows, H, d), 0xA5, dtype=torch.uint8, device="cuda")
+        nk.nvfp4_kv_dequant_workspace_fp8(pools[0], pools[1], synth.to_device(tables), synth.to_device(prefix),
+                                          synth.to_device(offs), kws, vws)
+    else:
+        kws = torch.full((rows, H, d), -7.0, dtype=torch.bfloat16, device="cuda")
+        vws = torch.full((rows, H, d), -7.0, dtype=torch.bfloat16, device="cuda")
+        nk.nvfp4_kv_dequant_workspace(pools[0], pools[1], synth.to_device(tables), synth.to_device(prefix),
+                                      synth.to_device(offs), kws, vws)
+    torch.cuda.synchronize()
+    for ws_t, (data, scale) in ((kws, ref_bytes[0]), (vws, ref_bytes[1])):
+        if fp8_ws:
+            cache = onv.workspace_fp8_bytes(data, scale, 1.0, 1.0)
+            ref = np.full((rows, H, d), 0xA5, np.uint8)
+            got = ws_t.cpu().numpy()
+        else:
+            cache = onv.workspace_bits(data, scale, 1.0)
+            ref = np.full((rows, H, d), int(synth.bf16_tensor_bits(torch.tensor([-7.0], dtype=torch.bfloat16))[0]),
+                          np.uint16)
+            got = synth.bf16_tensor_bits(ws_t)
+        for b in range(B):
+            n, off = int(prefix[b]), int(offs[b])
+            ref[off:off + n] = oatt.gather_tokens(cache, tables[b], n)
+        if not np.array_equal(got, ref):
+            bad = np.argwhere(got != ref)
+            i = tuple(bad[0])
+            raise AssertionError(f"{len(bad)} workspace elements differ; first at {i}: gpu {got[i]:#x} oracle {ref[i]:#x}")
+
+
 def _fp8_bytes(rng, shape):
     """Random FP8-E4M3 bytes over the whole finite range (NaN bytes replaced)."""
     b = rng.integers(0, 256, size=shape).astype(np.uint8)
