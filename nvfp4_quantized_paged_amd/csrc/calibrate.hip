@@ -12,9 +12,10 @@
 // a running maximum in device memory. Grid-stride over token rows; threads
 // take 16-byte pieces of a row, so every load instruction reads contiguous
 // row bytes, with eight independent loads in flight per thread; one atomic
-// per workgroup (same-address atomics serialise, so the grid is small). Non-negative floats order like
-// their bit patterns, so the fold is an integer atomic max on the bits.
-// NaN inputs are ignored (fmaxf), like the block-scale amax of the encoder.
+// per workgroup (same-address atomics serialise, so the grid is small).
+// Non-negative floats order like their bit patterns, so both the per-thread
+// maximum (with NaN patterns skipped, like the block maximum of the encoder)
+// and the fold into memory are integer maxima on the bits.
 #include "common.hpp"
 
 namespace nvfp4kv {
@@ -25,12 +26,18 @@ constexpr int kAbsmaxThreads = 256;
 constexpr int kAbsmaxMaxGroups = 512;       // one atomic per workgroup: few workgroups, each with more loads in flight
 constexpr int kAbsmaxUnroll = 8;             // independent 16-byte loads in flight per thread
 
-__device__ inline float absmax8(uint4 w, float m) {
+// Running maximum of bf16 magnitude bit patterns over eight elements, NaN
+// patterns (above 0x7F80) ignored. Non-negative floats order like their bit
+// patterns, so this is the float maximum without NaN semantics: an IEEE
+// maximum of a signalling NaN is a quiet NaN, which would drop the running
+// value.
+__device__ inline uint32_t absmax8(uint4 w, uint32_t m) {
   const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    m = fmaxf(m, fabsf(__uint_as_float(ww[e] << 16)));
-    m = fmaxf(m, fabsf(__uint_as_float(ww[e] & 0xFFFF0000u)));
+    const uint32_t lo = ww[e] & 0x7FFFu, hi = (ww[e] >> 16) & 0x7FFFu;
+    m = max(m, lo > 0x7F80u ? 0u : lo);
+    m = max(m, hi > 0x7F80u ? 0u : hi);
   }
   return m;
 }
@@ -41,7 +48,7 @@ __global__ __launch_bounds__(kAbsmaxThreads) void absmax_kernel(const uint16_t* 
                                                                int32_t num_tokens, int32_t row_chunks,
                                                                uint32_t* amax_bits) {
   __shared__ float red[kAbsmaxThreads / 64];
-  float m = 0.0f;
+  uint32_t mb = 0;                                   // bf16 magnitude pattern
   if (row_chunks <= kAbsmaxThreads) {
     const int tpp = kAbsmaxThreads / row_chunks;
     const int lt = threadIdx.x / row_chunks, c = threadIdx.x % row_chunks;
@@ -55,16 +62,16 @@ __global__ __launch_bounds__(kAbsmaxThreads) void absmax_kernel(const uint16_t* 
           w[k] = t < num_tokens ? reinterpret_cast<const uint4*>(x + t * stride)[c] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int k = 0; k < kAbsmaxUnroll; ++k) m = absmax8(w[k], m);
+        for (int k = 0; k < kAbsmaxUnroll; ++k) mb = absmax8(w[k], mb);
       }
     }
   } else {
     for (int64_t t = blockIdx.x; t < num_tokens; t += gridDim.x) {
       const uint4* row = reinterpret_cast<const uint4*>(x + t * stride);
-      for (int c = threadIdx.x; c < row_chunks; c += kAbsmaxThreads) m = absmax8(row[c], m);
+      for (int c = threadIdx.x; c < row_chunks; c += kAbsmaxThreads) mb = absmax8(row[c], mb);
     }
   }
-  m = wave_max(m);
+  float m = wave_max(__uint_as_float(mb << 16));   // no NaN left
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {

@@ -8,10 +8,22 @@
 //
 // One lane encodes one 16-channel block of one (token, head): it reads 32
 // bytes of bf16 with two 128-bit loads and writes 8 packed bytes plus one
-// scale byte. The element codes come from exact threshold compares: with
-// block scale S (E4M3) and tensor scale gs, the E2M1 midpoints m*S*gs are
-// exact fp32 products, so "a > m*S*gs" (or ">=" where the tie goes up to an
-// even code) is the round-to-nearest-even decision with no division.
+// scale byte. The element codes follow the FP32 recipe: with block scale S
+// (E4M3) and tensor scale gs, |x| is compared with fl32(m * fl32(S*gs)) for
+// the E2M1 midpoints m ("a > t", or ">=" where the tie goes up to an even
+// code). For a power-of-two gs (and source values of at most 8 significant
+// bits: bf16, or FP8 times a power-of-two scale) the thresholds are exact
+// products with at most 7 significant bits, so any |x| that is not on one is
+// at least 2^-9 (relative) away from it, and the quotient q = |x| / (S*gs)
+// decides the same way: one reciprocal multiply plus one FMA correction step
+// gives q exactly where it is a midpoint and within a few ulps elsewhere, and
+// the gfx950 conversion instruction rounds q to E2M1 (nearest even,
+// saturating), two elements per instruction. That path is checked against the
+// threshold definition for every finite bf16 value of both signs and every
+// E4M3 scale; blocks with non-finite elements, or whose quotients could
+// overflow, take the compares.
+#include <cmath>
+
 #include "common.hpp"
 
 namespace nvfp4kv {
@@ -42,6 +54,48 @@ __device__ inline uint32_t e2m1_code(float a, const float t[7]) {
   c += a >= t[5];
   c += a > t[6];
   return c;
+}
+
+// Codes of a block by the threshold compares (any scale, any finite or
+// non-finite element): packed nibbles, element 2i in the low nibble of byte i.
+__device__ inline void encode_compare(const float x[16], float sg, uint32_t& lo, uint32_t& hi) {
+  const float t7[7] = {0.25f * sg, 0.75f * sg, 1.25f * sg, 1.75f * sg,
+                       2.5f * sg, 3.5f * sg, 5.0f * sg};
+  // S = 0 (an all-zero block): every magnitude code is 0; computed without a branch
+  const uint32_t keep = sg > 0.0f ? 7u : 0u;
+  lo = 0;
+  hi = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t sign = (__float_as_uint(x[e]) >> 31) << 3;
+    const uint32_t nib = sign | (e2m1_code(fabsf(x[e]), t7) & keep);
+    if (e < 8) lo |= nib << (4 * e);
+    else hi |= nib << (4 * (e - 8));
+  }
+}
+
+// Codes of a block from the quotients (power-of-two scale, finite elements,
+// r = 1 / sg correctly rounded, or 0 for sg = 0): q0 = |x| r, then one
+// correction q1 = q0 + r (|x| - q0 sg) with both steps fused, the sign of x
+// copied onto q1 (so -0 and negatives that round to 0 keep it), and the
+// conversion instruction packs two codes per byte.
+__device__ inline void encode_quotient(const float x[16], float sg, float r, uint32_t& lo, uint32_t& hi) {
+  float q[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float a = fabsf(x[e]);
+    const float q0 = a * r;
+    const float q1 = fmaf(fmaf(-q0, sg, a), r, q0);
+    q[e] = copysignf(q1, x[e]);
+  }
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[2], q[3], 1.0f, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[4], q[5], 1.0f, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, q[6], q[7], 1.0f, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[8], q[9], 1.0f, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[10], q[11], 1.0f, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[12], q[13], 1.0f, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, q[14], q[15], 1.0f, 3);
 }
 
 // Page and in-page position of a slot (a shift and a mask for power-of-two pages).
@@ -103,7 +157,7 @@ __device__ inline void load_source_block(const QuantizeParams& p, int which, int
   }
 }
 
-template <int D, bool FP8SRC>
+template <int D, bool FP8SRC, bool QUOT>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void nvfp4_quantize_kernel(QuantizeParams p) {
   constexpr int nb = D / kBlock;                 // blocks per head row
   constexpr int kTokPerPass = 64 / nb;
@@ -119,24 +173,38 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void nvfp4_quantize_kernel(Qua
     const int64_t slot = p.slot_mapping[t];
     if (slot < 0 || slot >= p.num_slots) continue;
 
-    float amax = 0.0f;
+    // Block maximum on the magnitude bit patterns (non-negative floats order like
+    // integers): without NaN elements it is the float maximum exactly; NaN elements
+    // (patterns above 0x7F800000) are ignored in a second pass. A float max chain
+    // would not do: an IEEE maximum of a signalling NaN is a quiet NaN, which drops
+    // everything accumulated before it.
+    uint32_t bmax = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    for (int e = 0; e < 16; ++e) bmax = max(bmax, __float_as_uint(x[e]) & 0x7FFFFFFFu);
+    float amax = __uint_as_float(bmax);
+    if (bmax > 0x7F800000u) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t b = __float_as_uint(x[e]) & 0x7FFFFFFFu;
+        m = max(m, b > 0x7F800000u ? 0u : b);
+      }
+      amax = __uint_as_float(m);
+    }
     const float gs = p.gscale[which];
     const uint32_t sbyte = e4m3_encode_nonneg(amax / (6.0f * gs));
-    const float sg = e4m3_to_f32(sbyte) * gs;
-    const float t7[7] = {0.25f * sg, 0.75f * sg, 1.25f * sg, 1.75f * sg,
-                         2.5f * sg, 3.5f * sg, 5.0f * sg};
-    // S = 0 (an all-zero block): every magnitude code is 0; computed without a branch
-    const uint32_t keep = sg > 0.0f ? 7u : 0u;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t sign = (__float_as_uint(x[e]) >> 31) << 3;
-      const uint32_t nib = sign | (e2m1_code(fabsf(x[e]), t7) & keep);
-      if (e < 8) lo |= nib << (4 * e);
-      else hi |= nib << (4 * (e - 8));
+    // the scale byte decoded by the conversion instruction (exact for every E4M3 byte)
+    const float sg = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sbyte, 1.0f, false)[0] * gs;
+    uint32_t lo, hi;
+    bool done = false;
+    if constexpr (QUOT) {
+      const float r = sg > 0.0f ? 1.0f / sg : 0.0f;
+      if (bmax < 0x7F800000u && amax * r < 0x1p64f) {
+        encode_quotient(x, sg, r, lo, hi);
+        done = true;
+      }
     }
+    if (!done) encode_compare(x, sg, lo, hi);
     int64_t page, off;
     slot_position(p, slot, page, off);
     const int64_t row = (page * p.num_kv_heads + h) * p.page_size + off;
@@ -179,17 +247,35 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void fp8_quantize_kernel(Quant
 
 }  // namespace
 
+namespace {
+
+bool pow2_in_range(float s) {
+  int e;
+  return s > 0.0f && std::frexp(s, &e) == 0.5f && e >= -32 && e <= 33;
+}
+
+template <int D, bool FP8SRC>
+void launch_nvfp4_d(const QuantizeParams& p, dim3 grid, dim3 block, hipStream_t s) {
+  // quotient codes: power-of-two tensor scales and sources of at most 8 significant bits
+  const bool quot = pow2_in_range(p.gscale[0]) && pow2_in_range(p.gscale[1]) &&
+                    (!FP8SRC || (pow2_in_range(p.src_scale[0]) && pow2_in_range(p.src_scale[1])));
+  if (quot) hipLaunchKernelGGL((nvfp4_quantize_kernel<D, FP8SRC, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((nvfp4_quantize_kernel<D, FP8SRC, false>), grid, block, 0, s, p);
+}
+
+}  // namespace
+
 hipError_t launch_nvfp4_quantize(const QuantizeParams& p, hipStream_t s) {
   if (p.num_tokens == 0) return hipSuccess;
   const int64_t per_group = kTokPerWave * kWavesPerGroup;
   const dim3 grid((unsigned)((p.num_tokens + per_group - 1) / per_group), (unsigned)p.num_kv_heads, 2);
   const dim3 block(64 * kWavesPerGroup);
   if (p.head_dim == 64) {
-    if (p.src_fp8) hipLaunchKernelGGL((nvfp4_quantize_kernel<64, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((nvfp4_quantize_kernel<64, false>), grid, block, 0, s, p);
+    if (p.src_fp8) launch_nvfp4_d<64, true>(p, grid, block, s);
+    else launch_nvfp4_d<64, false>(p, grid, block, s);
   } else {
-    if (p.src_fp8) hipLaunchKernelGGL((nvfp4_quantize_kernel<128, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((nvfp4_quantize_kernel<128, false>), grid, block, 0, s, p);
+    if (p.src_fp8) launch_nvfp4_d<128, true>(p, grid, block, s);
+    else launch_nvfp4_d<128, false>(p, grid, block, s);
   }
   return hipGetLastError();
 }

@@ -194,6 +194,34 @@ def test_quantize_crafted_values_and_skipped_slots(nk, gs):
         assert_pool_equal(t, r, n)
 
 
+@pytest.mark.parametrize("gs", [1.0, GS_THIRD])
+def test_quantize_non_finite_elements(nk, gs):
+    """NaN (either sign) and +-inf elements among finite ones, against the FP32
+    recipe (the documented arithmetic; at a power-of-two gs it equals the exact
+    encode on finite inputs, which has no code for NaN): NaN is ignored by the
+    block maximum and gets magnitude 0 with its sign bit, inf saturates the
+    scale and its own code, the other elements of such blocks are encoded
+    normally. Blocks without them take the quotient path at a power-of-two gs."""
+    rng = np.random.default_rng(29)
+    T, H, P, d, pages = 64, 2, 16, 128, 4
+    say(f"case quantize non-finite: gs {gs}")
+    bits = synth.host_values(rng, (T, H, d))
+    flat = bits.reshape(-1)
+    pos = rng.permutation(flat.size)[:300]
+    specials = np.array([0x7FC0, 0xFFC0, 0x7F81, 0x7F80, 0xFF80], np.uint16)   # NaNs, +inf, -inf
+    flat[pos] = specials[rng.integers(0, specials.size, pos.size)]
+    slots = rng.permutation(pages * P)[:T].astype(np.int64)
+    kp, _ = gpu_quantize_nv(nk, pages, H, P, d, bits, bits, slots, gs)
+    with np.errstate(invalid="ignore", over="ignore"):
+        codes, s = onv.encode_blocks_fp32(onv.bf16_to_f64(bits).reshape(T, H, d // 16, 16), gs)
+    data = onv.pack_nibbles(codes.reshape(T, H, d))
+    kd, ks = onv.empty_cache(pages, H, P, d, fill=SENT)
+    kd[slots // P, :, slots % P] = data
+    ks[slots // P, :, slots % P] = s
+    assert_pool_equal(kp.data, kd, "K data")
+    assert_pool_equal(kp.scale, ks, "K scale")
+
+
 def test_quantize_golden_blocks(nk):
     import os
     path = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_block_vectors.txt")
@@ -564,7 +592,7 @@ def test_decode_global_scale(nk, gs):
 @pytest.mark.parametrize("mag", [3.0e4, 1.0e-5])
 def test_calibrated_global_scale_end_to_end(nk, mag):
     """Calibration on the GPU: the absmax kernel folds two chunks (one with a
-    strided source and a NaN, which is ignored) into a running maximum; the
+    strided source and quiet and signalling NaNs, which are ignored) into a running maximum; the
     global scale derived from it keeps a tensor far outside the E4M3 range
     quantizable; bytes bit-exact against the oracle's FP32 recipe, decode
     within tolerance."""
@@ -583,6 +611,8 @@ def test_calibrated_global_scale_end_to_end(nk, mag):
         t = synth.to_device_bf16(wide)[:, :x.shape[1]]
         rest = x[half:].copy()
         rest[3, 0, 7] = 0x7FC0                                           # NaN inside: ignored
+        snan = np.random.default_rng(31 + i).permutation(rest.size)[:24]
+        rest.reshape(-1)[snan] = np.where(np.arange(24) % 2 == 0, 0x7F81, 0xFF81)   # signalling NaNs too
         nk.nvfp4_kv_absmax(t, amax[i:i + 1])
         nk.nvfp4_kv_absmax(synth.to_device_bf16(rest), amax[i:i + 1])
         refs.append(max(np.abs(synth.bf16_bits_to_f64(x[:half])).max(), np.nanmax(np.abs(synth.bf16_bits_to_f64(rest)))))
