@@ -222,6 +222,48 @@ def test_quantize_non_finite_elements(nk, gs):
     assert_pool_equal(kp.scale, ks, "K scale")
 
 
+@pytest.mark.parametrize("gs", [1.0, 0.125])
+def test_quantize_every_value_under_every_scale(nk, gs):
+    """Every E4M3 block scale S (0x01..0x7E) with every finite bf16 magnitude up
+    to 6*S*gs, both signs: each block holds an anchor 6*S*gs (which fixes the
+    scale byte) and 15 of the values; about 4.3M elements through the library's
+    quantize, bit-exact against the oracle."""
+    rng = np.random.default_rng(37)
+    pos = np.arange(1, 0x7F80, dtype=np.uint32)
+    mags = synth.bf16_bits_to_f64(pos.astype(np.uint16))
+    blocks = []
+    for b in range(1, 0x7F):
+        s = float(onv.E4M3_VALUES[b]) * gs
+        vals = pos[mags <= 6.0 * s].astype(np.uint16)
+        vals = np.concatenate([vals, vals | 0x8000])
+        vals = rng.permutation(vals)
+        n = -(-vals.size // 15)
+        vals = np.resize(vals, n * 15).reshape(n, 15)
+        anc = synth.f32_to_bf16_bits(np.array([6.0 * s], np.float32))[0]
+        blk = np.empty((n, 16), np.uint16)
+        blk[:, :15] = vals
+        blk[:, 15] = anc
+        idx, k = np.arange(n), np.arange(n) % 16                   # the anchor at a varying position
+        moved = blk[idx, k].copy()
+        blk[idx, k] = anc
+        blk[:, 15] = np.where(k == 15, anc, moved)
+        blocks.append(blk)
+    blocks = np.concatenate(blocks)
+    d = 128
+    T = -(-blocks.shape[0] // (d // 16))
+    rows = np.zeros((T * (d // 16), 16), np.uint16)
+    rows[:blocks.shape[0]] = blocks
+    bits = rows.reshape(T, 1, d)
+    P = 16
+    pages = -(-T // P)
+    say(f"case quantize every value under every scale: gs {gs}, {blocks.shape[0]} blocks, {T} tokens")
+    slots = rng.permutation(pages * P)[:T].astype(np.int64)
+    kp, _ = gpu_quantize_nv(nk, pages, 1, P, d, bits, bits, slots, gs)
+    kd, ks, _, _ = oracle_nv(pages, 1, P, d, bits, bits, slots, gs)
+    assert_pool_equal(kp.scale, ks, "K scale")
+    assert_pool_equal(kp.data, kd, "K data")
+
+
 def test_quantize_golden_blocks(nk):
     import os
     path = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_block_vectors.txt")
