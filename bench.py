@@ -14,7 +14,10 @@ before timing. Prints ONE JSON line on stdout; diagnostics go to stderr.
 
   value           KV GB/s of the step: (packed + scale bytes) / step time
   roofline        dominant kernel (decode partial): algorithmic bytes per
-                  launch / mean launch time (HIP events on the launch stream)
+                  launch / mean launch time (HIP events on the launch stream);
+                  also as a fraction of the measured read bandwidth
+  hbm_read_probe  read bandwidth of the library's plain streaming-read kernel
+                  over 4 GiB (best of a few launch shapes)
   cpu_baseline    the CPU oracle (dequantize + fp64 attention) on a bounded
                   sample of (sequence, KV head) slices of the same workload
   fp8, extreme_context_1m, agentic_prefix_reuse
@@ -397,6 +400,34 @@ def cpu_baseline(wl, budget_s=12.0):
     }
 
 
+def read_probe(nk, reps=10):
+    """Achievable HBM read bandwidth: the library's streaming-read kernel over a 4 GiB buffer (far
+    beyond the 256 MB last-level cache), a few launch shapes, HIP events; the best one."""
+    import torch
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    runs = []
+    for flags in (nk.PROBE_NONTEMPORAL, 0, nk.PROBE_NONTEMPORAL | nk.PROBE_RANGE, nk.PROBE_RANGE):
+        for per_cu in (4, 8, 16, 32):
+            blocks = 256 * per_cu
+            for _ in range(2):
+                nk.hbm_read_probe(buf, blocks, flags, sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                nk.hbm_read_probe(buf, blocks, flags, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps / 1e3
+            runs.append({"nontemporal": bool(flags & nk.PROBE_NONTEMPORAL), "range_per_workgroup": bool(flags & nk.PROBE_RANGE),
+                         "workgroups": blocks, "gbs": round(buf.numel() / t / 1e9, 1)})
+    del buf
+    torch.cuda.empty_cache()
+    best = max(runs, key=lambda r: r["gbs"])
+    log(f"[bench] read probe best {best['gbs']} GB/s ({best})")
+    return {"gbs": best["gbs"], "bytes": 4 << 30, "best": best, "runs": runs}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,6 +505,10 @@ def main():
                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_partial_nvfp4_32k"),
                           "kernel": "decode_partial (NVFP4)", "algorithmic_bytes_per_launch": alg,
                           "mean_launch_ms": round(t_part * 1e3, 4)}
+    probe = read_probe(nk)
+    result["roofline"]["measured_read_gbs"] = probe["gbs"]
+    result["roofline"]["frac_of_measured_read"] = round(achieved / probe["gbs"], 4)
+    result["hbm_read_probe"] = probe
 
     if args.only == "all":
         f8 = Bench(nk, wl, True, variant)

@@ -335,6 +335,28 @@ int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, const void* k
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_chunk,
                       float sm_scale, void* out, void* stream);
 
+/*
+ * nvfp4kv_hbm_read_probe -- a measurement utility, not a step of the method:
+ * streams `bytes` from `buf` with 16-byte loads (eight loads in flight per
+ * thread, `blocks` workgroups of 256 threads) and folds them so that nothing
+ * is written in practice. Timing it gives the read bandwidth a plain
+ * streaming kernel reaches on the device, the second reference (beside the
+ * published HBM peak) for the decode kernel's roofline fraction.
+ *
+ *   buf       device, 16-byte aligned, `bytes` readable (a multiple of 16, >= 0)
+ *   flags     NVFP4KV_PROBE_NONTEMPORAL: non-temporal loads;
+ *             NVFP4KV_PROBE_RANGE: each workgroup reads one contiguous range
+ *             (else the workgroups stride over the whole buffer together)
+ *   sink      device uint32 the kernel may write (only if the fold of the data
+ *             equals a fixed value); 4-byte aligned
+ * Errors: NVFP4KV_EINVAL (bad size, blocks <= 0, unknown flags, NULL),
+ * NVFP4KV_EALIGN.
+ */
+#define NVFP4KV_PROBE_NONTEMPORAL 1
+#define NVFP4KV_PROBE_RANGE 2
+int nvfp4kv_hbm_read_probe(const void* buf, int64_t bytes, int32_t blocks, int32_t flags,
+                           uint32_t* sink, void* stream);
+
 /* Text of the last non-zero return on the calling thread ("" if none). */
 const char* nvfp4kv_last_error(void);
 

@@ -69,6 +69,7 @@ _SIGNATURES = {
     "nvfp4_kv_dequant_workspace_fp8": (ctypes.c_int, [P_GEOM, P_NV, P_NV, c_vp, c_i32, c_vp, c_vp, c_i32,
                                                       c_f32, c_f32, c_vp, c_vp, c_vp]),
     "nvfp4_global_scale_from_absmax": (c_f32, [c_f32]),
+    "nvfp4kv_hbm_read_probe": (ctypes.c_int, [c_vp, c_i64, c_i32, c_i32, c_vp, c_vp]),
 }
 
 _lib_handle = None
@@ -211,6 +212,23 @@ def nvfp4_kv_quantize(k, v, slot_mapping, k_pool: NVFP4Pool, v_pool: NVFP4Pool, 
 
 def fp8_kv_quantize(k, v, slot_mapping, k_pool: FP8Pool, v_pool: FP8Pool, stream=None):
     _quantize(lib().fp8_kv_quantize, k, v, slot_mapping, k_pool, v_pool, stream)
+
+
+PROBE_NONTEMPORAL, PROBE_RANGE = 1, 2
+
+
+def hbm_read_probe(buf, blocks, flags=PROBE_NONTEMPORAL, sink=None, stream=None):
+    """Stream-read every byte of buf (a 16-byte aligned device tensor whose size is a multiple of 16)
+    with the library's read-bandwidth kernel (a measurement utility); flags: PROBE_NONTEMPORAL,
+    PROBE_RANGE (one contiguous range per workgroup)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(lib().nvfp4kv_hbm_read_probe(buf.data_ptr(), nbytes, int(blocks), int(flags), sink.data_ptr(),
+                                        _stream(stream)))
+    return sink
 
 
 def nvfp4_kv_absmax(x, amax, stream=None):

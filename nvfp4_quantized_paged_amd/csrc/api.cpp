@@ -210,6 +210,21 @@ NVFP4KV_API int nvfp4_kv_absmax(const void* x, int64_t token_stride, int32_t num
                   fn);
 }
 
+NVFP4KV_API int nvfp4kv_hbm_read_probe(const void* buf, int64_t bytes, int32_t blocks, int32_t flags,
+                                       uint32_t* sink, void* stream) {
+  const char* fn = "nvfp4kv_hbm_read_probe";
+  if (bytes < 0 || bytes % 16 != 0) return fail(NVFP4KV_EINVAL, "%s: bytes %lld must be a non-negative multiple of 16", fn,
+                                                (long long)bytes);
+  if (blocks <= 0) return fail(NVFP4KV_EINVAL, "%s: blocks %d <= 0", fn, blocks);
+  if (flags & ~3) return fail(NVFP4KV_EINVAL, "%s: unknown flags %#x", fn, flags);
+  if (bytes == 0) return launched(hipSuccess, fn);
+  if (!buf || !sink) return fail(NVFP4KV_EINVAL, "%s: buf and sink must be non-NULL", fn);
+  if (!aligned16(buf) || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return fail(NVFP4KV_EALIGN, "%s: buf must be 16-byte aligned and sink 4-byte aligned", fn);
+  return launched(launch_hbm_read_probe(buf, bytes, blocks, flags, sink, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 NVFP4KV_API int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, const void* k_ws,
                                   const void* v_ws, const int64_t* ws_row_offsets, const int32_t* prefix_lens,
                                   int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -199,6 +199,20 @@ def test_absmax_rejects_bad_arguments(L):
     assert f(FAKE16, 1024, 4, 8, 128, FAKE4 + 1, None) == L.EALIGN
 
 
+def test_read_probe_rejects_bad_arguments(L):
+    f = L.lib().nvfp4kv_hbm_read_probe
+    FAKE16, FAKE4 = 1 << 20, (1 << 20) + 4
+    assert f(FAKE16, 0, 64, 1, FAKE4, None) == L.OK                 # nothing to read
+    assert f(FAKE16, -16, 64, 1, FAKE4, None) == L.EINVAL
+    assert f(FAKE16, 1000, 64, 1, FAKE4, None) == L.EINVAL           # not a multiple of 16
+    assert f(FAKE16, 1024, 0, 1, FAKE4, None) == L.EINVAL
+    assert f(None, 1024, 64, 1, FAKE4, None) == L.EINVAL
+    assert f(FAKE16, 1024, 64, 1, None, None) == L.EINVAL
+    assert f(FAKE16 + 8, 1024, 64, 1, FAKE4, None) == L.EALIGN
+    assert f(FAKE16, 1024, 64, 1, FAKE4 + 2, None) == L.EALIGN
+    assert f(FAKE16, 1024, 64, 4, FAKE4, None) == L.EINVAL           # unknown flag
+
+
 def test_global_scale_from_absmax(L):
     g = L.nvfp4_global_scale_from_absmax
     assert g(2688.0) == 1.0                       # 448 * 6: the largest block maps onto scale 448, element 6
