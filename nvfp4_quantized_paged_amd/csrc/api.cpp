@@ -210,6 +210,13 @@ NVFP4KV_API int nvfp4_kv_absmax(const void* x, int64_t token_stride, int32_t num
                   fn);
 }
 
+namespace nvfp4kv {
+// read_probe.hip: streaming read of `bytes` (a multiple of 16) from a 16-byte aligned buffer; `blocks`
+// workgroups; flags: bit 0 non-temporal loads, bit 1 one contiguous range per workgroup (else grid-stride)
+hipError_t launch_hbm_read_probe(const void* buf, int64_t bytes, int32_t blocks, int32_t flags, uint32_t* sink,
+                                 hipStream_t s);
+}  // namespace nvfp4kv
+
 NVFP4KV_API int nvfp4kv_hbm_read_probe(const void* buf, int64_t bytes, int32_t blocks, int32_t flags,
                                        uint32_t* sink, void* stream) {
   const char* fn = "nvfp4kv_hbm_read_probe";

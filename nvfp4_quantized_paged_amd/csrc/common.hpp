@@ -187,10 +187,6 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, bool fp8, boo
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_extend_attn(const ExtendParams& p, int head_dim, hipStream_t s);
 // running max |x| of a [tokens][row_elems] bf16 tensor (rows `stride` elements apart) into *amax
-// streaming read of `bytes` (a multiple of 16) from a 16-byte aligned buffer; `blocks` workgroups;
-// flags: bit 0 non-temporal loads, bit 1 one contiguous range per workgroup (else grid-stride)
-hipError_t launch_hbm_read_probe(const void* buf, int64_t bytes, int32_t blocks, int32_t flags, uint32_t* sink,
-                                 hipStream_t s);
 hipError_t launch_absmax(const uint16_t* x, int64_t stride, int32_t num_tokens, int32_t row_elems,
                          float* amax, hipStream_t s);
 
