@@ -434,8 +434,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--variant", choices=["auto", "valu", "mfma", "mfma_lut"], default="auto")
-    ap.add_argument("--only", choices=["nvfp4", "fp8", "all"], default="all",
-                    help="nvfp4 / fp8: only that 32K decode step (for profiling)")
+    ap.add_argument("--only", choices=["nvfp4", "fp8", "agentic", "all"], default="all",
+                    help="nvfp4 / fp8: only that 32K decode step; agentic: only the prefix-reuse step with "
+                         "its extend attention and calibration (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
@@ -463,6 +464,10 @@ def main():
     variant = {"auto": nk.VARIANT_AUTO, "valu": nk.VARIANT_VALU, "mfma": nk.VARIANT_MFMA,
                "mfma_lut": nk.VARIANT_MFMA_LUT}[args.variant]
     wl = synth.WORKLOADS[3]
+    if args.only == "agentic":
+        res = agentic(nk, synth.WORKLOADS[5], max(5, args.steps // 2), args.warmup)
+        print(json.dumps({"agentic_prefix_reuse": res}), flush=True)
+        return
     if args.only == "fp8":
         f8 = Bench(nk, wl, True, variant)
         t8 = f8.time_steps(args.steps, args.warmup)
