@@ -55,7 +55,11 @@ struct ExtCfg {
   static constexpr int kQPerWave = 16 * kQT;
   static constexpr int kQPerGroup = kQPerWave * kWQ;
   static constexpr int kKPitch = D + 8;             // K row pitch (bf16): 16-byte reads of 16 rows spread over banks
-  static constexpr int kVPitch = kKB + 4;           // V^T row pitch (bf16)
+  // V^T row pitch (bf16): 34 dwords, so the 16 rows of an operand read (16 lanes of 8 bytes per
+  // LDS cycle) fall on distinct bank pairs; the 4-key chunks of row r are stored XOR-swizzled by
+  // (r >> 4) & 3, which spreads the transposing stores (16 rows four apart per cycle) over all
+  // banks and is a constant for every operand read
+  static constexpr int kVPitch = kKB + 4;
   static constexpr int kKSteps = D / 32;
   static constexpr int kCTiles = D / 16;
 };
@@ -196,11 +200,14 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
           const int wd = c >> 1;
           const u32x2_t out = {__builtin_amdgcn_perm(vreg[i][1][wd], vreg[i][0][wd], sel),
                                __builtin_amdgcn_perm(vreg[i][3][wd], vreg[i][2][wd], sel)};
-          *reinterpret_cast<u32x2_t*>(&vt_lds[buf][(4 * c4 + c) * C::kVPitch + 4 * kq]) = out;
+          *reinterpret_cast<u32x2_t*>(&vt_lds[buf][(4 * c4 + c) * C::kVPitch + 4 * (kq ^ ((c4 >> 2) & 3))]) = out;
         }
       }
     }
   };
+
+  // element offset of this lane's 4-key chunk within a 16-key tile of a V^T row, per swizzle value
+  const int vswz[4] = {4 * (grp ^ 0), 4 * (grp ^ 1), 4 * (grp ^ 2), 4 * (grp ^ 3)};
 
   load_block(0);
   store_block(0);
@@ -288,9 +295,10 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
       }
 #pragma unroll
       for (int c = 0; c < C::kCTiles; ++c) {
-        const __bf16* vrow = &vl[(16 * c + col) * C::kVPitch];
-        const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * t + 4 * grp);
-        const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * (t + 1) + 4 * grp);
+        // row 16c + col: chunk 4t + grp sits at 4t + (grp ^ (c & 3))
+        const __bf16* vrow = &vl[(16 * c + col) * C::kVPitch] + vswz[c & 3];
+        const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * t);
+        const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * (t + 1));
         const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int n = 0; n < NT; ++n) o[n][c] = mfma_bf16(a, pb[n], o[n][c]);
