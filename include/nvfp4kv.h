@@ -169,7 +169,10 @@ int nvfp4_kv_quantize_fp8(const nvfp4kv_geom* geom, const void* k, const void* v
  *   k_ws, v_ws      device bf16 [ws_row_offsets[batch]][Hkv][d]
  * Row off_b + t receives e2m1 * S * global_scale of token t, rounded to bf16
  * (exact when global_scale is a power of two: every E2M1 x E4M3 product is a
- * bf16 value). Requires prefix_len <= ws_row_offsets[b+1] - ws_row_offsets[b].
+ * bf16 value). Requires prefix_len <= ws_row_offsets[b+1] - ws_row_offsets[b]
+ * and prefix_len <= max_pages_per_seq * page_size (not checked: device data).
+ * Errors: NVFP4KV_EINVAL also when max_pages_per_seq * page_size exceeds
+ * 2^31 - 1 or batch exceeds 65535.
  */
 int nvfp4_kv_dequant_workspace(const nvfp4kv_geom* geom, const nvfp4kv_cache* k_cache,
                                const nvfp4kv_cache* v_cache, const int32_t* block_tables,
@@ -324,11 +327,17 @@ float nvfp4_global_scale_from_absmax(float amax);
  *   ws_row_offsets  device int64 [batch + 1]
  *   prefix_lens     device int32 [batch]
  *   max_chunk       >= every chunk length (sizes the grid); 0 is a no-op
- *   sm_scale        logit scale (finite)
+ *   sm_scale        logit scale (finite, either sign)
  *   out             device bf16 [q rows][num_q_heads][head_dim]
  * Query i of sequence b sits at position prefix_lens[b] + i and attends to keys
  * j <= prefix_lens[b] + i; query head h reads KV head h / (num_q_heads /
  * num_kv_heads), a group of 1, 2, 4, 8 or 16.
+ * Errors: NVFP4KV_EINVAL (negative sizes, heads not a multiple, non-finite
+ * sm_scale, ceil(max_chunk / 16) * num_kv_heads * batch above 2^31 - 1, or
+ * num_kv_heads * head_dim * 128 above 2^31 - 1, NULL pointers),
+ * NVFP4KV_EUNSUPPORTED (group or head_dim), NVFP4KV_EALIGN (q, k_ws, v_ws,
+ * out not 16-byte aligned). Offsets, lengths and chunk sizes in device
+ * memory are not checked.
  */
 int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, const void* k_ws, const void* v_ws,
                       const int64_t* ws_row_offsets, const int32_t* prefix_lens, int32_t batch,

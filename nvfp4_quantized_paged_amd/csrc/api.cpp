@@ -237,8 +237,8 @@ NVFP4KV_API int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, c
                                   int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_chunk, float sm_scale, void* out, void* stream) {
   const char* fn = "nvfp4_extend_attn";
-  if (batch < 0 || batch > kGridYZ) return fail(NVFP4KV_EINVAL, "%s: batch %d out of range [0, %d]", fn, batch, kGridYZ);
-  if (num_kv_heads <= 0 || num_kv_heads > kGridYZ || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+  if (batch < 0) return fail(NVFP4KV_EINVAL, "%s: batch %d < 0", fn, batch);
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return fail(NVFP4KV_EINVAL, "%s: heads %d / %d (num_q_heads must be a multiple of num_kv_heads)", fn,
                 num_q_heads, num_kv_heads);
   const int32_t group = num_q_heads / num_kv_heads;
@@ -248,6 +248,12 @@ NVFP4KV_API int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, c
     return fail(NVFP4KV_EUNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
   if (max_chunk < 0) return fail(NVFP4KV_EINVAL, "%s: max_chunk %d < 0", fn, max_chunk);
   if (!isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "%s: sm_scale must be finite", fn);
+  // one workgroup per (at least 16 queries, KV head, sequence); a 64-row key block addressed in 32 bits
+  if ((int64_t)((max_chunk + 15) / 16) * num_kv_heads * batch > 0x7FFFFFFFLL)
+    return fail(NVFP4KV_EINVAL, "%s: max_chunk / 16 * num_kv_heads * batch exceeds 2^31 - 1", fn);
+  if ((int64_t)num_kv_heads * head_dim * 2 * 64 > 0x7FFFFFFFLL)
+    return fail(NVFP4KV_EINVAL, "%s: num_kv_heads %d too large (a 64-row block must span < 2 GiB)", fn,
+                num_kv_heads);
   if (batch == 0 || max_chunk == 0) return launched(hipSuccess, fn);
   if (!q || !q_row_offsets || !k_ws || !v_ws || !ws_row_offsets || !prefix_lens || !out)
     return fail(NVFP4KV_EINVAL, "%s: pointers must be non-NULL", fn);
@@ -418,6 +424,8 @@ int dequant_workspace(const char* fn, const nvfp4kv_geom* geom, const nvfp4kv_ca
   if (!block_tables || !prefix_lens || !ws_row_offsets || !k_ws || !v_ws)
     return fail(NVFP4KV_EINVAL, "%s: block_tables, prefix_lens, ws_row_offsets, k_ws and v_ws must be non-NULL", fn);
   if (max_pages_per_seq <= 0) return fail(NVFP4KV_EINVAL, "%s: max_pages_per_seq %d must be > 0", fn, max_pages_per_seq);
+  if ((int64_t)max_pages_per_seq * geom->page_size > 0x7FFFFFFFLL)   // token index range of a sequence (and the grid)
+    return fail(NVFP4KV_EINVAL, "%s: max_pages_per_seq * page_size exceeds 2^31 - 1", fn);
   if (!aligned16(k_ws) || !aligned16(v_ws)) return fail(NVFP4KV_EALIGN, "%s: workspaces must be 16-byte aligned", fn);
   WorkspaceParams p{};
   p.data[0] = k_cache->data;

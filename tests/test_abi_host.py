@@ -168,6 +168,7 @@ def test_workspace_dequant_rejects_bad_arguments(L):
     assert call(bt=None) == L.EINVAL
     assert call(offs=None) == L.EINVAL
     assert call(maxp=0) == L.EINVAL
+    assert call(maxp=1 << 30) == L.EINVAL                           # 2^30 pages of 16 tokens: beyond int32 positions
     assert call(kw=FAKE + 2) == L.EALIGN
     assert call(B=0, bt=None, pl=None, offs=None, kw=None, vw=None) == L.OK
 
@@ -197,6 +198,30 @@ def test_absmax_rejects_bad_arguments(L):
     assert f(FAKE16 + 2, 1024, 4, 8, 128, FAKE4, None) == L.EALIGN
     assert f(FAKE16, 1028, 4, 8, 128, FAKE4, None) == L.EALIGN
     assert f(FAKE16, 1024, 4, 8, 128, FAKE4 + 1, None) == L.EALIGN
+
+
+def test_extend_rejects_bad_arguments(L):
+    f = L.lib().nvfp4_extend_attn
+    F = 1 << 20
+    ok = dict(batch=2, hq=8, hkv=2, d=128, mc=64, sm=0.088)
+
+    def call(q=F, qo=F, k=F, v=F, wo=F, pl=F, out=F, **kw):
+        a = dict(ok, **kw)
+        return f(q, qo, k, v, wo, pl, a["batch"], a["hq"], a["hkv"], a["d"], a["mc"], a["sm"], out, None)
+
+    assert call(batch=0) == L.OK and call(mc=0) == L.OK            # nothing to do
+    assert call(batch=-1) == L.EINVAL
+    assert call(mc=-1) == L.EINVAL
+    assert call(hkv=0) == L.EINVAL
+    assert call(hq=6, hkv=4) == L.EINVAL                            # not a multiple
+    assert call(hq=6, hkv=2) == L.EUNSUPPORTED                      # group 3
+    assert call(hq=64, hkv=2) == L.EUNSUPPORTED                     # group 32
+    assert call(d=96) == L.EUNSUPPORTED
+    assert call(sm=float("nan")) == L.EINVAL and call(sm=float("inf")) == L.EINVAL
+    assert call(batch=1 << 20, hkv=1024, hq=1024, mc=1 << 12) == L.EINVAL   # grid above 2^31 - 1
+    assert call(hkv=1 << 17, hq=1 << 17) == L.EINVAL               # 64-row block above 2 GiB
+    assert call(q=None) == L.EINVAL and call(pl=None) == L.EINVAL and call(out=None) == L.EINVAL
+    assert call(q=F + 2) == L.EALIGN and call(k=F + 8) == L.EALIGN and call(out=F + 4) == L.EALIGN
 
 
 def test_read_probe_rejects_bad_arguments(L):
