@@ -326,11 +326,12 @@ def test_fp8_quantize_every_bf16_value(nk):
 # dequantize-to-workspace
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape", [(8, 128, 16, 1.0), (1, 64, 16, 1.0), (3, 64, 32, 1.0), (8, 128, 16, GS_THIRD)])
+@pytest.mark.parametrize("shape", [(8, 128, 16, 1.0), (1, 64, 16, 1.0), (3, 64, 32, 1.0), (8, 128, 16, GS_THIRD),
+                                   (2, 128, 48, 1.0)])
 def test_dequant_workspace_agentic_small(nk, shape):
     H0, d0, P0, gs = shape
     wl = synth.Workload(95, "ws", 7, 2 * H0, H0, d0, P0, 0, False, 0, len_min=48, len_max=131,
-                        shared_prefix=32, chunk=9)
+                        shared_prefix=max(32, P0), chunk=9)   # the shared prefix is whole pages
     a = synth.host_agentic(wl)
     H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
     say(f"case workspace small agentic: B 7 pages {a.num_pages} gs {gs}")
@@ -575,6 +576,17 @@ def test_extend_attention_long_prefix(nk, G, d, sm_sign):
 # ---------------------------------------------------------------------------
 # decode attention
 # ---------------------------------------------------------------------------
+
+def test_decode_page_size_not_a_power_of_two(nk):
+    """Page size 48 (a multiple of 16, not a power of two: the slot and page
+    arithmetic take divisions), a context that ends inside a page, every
+    kernel variant and several split counts, against the oracle."""
+    wl = synth.Workload(98, "page48", 3, 8, 2, 128, 48, 1000, False, 0)
+    inp = synth.host_uniform_decode(wl)
+    say(f"case decode page 48: {wl}")
+    decode_problem(nk, inp, splits_list=(0, 1, 3, 7),
+                   variants=(None, nk.VARIANT_VALU, nk.VARIANT_MFMA, nk.VARIANT_MFMA_LUT), label="page48")
+
 
 def test_decode_tiny_workload(nk):
     wl = synth.WORKLOADS[1]
