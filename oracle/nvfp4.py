@@ -70,9 +70,9 @@ def is_power_of_two(gs: float) -> bool:
 
 
 def encode_blocks_fp32(x: np.ndarray, gs: float):
-    """Encode with a calibrated global scale, in the FP32 arithmetic of the
-    NVFP4 recipe (reading A12 of this build; the pages fix only that the
-    tensor scale is FP32):
+    """Encode with a calibrated global scale, in FP32 arithmetic. The NVFP4
+    page (section A3) fixes only that the tensor scale is FP32; where it
+    leaves the arithmetic open, each step below is one FP32 operation:
 
       S     = E4M3(fl32(amax / fl32(6 * gs)))        nearest even, saturating
       S_eff = fl32(S * gs)
