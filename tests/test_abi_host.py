@@ -277,3 +277,15 @@ def test_fp8_path2_entry_points_validate(L):
     assert deq(bt=None) == L.EINVAL
     assert deq(kw=FAKE + 8) == L.EALIGN
     assert deq(B=0, bt=None, pl=None, offs=None, kw=None, vw=None) == L.OK
+
+
+def test_binding_fails_loudly_without_the_library(L, monkeypatch, tmp_path):
+    """No silent fallback: with the native library absent, every entry point raises."""
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libnvfp4kv.so"))
+    monkeypatch.setattr(L, "_lib_handle", None)
+    with pytest.raises(ImportError):
+        L.lib()
+    with pytest.raises(ImportError):
+        L.nvfp4_global_scale_from_absmax(1.0)
+    with pytest.raises(ImportError):
+        L.nvfp4_paged_decode_num_splits(1, 1, 16, 16)
