@@ -733,6 +733,38 @@ def test_decode_invariants(nk):
     assert torch.equal(kp.data, data_before), "decode must not write the cache"
 
 
+def test_side_stream_matches_default_stream(nk):
+    """Quantize, dequantize and decode issued back to back on a side stream
+    (default priority; each call ordered after the previous one on that stream
+    only) give bytes and outputs identical to the default-stream run."""
+    wl = synth.Workload(93, "inv", 4, 16, 2, 128, 16, 700, True, 0)
+    inp = synth.host_uniform_decode(wl)
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    say("case side stream")
+    k, v = synth.to_device_bf16(inp.k), synth.to_device_bf16(inp.v)
+    slots = synth.to_device(inp.slot_mapping)
+    q = synth.to_device_bf16(inp.q)
+    bt, sl = synth.to_device(inp.block_tables), synth.to_device(inp.seq_lens)
+    offs = np.zeros(wl.batch + 1, np.int64)
+    offs[1:] = np.cumsum(inp.seq_lens)
+    rows = int(offs[-1])
+    results = []
+    for side in (False, True):
+        kp, vp = nv_pools(nk, inp.num_pages, H, P, d)
+        kws = torch.empty((rows, H, d), dtype=torch.bfloat16, device="cuda")
+        vws = torch.empty_like(kws)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream() if side else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            nk.nvfp4_kv_quantize(k, v, slots, kp, vp, stream=s)
+            nk.nvfp4_kv_dequant_workspace(kp, vp, bt, sl, synth.to_device(offs), kws, vws, stream=s)
+            out = nk.nvfp4_paged_decode_attn(q, kp, vp, bt, sl, wl.sm_scale, num_splits=5, stream=s)
+        torch.cuda.synchronize()
+        results.append((kp.data.clone(), kp.scale.clone(), kws.clone(), out.clone()))
+    for a, b, what in zip(results[0], results[1], ("K data", "K scale", "K workspace", "decode output")):
+        assert torch.equal(a, b), what
+
+
 def test_fp8_decode_moderate(nk):
     wl = synth.WORKLOADS[2]
     inp = synth.host_uniform_decode(wl, batch=4)
