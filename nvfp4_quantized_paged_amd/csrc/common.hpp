@@ -82,18 +82,6 @@ __device__ inline void fp8x4_to_f32(uint32_t w, float out[4]) {
   out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
 }
 
-// Four floats -> four OCP E4M3 bytes (element i in byte i), nearest even,
-// saturating at +-448, sign of zero kept. The conversion instruction rounds to
-// nearest even but turns magnitudes that round past 448 into NaN, so the
-// inputs are clamped first; checked on MI355X against the exact encoder for
-// every finite bf16 value, every E2M1 x E4M3 product and 1M random floats.
-__device__ inline uint32_t f32x4_to_fp8(float a, float b, float c, float d) {
-  const auto clamp = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(a), clamp(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(c), clamp(d), w, true);
-  return (uint32_t)w;
-}
-
 // ---------------------------------------------------------------------------
 // wave64 reductions
 // ---------------------------------------------------------------------------
