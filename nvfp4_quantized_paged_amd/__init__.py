@@ -128,6 +128,79 @@ def _need(t: torch.Tensor, dtype, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+# Shape checks. The C ABI receives pointers and the sizes passed beside them;
+# it cannot see how large each tensor is. A tensor smaller than those sizes
+# imply (fewer V tokens than K tokens, a short slot mapping, a smaller V pool)
+# would make a kernel read or write past it, so the binding compares every
+# tensor with the sizes it passes. They only inspect shapes, so they work on
+# tensors of any device.
+
+def _shape(t: torch.Tensor, shape, name: str):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows_of(t: torch.Tensor, g: "Geom", name: str):
+    """t must be [rows][Hkv][d] for the pool geometry g."""
+    if t.dim() != 3 or tuple(t.shape[1:]) != (g.num_kv_heads, g.head_dim):
+        raise ValueError(f"{name} must be [rows][{g.num_kv_heads}][{g.head_dim}], got {tuple(t.shape)}")
+
+
+def _pool_geom(k_pool, v_pool) -> "Geom":
+    gk, gv = k_pool.geom, v_pool.geom
+    if (gk.num_pages, gk.page_size, gk.num_kv_heads, gk.head_dim) != \
+            (gv.num_pages, gv.page_size, gv.num_kv_heads, gv.head_dim):
+        raise ValueError("the K and V pools must have the same geometry")
+    return gk
+
+
+def _check_quantize_shapes(k, v, slot_mapping, k_pool, v_pool) -> "Geom":
+    g = _pool_geom(k_pool, v_pool)
+    T = k.shape[0] if k.dim() == 3 else -1
+    _shape(k, (T, g.num_kv_heads, g.head_dim), "k")
+    _shape(v, (T, g.num_kv_heads, g.head_dim), "v")
+    _shape(slot_mapping, (T,), "slot_mapping")
+    return g
+
+
+def _check_workspace_shapes(k_pool, v_pool, block_tables, prefix_lens, ws_row_offsets, k_ws, v_ws) -> "Geom":
+    g = _pool_geom(k_pool, v_pool)
+    if block_tables.dim() != 2:
+        raise ValueError(f"block_tables must be [batch][max_pages], got {tuple(block_tables.shape)}")
+    B = block_tables.shape[0]
+    _shape(prefix_lens, (B,), "prefix_lens")
+    _shape(ws_row_offsets, (B + 1,), "ws_row_offsets")
+    _rows_of(k_ws, g, "k_ws")
+    _shape(v_ws, k_ws.shape, "v_ws")
+    return g
+
+
+def _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, out=None) -> "Geom":
+    g = _pool_geom(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != g.head_dim:
+        raise ValueError(f"q must be [batch][num_q_heads][{g.head_dim}], got {tuple(q.shape)}")
+    B = q.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError(f"block_tables must be [{B}][max_pages], got {tuple(block_tables.shape)}")
+    _shape(seq_lens, (B,), "seq_lens")
+    if out is not None:
+        _shape(out, q.shape, "out")
+    return g
+
+
+def _check_extend_shapes(q, q_row_offsets, k_ws, v_ws, ws_row_offsets, prefix_lens, out=None):
+    B = prefix_lens.shape[0] if prefix_lens.dim() == 1 else -1
+    _shape(prefix_lens, (B,), "prefix_lens")
+    _shape(q_row_offsets, (B + 1,), "q_row_offsets")
+    _shape(ws_row_offsets, (B + 1,), "ws_row_offsets")
+    if q.dim() != 3 or k_ws.dim() != 3 or q.shape[2] != k_ws.shape[2]:
+        raise ValueError(f"q [rows][Hq][d] and k_ws [rows][Hkv][d] must share d, got {tuple(q.shape)} and "
+                         f"{tuple(k_ws.shape)}")
+    _shape(v_ws, k_ws.shape, "v_ws")
+    if out is not None:
+        _shape(out, q.shape, "out")
+
+
 # ---------------------------------------------------------------------------
 # pools
 # ---------------------------------------------------------------------------
@@ -155,6 +228,7 @@ class NVFP4Pool:
     def desc(self) -> NVFP4CacheDesc:
         _need(self.data, torch.uint8, "pool data")
         _need(self.scale, torch.uint8, "pool scale")
+        _shape(self.scale, tuple(self.data.shape[:3]) + (self.data.shape[3] // 8,), "pool scale")
         return NVFP4CacheDesc(self.data.data_ptr(), self.scale.data_ptr(), self.global_scale)
 
 
@@ -193,7 +267,7 @@ def _quantize(fn, k, v, slot_mapping, k_pool, v_pool, stream):
             raise ValueError(f"{name} must be [T][Hkv][d]")
         if t.shape[0] > 0 and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
             raise ValueError(f"{name} must be [T][Hkv][d] with dense heads")
-    g = k_pool.geom
+    g = _check_quantize_shapes(k, v, slot_mapping, k_pool, v_pool)
     if k.shape[0] == 0:
         stride = g.num_kv_heads * g.head_dim
     else:
@@ -257,6 +331,7 @@ def nvfp4_extend_attn(q, q_row_offsets, k_ws, v_ws, ws_row_offsets, prefix_lens,
     _need(q_row_offsets, torch.int64, "q_row_offsets")
     _need(ws_row_offsets, torch.int64, "ws_row_offsets")
     _need(prefix_lens, torch.int32, "prefix_lens")
+    _check_extend_shapes(q, q_row_offsets, k_ws, v_ws, ws_row_offsets, prefix_lens, out)
     if max_chunk is None:
         max_chunk = int((q_row_offsets[1:] - q_row_offsets[:-1]).max().item()) if prefix_lens.numel() else 0
     if out is None:
@@ -284,7 +359,7 @@ def nvfp4_kv_quantize_fp8(k, v, slot_mapping, k_pool: NVFP4Pool, v_pool: NVFP4Po
             raise TypeError(f"{name} must be a uint8 (FP8-E4M3) device tensor [T][Hkv][d]")
         if t.shape[0] > 0 and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
             raise ValueError(f"{name} must be [T][Hkv][d] with dense heads")
-    g = k_pool.geom
+    g = _check_quantize_shapes(k, v, slot_mapping, k_pool, v_pool)
     if k.shape[0] > 0 and k.stride(0) != v.stride(0):
         raise ValueError("k and v must share a token stride")
     stride = k.stride(0) if k.shape[0] > 0 else g.num_kv_heads * g.head_dim
@@ -292,6 +367,9 @@ def nvfp4_kv_quantize_fp8(k, v, slot_mapping, k_pool: NVFP4Pool, v_pool: NVFP4Po
         _need(ws_rows, torch.int64, "ws_rows")
         _need(k_ws, torch.uint8, "k_ws")
         _need(v_ws, torch.uint8, "v_ws")
+        _shape(ws_rows, (k.shape[0],), "ws_rows")
+        _rows_of(k_ws, g, "k_ws")
+        _shape(v_ws, k_ws.shape, "v_ws")
     _check(lib().nvfp4_kv_quantize_fp8(
         ctypes.byref(g), k.data_ptr(), v.data_ptr(), stride, k.shape[0], slot_mapping.data_ptr(),
         float(k_src_scale), float(v_src_scale), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()),
@@ -306,7 +384,7 @@ def nvfp4_kv_dequant_workspace_fp8(k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_t
     _need(ws_row_offsets, torch.int64, "ws_row_offsets")
     _need(k_ws, torch.uint8, "k_ws")
     _need(v_ws, torch.uint8, "v_ws")
-    g = k_pool.geom
+    g = _check_workspace_shapes(k_pool, v_pool, block_tables, prefix_lens, ws_row_offsets, k_ws, v_ws)
     _check(lib().nvfp4_kv_dequant_workspace_fp8(
         ctypes.byref(g), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()), block_tables.data_ptr(),
         block_tables.shape[1], prefix_lens.data_ptr(), ws_row_offsets.data_ptr(), prefix_lens.shape[0],
@@ -321,7 +399,7 @@ def nvfp4_kv_dequant_workspace(k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_table
     _need(ws_row_offsets, torch.int64, "ws_row_offsets")
     _need(k_ws, torch.bfloat16, "k_ws")
     _need(v_ws, torch.bfloat16, "v_ws")
-    g = k_pool.geom
+    g = _check_workspace_shapes(k_pool, v_pool, block_tables, prefix_lens, ws_row_offsets, k_ws, v_ws)
     _check(lib().nvfp4_kv_dequant_workspace(
         ctypes.byref(g), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()), block_tables.data_ptr(),
         block_tables.shape[1], prefix_lens.data_ptr(), ws_row_offsets.data_ptr(), prefix_lens.shape[0],
@@ -345,6 +423,8 @@ def _decode_args(q, block_tables, seq_lens):
     _need(q, torch.bfloat16, "q")
     _need(block_tables, torch.int32, "block_tables")
     _need(seq_lens, torch.int32, "seq_lens")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [batch][num_q_heads][head_dim], got {tuple(q.shape)}")
     B, Hq, d = q.shape
     return B, Hq, d
 
@@ -358,7 +438,7 @@ def _resolve_splits(num_splits, B, pool_geom, max_pages):
 def _decode(fn_name, pool_cls_desc, q, k_pool, v_pool, block_tables, seq_lens, sm_scale, num_splits,
             workspace, out, stream):
     B, Hq, d = _decode_args(q, block_tables, seq_lens)
-    g = k_pool.geom
+    g = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, out)
     splits = _resolve_splits(num_splits, B, g, block_tables.shape[1])
     if workspace is None:
         workspace = decode_workspace(B, Hq, d, splits, q.device)
@@ -376,7 +456,7 @@ def _decode(fn_name, pool_cls_desc, q, k_pool, v_pool, block_tables, seq_lens, s
 def _partial(fn_name, q, k_pool, v_pool, block_tables, seq_lens, sm_scale, num_splits, variant, workspace,
              stream):
     B, Hq, d = _decode_args(q, block_tables, seq_lens)
-    g = k_pool.geom
+    g = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens)
     if workspace is None:
         workspace = decode_workspace(B, Hq, d, num_splits, q.device)
     _check(getattr(lib(), fn_name)(
@@ -414,6 +494,7 @@ def fp8_paged_decode_partial(q, k_pool, v_pool, block_tables, seq_lens, sm_scale
 
 def nvfp4kv_lse_merge(workspace, batch, num_q_heads, head_dim, num_splits, out_scale, out, stream=None):
     _need(out, torch.bfloat16, "out")
+    _shape(out, (batch, num_q_heads, head_dim), "out")
     _check(lib().nvfp4kv_lse_merge(workspace.data_ptr(), workspace.numel() * workspace.element_size(), batch,
                                    num_q_heads, head_dim, num_splits, float(out_scale), out.data_ptr(),
                                    _stream(stream)))

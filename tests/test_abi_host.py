@@ -289,3 +289,68 @@ def test_binding_fails_loudly_without_the_library(L, monkeypatch, tmp_path):
         L.nvfp4_global_scale_from_absmax(1.0)
     with pytest.raises(ImportError):
         L.nvfp4_paged_decode_num_splits(1, 1, 16, 16)
+
+
+def test_binding_rejects_tensors_smaller_than_the_sizes_it_passes(L):
+    """The C ABI cannot see tensor sizes; the binding compares every tensor with
+    the sizes it passes, so a short V, slot mapping, table, pool or output raises
+    before anything is launched (CPU tensors: the checks look at shapes only)."""
+    import torch
+    nk = L
+    T, H, P, d, pages, B = 5, 2, 16, 64, 4, 3
+    pool = lambda n=pages, h=H: nk.NVFP4Pool(torch.empty((n, h, P, d // 2), dtype=torch.uint8),
+                                             torch.empty((n, h, P, d // 16), dtype=torch.uint8))
+    kp, vp = pool(), pool()
+    k = torch.empty((T, H, d), dtype=torch.bfloat16)
+    slots = torch.empty(T, dtype=torch.int64)
+    assert nk._check_quantize_shapes(k, k.clone(), slots, kp, vp).num_pages == pages
+    with pytest.raises(ValueError, match="v must have shape"):
+        nk._check_quantize_shapes(k, k[:T - 1], slots, kp, vp)
+    with pytest.raises(ValueError, match="slot_mapping"):
+        nk._check_quantize_shapes(k, k, slots[:T - 1], kp, vp)
+    with pytest.raises(ValueError, match="k must have shape"):
+        nk._check_quantize_shapes(torch.empty((T, H, 2 * d), dtype=torch.bfloat16), k, slots, kp, vp)
+    with pytest.raises(ValueError, match="same geometry"):
+        nk._check_quantize_shapes(k, k, slots, kp, pool(n=pages - 1))
+
+    bt = torch.empty((B, 8), dtype=torch.int32)
+    ws = torch.empty((40, H, d), dtype=torch.bfloat16)
+    pl, offs = torch.empty(B, dtype=torch.int32), torch.empty(B + 1, dtype=torch.int64)
+    nk._check_workspace_shapes(kp, vp, bt, pl, offs, ws, ws.clone())
+    with pytest.raises(ValueError, match="prefix_lens"):
+        nk._check_workspace_shapes(kp, vp, bt, pl[:B - 1], offs, ws, ws)
+    with pytest.raises(ValueError, match="ws_row_offsets"):
+        nk._check_workspace_shapes(kp, vp, bt, pl, offs[:B], ws, ws)
+    with pytest.raises(ValueError, match="v_ws"):
+        nk._check_workspace_shapes(kp, vp, bt, pl, offs, ws, ws[:10])
+    with pytest.raises(ValueError, match="k_ws"):
+        nk._check_workspace_shapes(kp, vp, bt, pl, offs, torch.empty((40, H + 1, d), dtype=torch.bfloat16), ws)
+
+    q = torch.empty((B, 4 * H, d), dtype=torch.bfloat16)
+    sl = torch.empty(B, dtype=torch.int32)
+    nk._check_decode_shapes(q, kp, vp, bt, sl, q.clone())
+    with pytest.raises(ValueError, match="seq_lens"):
+        nk._check_decode_shapes(q, kp, vp, bt, sl[:B - 1])
+    with pytest.raises(ValueError, match="block_tables"):
+        nk._check_decode_shapes(q, kp, vp, bt[:B - 1], sl)
+    with pytest.raises(ValueError, match="out"):
+        nk._check_decode_shapes(q, kp, vp, bt, sl, q[:B - 1])
+    with pytest.raises(ValueError, match="q must be"):
+        nk._check_decode_shapes(torch.empty((B, 4 * H, 2 * d), dtype=torch.bfloat16), kp, vp, bt, sl)
+    with pytest.raises(ValueError, match="same geometry"):
+        nk._check_decode_shapes(q, kp, pool(h=H + 1), bt, sl)
+
+    rows = torch.empty((12, 4 * H, d), dtype=torch.bfloat16)
+    qo = torch.empty(B + 1, dtype=torch.int64)
+    nk._check_extend_shapes(rows, qo, ws, ws, offs, pl, rows.clone())
+    with pytest.raises(ValueError, match="q_row_offsets"):
+        nk._check_extend_shapes(rows, qo[:B], ws, ws, offs, pl)
+    with pytest.raises(ValueError, match="share d"):
+        nk._check_extend_shapes(rows, qo, torch.empty((40, H, 2 * d), dtype=torch.bfloat16), ws, offs, pl)
+    with pytest.raises(ValueError, match="v_ws"):
+        nk._check_extend_shapes(rows, qo, ws, ws[:39], offs, pl)
+
+    bad_scale = nk.NVFP4Pool(torch.empty((pages, H, P, d // 2), dtype=torch.uint8),
+                             torch.empty((pages, H, P, d // 32), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="pool scale"):
+        nk._shape(bad_scale.scale, tuple(bad_scale.data.shape[:3]) + (bad_scale.data.shape[3] // 8,), "pool scale")

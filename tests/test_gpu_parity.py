@@ -765,6 +765,38 @@ def test_side_stream_matches_default_stream(nk):
         assert torch.equal(a, b), what
 
 
+def test_binding_rejects_mismatched_device_tensors(nk):
+    """The wrappers compare every device tensor with the sizes they pass to the
+    C ABI: a short V, slot mapping, seq_lens, output or V pool raises ValueError
+    and nothing is launched (the pools keep their sentinel bytes)."""
+    say("case binding shape checks")
+    T, H, P, d, pages, B = 6, 2, 16, 64, 4, 2
+    kp, vp = nv_pools(nk, pages, H, P, d)
+    k = torch.zeros((T, H, d), dtype=torch.bfloat16, device="cuda")
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):
+        nk.nvfp4_kv_quantize(k, k[:T - 1], slots, kp, vp)
+    with pytest.raises(ValueError):
+        nk.nvfp4_kv_quantize(k, k, slots[:T - 1], kp, vp)
+    small_v, _ = nv_pools(nk, pages - 1, H, P, d)
+    with pytest.raises(ValueError):
+        nk.nvfp4_kv_quantize(k, k, slots, kp, small_v)
+    q = torch.zeros((B, 2 * H, d), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((B, 2), dtype=torch.int32, device="cuda")
+    sl = torch.full((B,), 8, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        nk.nvfp4_paged_decode_attn(q, kp, vp, bt, sl[:1], d ** -0.5)
+    with pytest.raises(ValueError):
+        nk.nvfp4_paged_decode_attn(q, kp, vp, bt, sl, d ** -0.5, out=q[:1].clone())
+    ws = torch.zeros((16, H, d), dtype=torch.bfloat16, device="cuda")
+    offs = torch.tensor([0, 8, 16], dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):
+        nk.nvfp4_kv_dequant_workspace(kp, vp, bt, sl, offs, ws, ws[:8])
+    torch.cuda.synchronize()
+    for t in (kp.data, kp.scale, vp.data, vp.scale):
+        assert bool((t == SENT).all()), "a rejected call must not launch anything"
+
+
 def test_fp8_decode_moderate(nk):
     wl = synth.WORKLOADS[2]
     inp = synth.host_uniform_decode(wl, batch=4)
