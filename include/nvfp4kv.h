@@ -30,11 +30,13 @@
  *    of the last failure on the calling thread is nvfp4kv_last_error().
  *    No C++ exception crosses the ABI.
  *  - Data-dependent contract violations cannot be checked on the host and
- *    are undefined behaviour: block-table entries outside [0, num_pages),
- *    seq_len or prefix_len > max_pages_per_seq * page_size, or two tokens of
- *    one call mapping to the same slot. (As a safety net, not a guarantee of
- *    meaningful results, the MFMA decode and the workspace kernels clamp page
- *    indices into the pool and quantize skips slots outside it.)
+ *    are undefined behaviour: block-table entries outside [0, num_pages), or
+ *    two tokens of one call mapping to the same slot. (As a safety net, not a
+ *    guarantee of meaningful results, the MFMA decode and the workspace
+ *    kernels clamp page indices into the pool and quantize skips slots
+ *    outside it.) A seq_len or prefix_len above max_pages_per_seq * page_size
+ *    is taken as that many tokens: no token past the block table's reach is
+ *    read.
  *  - bf16 tensors are IEEE bfloat16 bit patterns (uint16). Base pointers of
  *    packed/bf16 buffers must be 16-byte aligned (128-bit accesses).
  *  - Supported shapes: head_dim 64 or 128; page_size a positive multiple of
@@ -170,7 +172,8 @@ int nvfp4_kv_quantize_fp8(const nvfp4kv_geom* geom, const void* k, const void* v
  * Row off_b + t receives e2m1 * S * global_scale of token t, rounded to bf16
  * (exact when global_scale is a power of two: every E2M1 x E4M3 product is a
  * bf16 value). Requires prefix_len <= ws_row_offsets[b+1] - ws_row_offsets[b]
- * and prefix_len <= max_pages_per_seq * page_size (not checked: device data).
+ * (not checked: device data); a prefix_len above max_pages_per_seq *
+ * page_size is taken as that many tokens.
  * Errors: NVFP4KV_EINVAL also when max_pages_per_seq * page_size exceeds
  * 2^31 - 1 or batch exceeds 65535.
  */
@@ -223,7 +226,8 @@ size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  *
  *   q            device bf16 [batch][num_q_heads][d]
  *   block_tables device int32 [batch][max_pages_per_seq]
- *   seq_lens     device int32 [batch]; 0 gives an all-zero output row
+ *   seq_lens     device int32 [batch]; 0 gives an all-zero output row; values above
+ *                max_pages_per_seq * page_size are taken as that many tokens
  *   sm_scale     softmax scale (1/sqrt(d) in the pages' models)
  *   num_splits   1..4096, or 0 for nvfp4_paged_decode_num_splits(...)
  *   workspace    device, >= nvfp4_paged_decode_workspace_bytes(...) bytes
@@ -231,6 +235,8 @@ size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * The K global scale multiplies the logits and the V global scale multiplies
  * the output (the page's "BMM scale parameters"). Pages may be shared by
  * several sequences (prefix aliasing); the cache is only read.
+ * Errors: NVFP4KV_EINVAL also when max_pages_per_seq * page_size exceeds
+ * 2^31 - 1 (every decode entry point).
  */
 int nvfp4_paged_decode_attn(const nvfp4kv_geom* geom, const void* q,
                             const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,

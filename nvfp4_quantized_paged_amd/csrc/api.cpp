@@ -93,6 +93,8 @@ int check_decode(const nvfp4kv_geom* g, const void* q, const int32_t* block_tabl
   if (!aligned16(q)) return fail(NVFP4KV_EALIGN, "%s: q must be 16-byte aligned", fn);
   if (batch < 0 || batch > kGridYZ) return fail(NVFP4KV_EINVAL, "%s: batch %d out of range [0, %d]", fn, batch, kGridYZ);
   if (max_pages <= 0) return fail(NVFP4KV_EINVAL, "%s: max_pages_per_seq %d must be > 0", fn, max_pages);
+  if ((int64_t)max_pages * g->page_size > 0x7FFFFFFFLL)   // token index range of a sequence
+    return fail(NVFP4KV_EINVAL, "%s: max_pages_per_seq * page_size exceeds 2^31 - 1", fn);
   if (num_q_heads <= 0 || num_q_heads % g->num_kv_heads != 0)
     return fail(NVFP4KV_EINVAL, "%s: num_q_heads %d must be a positive multiple of num_kv_heads %d", fn,
                 num_q_heads, g->num_kv_heads);

@@ -333,8 +333,9 @@ void decode_partial_mfma_kernel(DecodeParams p) {
   const int grp = lane >> 4;        // lane group
   const int G = p.group;
   const int S = p.num_splits;
-  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);   // wave-uniform: keeps offsets scalar
   const int P = p.page_size;
+  // wave-uniform (keeps offsets scalar); tokens past the table's reach are not read
+  const int L = min(__builtin_amdgcn_readfirstlane(p.seq_lens[b]), p.max_pages * P);
   const int per = ceil_div(ceil_div(L, S), P) * P;
   const int t0 = j * per;
   const Item it{p.block_tables + (int64_t)b * p.max_pages, g, min(L, t0 + per)};

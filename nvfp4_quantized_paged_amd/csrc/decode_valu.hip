@@ -59,8 +59,8 @@ __global__ __launch_bounds__(64) void decode_partial_valu_kernel(DecodeParams p)
   const int lane = threadIdx.x;
   const int G = p.group;
   const int S = p.num_splits;
-  const int L = p.seq_lens[b];
   const int P = p.page_size;
+  const int L = min(p.seq_lens[b], p.max_pages * P);   // tokens past the table's reach are not read
   const int per = ceil_div(ceil_div(L, S), P) * P;
   const int t0 = j * per;
   const int t1 = min(L, t0 + per);

@@ -56,7 +56,8 @@ __global__ __launch_bounds__(64 * kWsWaves) void nvfp4_dequant_ws_kernel(Workspa
   const int wave = threadIdx.x >> 6;
   const int nb = p.head_dim / kBlock;
   const int items = p.num_kv_heads * nb * 2;          // 8-channel half-blocks of one row
-  const int prefix = __builtin_amdgcn_readfirstlane(p.prefix_lens[b]);
+  // tokens past the table's reach are not read
+  const int prefix = min(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.max_pages * p.page_size);
   const int64_t row0 = p.row_offsets[b];
   const int P = p.page_size;
   constexpr int kWsRowsPerWave = rows_per_wave<FP8OUT>();

@@ -119,6 +119,8 @@ def test_decode_rejects_bad_arguments(L):
     assert _decode(L, g, out=None) == L.EINVAL
     assert _decode(L, g, B=-1) == L.EINVAL
     assert _decode(L, g, maxp=0) == L.EINVAL
+    assert _decode(L, g, maxp=(1 << 31) // 16) == L.EINVAL     # max_pages * page_size past 2^31 - 1
+    assert "2^31" in L.last_error()
     assert _decode(L, _geom(L, H=2), Hq=3) == L.EINVAL
     assert _decode(L, g, Hq=32) == L.EUNSUPPORTED
     assert _decode(L, g, S=5000) == L.EINVAL

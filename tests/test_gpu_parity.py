@@ -765,6 +765,41 @@ def test_side_stream_matches_default_stream(nk):
         assert torch.equal(a, b), what
 
 
+def test_lengths_past_the_block_table_are_clamped(nk):
+    """A seq_len or prefix_len above max_pages_per_seq * page_size is taken as
+    that many tokens: the decode output and the workspace equal those of the
+    clamped length bit for bit, and no row past them is written."""
+    wl = synth.Workload(94, "clamp", 3, 8, 2, 64, 16, 96, False, 0)
+    inp = synth.host_uniform_decode(wl)
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    say("case lengths past the block table")
+    kp, vp = nv_pools(nk, inp.num_pages, H, P, d)
+    nk.nvfp4_kv_quantize(synth.to_device_bf16(inp.k), synth.to_device_bf16(inp.v),
+                         synth.to_device(inp.slot_mapping), kp, vp)
+    q, bt = synth.to_device_bf16(inp.q), synth.to_device(inp.block_tables)
+    reach = bt.shape[1] * P
+    at = torch.full((wl.batch,), reach, dtype=torch.int32, device="cuda")
+    past = torch.tensor([reach + 1, reach + 1000, 1 << 30], dtype=torch.int32, device="cuda")
+    for S in (1, 3):
+        a = nk.nvfp4_paged_decode_attn(q, kp, vp, bt, at, wl.sm_scale, num_splits=S)
+        b = nk.nvfp4_paged_decode_attn(q, kp, vp, bt, past, wl.sm_scale, num_splits=S)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"splits {S}"
+    rows = wl.batch * (reach + 8)
+    offs = torch.arange(0, rows + 1, reach + 8, dtype=torch.int64, device="cuda")
+    results = []
+    for lens in (at, past):
+        kws = torch.full((rows, H, d), -7.0, dtype=torch.bfloat16, device="cuda")
+        vws = torch.full_like(kws, -7.0)
+        nk.nvfp4_kv_dequant_workspace(kp, vp, bt, lens, offs, kws, vws)
+        torch.cuda.synchronize()
+        results.append((kws, vws))
+    assert torch.equal(results[0][0], results[1][0]) and torch.equal(results[0][1], results[1][1])
+    for b_ in range(wl.batch):   # the 8 rows after each prefix keep their fill
+        tail = results[1][0][b_ * (reach + 8) + reach:(b_ + 1) * (reach + 8)]
+        assert bool((tail == -7.0).all())
+
+
 def test_binding_rejects_mismatched_device_tensors(nk):
     """The wrappers compare every device tensor with the sizes they pass to the
     C ABI: a short V, slot mapping, seq_lens, output or V pool raises ValueError
