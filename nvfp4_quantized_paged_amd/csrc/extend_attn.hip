@@ -219,6 +219,11 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
     const __bf16* kl = k_lds[buf];
     const __bf16* vl = vt_lds[buf];
 
+    // The compiler's default schedule kept one or two LDS operand reads in flight and waited
+    // for each right before its MFMAs; the built-in interleave strategies issue the reads
+    // several products ahead (strategy 1 here, 0 for the PV products: measured on MI355X,
+    // agentic chunk 4.75 -> 4.28 ms, outputs bit-identical).
+    __builtin_amdgcn_iglp_opt(1);
     // ---- S^T = K Q^T: lane (query col, grp) of tile n holds keys 16t + 4grp + i of key tile t;
     // each K operand read from LDS feeds the NT query tiles
     float sc[NT][4][4];
@@ -281,6 +286,7 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[n][t][i] = __builtin_amdgcn_exp2f(fmaf(sc[n][t][i], cs, -m[n]));
 
+    __builtin_amdgcn_iglp_opt(0);
     // ---- O^T += V^T P^T over key-tile pairs: k-slot (grp, e) is key 16t + 4grp + e (e < 4)
     // or 16(t + 1) + 4grp + e - 4, the same keys the lane holds in sc[n][t], sc[n][t + 1]
 #pragma unroll
