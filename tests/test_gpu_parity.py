@@ -621,6 +621,35 @@ def test_decode_group_and_shape_coverage(nk, shape):
     decode_problem(nk, inp, splits_list=(1, 3), variants=(None, nk.VARIANT_VALU), label=f"G{G}-H{H}-d{d}-P{P}")
 
 
+@pytest.mark.parametrize("case", range(10))
+def test_decode_randomized_shapes(nk, case):
+    """Seeded random combinations of the shape dimensions the fixed cases take
+    one at a time: batch, query group (odd sizes included), KV heads, head_dim,
+    page size, ragged lengths within the batch (zeros included), pages of one
+    sequence aliased by another, and split counts from 1 to more splits than
+    pages; quantize bytes exact and every decode variant within tolerance."""
+    rng = np.random.default_rng(4242 + case)
+    G = int(rng.choice([1, 2, 3, 5, 6, 8, 12, 16]))
+    H = int(rng.choice([1, 2, 3]))
+    d = int(rng.choice([64, 128]))
+    P = int(rng.choice([16, 32, 48, 64]))
+    B = int(rng.integers(1, 6))
+    ctx = int(rng.integers(1, 801))
+    wl = synth.Workload(200 + case, "random", B, G * H, H, d, P, ctx, bool(rng.integers(0, 2)), 0)
+    inp = synth.host_uniform_decode(wl)
+    inp.seq_lens[:] = rng.integers(0, ctx + 1, B).astype(np.int32)
+    inp.seq_lens[int(rng.integers(0, B))] = ctx
+    alias = B > 1 and bool(rng.integers(0, 2))
+    if alias:   # sequence 1 reads sequence 0's leading pages (a shared prefix)
+        k = int(rng.integers(1, inp.block_tables.shape[1] + 1))
+        inp.block_tables[1, :k] = inp.block_tables[0, :k]
+    splits = tuple(int(x) for x in rng.choice([0, 1, 2, 3, 5, 9, 17, 64], size=2, replace=False))
+    say(f"case decode random {case}: B {B} G {G} Hkv {H} d {d} P {P} ctx {ctx} lens {inp.seq_lens.tolist()} "
+        f"alias {alias} splits {splits}")
+    decode_problem(nk, inp, splits_list=splits,
+                   variants=(None, nk.VARIANT_VALU, nk.VARIANT_MFMA, nk.VARIANT_MFMA_LUT), label=f"random{case}")
+
+
 @pytest.mark.parametrize("shape", [(8, 128, 16, 4096), (4, 64, 32, 700), (5, 128, 64, 3000)])
 def test_decode_lut_unpack_matches_conversion(nk, shape):
     """The register-LUT E2M1 unpack and the conversion-instruction unpack give
