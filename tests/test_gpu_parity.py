@@ -573,6 +573,47 @@ def test_extend_attention_long_prefix(nk, G, d, sm_sign):
     check_out(out, ref, mass, f"extend long G{G} d{d} sm{sm:+.3f}")
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_extend_attention_randomized(nk, case):
+    """Seeded random extend problems: batch, query group, KV heads, head_dim,
+    ragged prefixes and chunks (zeros included), spare workspace rows between
+    sequences, a max_chunk above the longest chunk and either sign of the logit
+    scale; against the oracle."""
+    rng = np.random.default_rng(5151 + case)
+    B = int(rng.integers(1, 6))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 3]))
+    d = int(rng.choice([64, 128]))
+    Hq = G * Hkv
+    prefix = rng.integers(0, 701, B).astype(np.int32)
+    chunk = rng.integers(0, 261, B).astype(np.int32)
+    full = int(rng.integers(0, B))
+    chunk[full] = int(rng.integers(1, 261))                     # at least one query
+    if case % 2 == 0:
+        prefix[0] = 0                                           # an empty prefix
+    if B > 1 and case % 3 == 0:
+        chunk[(full + 1) % B] = 0                               # an empty chunk
+    spare = rng.integers(0, 6, B)
+    ws_offs = np.zeros(B + 1, np.int64)
+    ws_offs[1:] = np.cumsum(prefix + chunk + spare)
+    rows = int(ws_offs[-1])
+    sm = float(rng.choice([1.0, -1.0])) / math.sqrt(d)
+    say(f"case extend random {case}: B {B} G {G} Hkv {Hkv} d {d} prefix {prefix.tolist()} chunk {chunk.tolist()} "
+        f"sm {sm:+.3f}")
+    kb = synth.host_values(rng, (rows, Hkv, d))
+    vb = synth.host_values(rng, (rows, Hkv, d))
+    q_offs = np.zeros(B + 1, np.int64)
+    q_offs[1:] = np.cumsum(chunk)
+    qb = synth.host_values(rng, (int(chunk.sum()), Hq, d))
+    out = nk.nvfp4_extend_attn(synth.to_device_bf16(qb), synth.to_device(q_offs), synth.to_device_bf16(kb),
+                               synth.to_device_bf16(vb), synth.to_device(ws_offs), synth.to_device(prefix), sm,
+                               max_chunk=int(chunk.max()) + int(rng.integers(0, 40)))
+    torch.cuda.synchronize()
+    ref, mass = oatt.extend_attention(synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb),
+                                      synth.bf16_bits_to_f64(vb), q_offs, ws_offs, prefix, sm)
+    check_out(out, ref, mass, f"extend random {case}")
+
+
 # ---------------------------------------------------------------------------
 # decode attention
 # ---------------------------------------------------------------------------
