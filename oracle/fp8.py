@@ -27,10 +27,12 @@ def quantize_rows(x_bits: np.ndarray, scale: float = 1.0) -> np.ndarray:
 
 def write_cache(cache: np.ndarray, x_bits: np.ndarray, slot_mapping: np.ndarray,
                 scale: float = 1.0) -> None:
+    """Token row i goes to physical slot slot_mapping[i]; a slot below 0 or past
+    the pool (>= pages * page_size) skips the token."""
     P = cache.shape[2]
     rows = quantize_rows(x_bits, scale)
     sm = np.asarray(slot_mapping, dtype=np.int64)
-    keep = sm >= 0
+    keep = (sm >= 0) & (sm < cache.shape[0] * P)
     cache[sm[keep] // P, :, sm[keep] % P, :] = rows[keep]
 
 

@@ -183,11 +183,12 @@ def empty_cache(num_pages: int, num_kv_heads: int, page_size: int, head_dim: int
 
 def write_cache(data: np.ndarray, scale: np.ndarray, x_bits: np.ndarray,
                 slot_mapping: np.ndarray, gs: float = 1.0) -> None:
-    """Quantize-on-write: token row i goes to physical slot slot_mapping[i] (< 0: skipped)."""
+    """Quantize-on-write: token row i goes to physical slot slot_mapping[i]; a slot
+    below 0 or past the pool (>= pages * page_size) skips the token."""
     P = data.shape[2]
     rd, rs = quantize_rows(x_bits, gs)
     sm = np.asarray(slot_mapping, dtype=np.int64)
-    keep = sm >= 0
+    keep = (sm >= 0) & (sm < data.shape[0] * P)
     page, off = sm[keep] // P, sm[keep] % P
     data[page, :, off, :] = rd[keep]
     scale[page, :, off, :] = rs[keep]

@@ -355,6 +355,60 @@ def test_dequant_workspace_agentic_small(nk, shape):
     assert np.array_equal(synth.bf16_tensor_bits(vws), vref)
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_quantize_and_workspace_randomized(nk, case):
+    """Seeded random geometries (KV heads, head_dim, page size), tokens written
+    to a random permutation of slots with some skipped (negative or past the
+    pool), then ragged prefixes dequantized through block tables whose
+    leading pages are sometimes shared: pool bytes and workspace bits exact,
+    untouched bytes and spare rows unchanged."""
+    rng = np.random.default_rng(6161 + case)
+    H = int(rng.choice([1, 2, 3, 5]))
+    d = int(rng.choice([64, 128]))
+    P = int(rng.choice([16, 32, 48, 64]))
+    B = int(rng.integers(1, 6))
+    gs = [1.0, 0.25, GS_THIRD][case % 3]
+    lens = rng.integers(0, 400, B).astype(np.int32)
+    pages_per = max(1, int(-(-lens.max() // P)))
+    num_pages = B * pages_per + int(rng.integers(0, 4))
+    bt = rng.permutation(num_pages)[:B * pages_per].astype(np.int32).reshape(B, pages_per)
+    if B > 1 and case % 2 == 0:                        # sequence 1 shares sequence 0's first page(s)
+        k = int(rng.integers(1, pages_per + 1))
+        bt[1, :k] = bt[0, :k]
+    toks = [(b, t) for b in range(B) for t in range(int(lens[b]))
+            if not (B > 1 and case % 2 == 0 and b == 1 and t < k * P)]   # shared pages are written once
+    T = len(toks)
+    slots = np.array([int(bt[b, t // P]) * P + t % P for b, t in toks], np.int64)
+    extra = np.array([-1, -5, num_pages * P, num_pages * P + 3], np.int64)  # skipped slots
+    kb = synth.host_values(rng, (T + 4, H, d))
+    vb = synth.host_values(rng, (T + 4, H, d))
+    all_slots = np.concatenate([slots, extra])
+    order = rng.permutation(T + 4)
+    say(f"case quantize+workspace random {case}: H {H} d {d} P {P} B {B} gs {gs} lens {lens.tolist()} pages {num_pages}")
+    kp, vp = gpu_quantize_nv(nk, num_pages, H, P, d, kb[order], vb[order], all_slots[order], gs)
+    kd, ks, vd, vs = oracle_nv(num_pages, H, P, d, kb[order], vb[order], all_slots[order], gs)
+    assert_pool_equal(kp.data, kd, "K data")
+    assert_pool_equal(kp.scale, ks, "K scale")
+    assert_pool_equal(vp.data, vd, "V data")
+    assert_pool_equal(vp.scale, vs, "V scale")
+    prefix = np.array([int(rng.integers(0, n + 1)) for n in lens], np.int32)
+    ws_offs = np.zeros(B + 1, np.int64)
+    ws_offs[1:] = np.cumsum(lens + rng.integers(0, 4, B))
+    rows = max(1, int(ws_offs[-1]))
+    kws = torch.full((rows, H, d), -7.0, dtype=torch.bfloat16, device="cuda")
+    vws = torch.full((rows, H, d), -7.0, dtype=torch.bfloat16, device="cuda")
+    nk.nvfp4_kv_dequant_workspace(kp, vp, synth.to_device(bt), synth.to_device(prefix), synth.to_device(ws_offs),
+                                  kws, vws)
+    torch.cuda.synchronize()
+    fill = int(synth.bf16_tensor_bits(torch.tensor([-7.0], dtype=torch.bfloat16))[0])
+    kref = oatt.dequant_workspace(onv.dequant_cache(kd, ks, gs), bt, prefix, ws_offs, rows, fill,
+                                  cache_bits=onv.workspace_bits(kd, ks, gs))
+    vref = oatt.dequant_workspace(onv.dequant_cache(vd, vs, gs), bt, prefix, ws_offs, rows, fill,
+                                  cache_bits=onv.workspace_bits(vd, vs, gs))
+    assert np.array_equal(synth.bf16_tensor_bits(kws), kref)
+    assert np.array_equal(synth.bf16_tensor_bits(vws), vref)
+
+
 @pytest.mark.parametrize("fp8_ws", [False, True])
 def test_dequant_workspace_every_scale_byte(nk, fp8_ws):
     """Pools written directly with every finite E4M3 scale byte (both signs,

@@ -204,7 +204,8 @@ def test_nibble_order_and_cache_layout():
     P, H, d = 16, 2, 32
     x = _bf16_bits(formats.E2M1_VALUES[rng.integers(0, 16, size=(3, H, d))])
     data, scale = nvfp4.empty_cache(4, H, P, d, fill=0xAB)
-    nvfp4.write_cache(data, scale, x, np.array([2 * P + 5, -1, 0 * P + 15]))
+    # a negative slot and one past the pool (4 pages * P) skip their rows, as the entry point does
+    nvfp4.write_cache(data, scale, np.concatenate([x, x[:1]]), np.array([2 * P + 5, -1, 0 * P + 15, 4 * P]))
     rd, rs = nvfp4.quantize_rows(x)
     assert np.array_equal(data[2, :, 5], rd[0]) and np.array_equal(scale[2, :, 5], rs[0])
     assert np.array_equal(data[0, :, 15], rd[2]) and np.array_equal(scale[0, :, 15], rs[2])
