@@ -722,7 +722,8 @@ def test_decode_randomized_shapes(nk, case):
     one at a time: batch, query group (odd sizes included), KV heads, head_dim,
     page size, ragged lengths within the batch (zeros included), pages of one
     sequence aliased by another, and split counts from 1 to more splits than
-    pages; quantize bytes exact and every decode variant within tolerance."""
+    pages; quantize bytes exact and every decode variant within tolerance, for
+    the NVFP4 cache and the FP8-E4M3 baseline cache."""
     rng = np.random.default_rng(4242 + case)
     G = int(rng.choice([1, 2, 3, 5, 6, 8, 12, 16]))
     H = int(rng.choice([1, 2, 3]))
@@ -743,6 +744,30 @@ def test_decode_randomized_shapes(nk, case):
         f"alias {alias} splits {splits}")
     decode_problem(nk, inp, splits_list=splits,
                    variants=(None, nk.VARIANT_VALU, nk.VARIANT_MFMA, nk.VARIANT_MFMA_LUT), label=f"random{case}")
+    # the same problem over the FP8-E4M3 baseline cache
+    kf, vf = f8_pools(nk, inp.num_pages, H, P, d)
+    nk.fp8_kv_quantize(synth.to_device_bf16(inp.k), synth.to_device_bf16(inp.v), synth.to_device(inp.slot_mapping),
+                       kf, vf)
+    kr = np.full((inp.num_pages, H, P, d), SENT, np.uint8)
+    vr = kr.copy()
+    of8.write_cache(kr, inp.k, inp.slot_mapping)
+    of8.write_cache(vr, inp.v, inp.slot_mapping)
+    torch.cuda.synchronize()
+    assert_pool_equal(kf.data, kr, "fp8 K")
+    assert_pool_equal(vf.data, vr, "fp8 V")
+    ref, mass = oatt.paged_decode(inp.q, of8.dequant_cache(kr), of8.dequant_cache(vr), inp.block_tables,
+                                  inp.seq_lens, wl.sm_scale)
+    q, bt, sl = synth.to_device_bf16(inp.q), synth.to_device(inp.block_tables), synth.to_device(inp.seq_lens)
+    for S in splits:
+        out = nk.fp8_paged_decode_attn(q, kf, vf, bt, sl, wl.sm_scale, num_splits=S)
+        torch.cuda.synchronize()
+        check_out(out, ref, mass, f"random{case} fp8 splits={S}")
+    Sx = splits[0] or nk.nvfp4_paged_decode_num_splits(B, H, bt.shape[1], P)
+    ws = nk.fp8_paged_decode_partial(q, kf, vf, bt, sl, wl.sm_scale, Sx, variant=nk.VARIANT_VALU)
+    out = torch.empty_like(q)
+    nk.nvfp4kv_lse_merge(ws, B, G * H, d, Sx, vf.scale, out)
+    torch.cuda.synchronize()
+    check_out(out, ref, mass, f"random{case} fp8 VALU")
 
 
 @pytest.mark.parametrize("shape", [(8, 128, 16, 4096), (4, 64, 32, 700), (5, 128, 64, 3000)])
