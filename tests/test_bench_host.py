@@ -1,0 +1,46 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU guard, the algorithmic
+byte counts behind the roofline figure, and the traffic read-back's guard on
+the decode kernel's source digest."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_algorithmic_bytes_of_the_long_context_decode_launch():
+    """KV packed + scales (144 B per token per KV head at d = 128), q in bf16 and
+    the fp32 partials: 1,690,681,344 B per launch at 32K, batch 44, 32 splits."""
+    wl = synth.WORKLOADS[3]
+    assert (wl.batch, wl.context, wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.num_splits) == \
+        (44, 32768, 8, 40, 128, 32)
+    kvb = bench.kv_bytes(wl)
+    assert kvb == 44 * 32768 * 8 * 144
+    alg = kvb + wl.batch * wl.num_q_heads * wl.head_dim * 2 + bench.partial_bytes(wl, wl.num_splits)
+    assert alg == 1_690_681_344
+    # the FP8 cache moves d bytes per element pair instead of d/2 + d/16: 1/0.5625 as many
+    assert bench.kv_bytes(wl, fp8=True) * 9 == kvb * 16
+
+
+def test_traffic_read_back_follows_the_source_digest(tmp_path, monkeypatch):
+    assert bench.read_traffic("no_such_kernel") is None
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "k_traffic.txt").write_text(f"# comment: ignored\nsource_digest: {bench.source_digest()}\n"
+                                        "hbm_bytes_per_launch: 1234\n")
+    (prof / "old_traffic.txt").write_text("source_digest: 0000000000000000\nhbm_bytes_per_launch: 1234\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "DECODE_SOURCES", [os.path.join(ROOT, p) for p in bench.DECODE_SOURCES])
+    assert bench.read_traffic("k") == 1234.0
+    assert bench.read_traffic("old") is None
