@@ -233,6 +233,20 @@ __device__ inline void load_chunk(const DecodeParams& p, const Item& it, int ts,
   for (int t = 0; t < Cfg<D, FP8, T>::kTiles; ++t) load_tile<D, FP8, T, PW>(p, it, ts + 16 * t, lane, buf[t]);
 }
 
+// Maximum over the four 16-lane rows (lanes i, i^16, i^32, i^48) on the VALU:
+// gfx950's row swaps exchange rows 0<->1 and 2<->3 (16) or rows 0,1<->2,3 (32)
+// of a register with itself, so each lane sees its partner's value without the
+// LDS permutes a shuffle compiles to (measured on MI355X: ~1% at 32K and 1M,
+// partials bit-identical).
+__device__ inline float max_over_rows(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 // Running softmax state and output accumulators of one wave.
 template <int D>
 struct Acc {
@@ -284,8 +298,7 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
   for (int t = 0; t < C::kTiles; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[t][i]);
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  cmax = max_over_rows(cmax);
   const float mnew = fmaxf(a.m, cmax * cs);
   const float alpha = __builtin_amdgcn_exp2f(a.m - mnew);
   a.m = mnew;
