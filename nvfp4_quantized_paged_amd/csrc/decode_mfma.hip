@@ -27,8 +27,9 @@
 //    layout (lane (c, g) = tokens 4g..4g+3 of channel c), exactly (one
 //    nonzero product per output). Two such outputs, packed to f16, are the A
 //    operand of O^T[c][h] += V^T[c][t] P[t][h], and the softmax output C of
-//    the same two tiles is already the B operand in the same lane: no
-//    cross-lane data movement anywhere in the loop.
+//    the same two tiles is already the B operand in the same lane: the only
+//    cross-lane step in the loop is the softmax's maximum over the four lane
+//    rows of a head (two VALU row swaps), and no LDS is used.
 //  * Loads: buffer loads with a fixed per-lane offset and a scalar offset
 //    (page from the block table, clamped into the pool), so no vector ALU
 //    goes into addressing. Pools below 2 GiB use one descriptor per array,
