@@ -397,6 +397,7 @@ def cpu_baseline(wl, budget_s=12.0):
                   f"softmax attention of {wl.group} query heads over {wl.context} tokens each, "
                   f"{elapsed:.1f}s on 1 thread (BLAS limited to 1)",
         "steps_per_s": round(gbs * 1e9 / step_bytes, 6),
+        "host_cpus": os.cpu_count(), "host_cpus_usable": len(os.sched_getaffinity(0)), "blas_threads": 1,
     }
 
 

@@ -1,6 +1,6 @@
 """Host-side checks of bench.py (no GPU): the one-GPU guard, the algorithmic
 byte counts behind the roofline figure, and the traffic read-back's guard on
-the decode kernel's source digest."""
+the decode kernel's source digest; the CPU-oracle baseline's report."""
 import os
 import subprocess
 import sys
@@ -44,3 +44,12 @@ def test_traffic_read_back_follows_the_source_digest(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "DECODE_SOURCES", [os.path.join(ROOT, p) for p in bench.DECODE_SOURCES])
     assert bench.read_traffic("k") == 1234.0
     assert bench.read_traffic("old") is None
+
+
+def test_cpu_baseline_reports_the_oracle_and_the_host_cores():
+    # the tiny decode workload, a fraction of a second of oracle work
+    res = bench.cpu_baseline(synth.WORKLOADS[1], budget_s=0.2)
+    assert res["kind"] == "oracle" and res["unit"] == "GB/s" and res["cores"] == 1
+    assert res["value"] > 0 and res["steps_per_s"] > 0
+    assert res["host_cpus"] >= res["host_cpus_usable"] >= 1 and res["blas_threads"] == 1
+    assert "slices of" in res["sample"]
