@@ -539,3 +539,120 @@ def test_extend_attention_pins():
             w = [math.exp(x - mx) for x in s]
             o = [sum(w[j] * v[j, g, c] for j in range(L + i + 1)) / sum(w) for c in range(d)]
             assert np.allclose(out[i, h], o, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding (the workspace at a calibrated scale, and the input generator)
+# ---------------------------------------------------------------------------
+
+def _bf16_rounding_cases(n_random=4_000_000):
+    """float32 bit patterns that decide a bf16 rounding rule: every finite bf16
+    value's exact halfway point to its upper neighbour (both signs), one f32
+    ulp either side of it, the value itself, plus random finite patterns."""
+    b = np.arange(1 << 15, dtype=np.uint32)                      # non-negative bf16 patterns
+    b = b[(b & 0x7F80) != 0x7F80]                                 # finite only
+    hi = np.concatenate([b, b | 0x8000]) << 16                    # both signs
+    pats = np.concatenate([hi, hi | 0x8000, hi | 0x7FFF, hi | 0x8001, hi | 0x0001])
+    rng = np.random.default_rng(40)
+    r = rng.integers(0, 1 << 32, size=n_random, dtype=np.uint64).astype(np.uint32)
+    r = r[(r & 0x7F800000) != 0x7F800000]
+    return np.concatenate([pats, r]).astype(np.uint32).view(np.float32)
+
+
+def _torch_bf16_bits(x):
+    """torch's CPU float32 -> bfloat16 cast, an independent round-to-nearest-even."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rounding_matches_torch():
+    """oracle f32_to_bf16_rne (the last step of the workspace value at any
+    calibrated scale) and the input generator's rounding, against torch's
+    float32 -> bfloat16 cast on every halfway point and 4M random patterns."""
+    x = _bf16_rounding_cases()
+    want = _torch_bf16_bits(x)
+    assert np.array_equal(nvfp4.f32_to_bf16_rne(x), want)
+    import synth
+    assert np.array_equal(synth.f32_to_bf16_bits(x), want)
+
+
+def test_bf16_rounding_pin_catches_planted_mistakes():
+    """Truncation, or ties rounded away from zero, must fail the torch pin."""
+    x = _bf16_rounding_cases(n_random=0)
+    want = _torch_bf16_bits(x)
+    u = x.view(np.uint32).astype(np.uint64)
+    truncate = (u >> 16).astype(np.uint16)
+    ties_away = ((u + 0x8000) >> 16).astype(np.uint16)
+    assert not np.array_equal(truncate, want)
+    assert not np.array_equal(ties_away, want)
+
+
+def test_workspace_bits_at_a_calibrated_scale_match_torch():
+    """Every workspace value bf16(fl32(e2m1 * fl32(S * gs))) at gs = fl32(1/3):
+    all 16 E2M1 codes under every finite E4M3 scale byte, against the same
+    float32 products and bf16 cast done in torch from torch's own E4M3 decode."""
+    gs = np.float32(1.0 / 3.0)
+    e2m1 = np.loadtxt(os.path.join(GOLDEN, "e2m1_magnitudes.txt"), dtype=np.float32)
+    e2m1 = np.concatenate([e2m1, -e2m1])                              # codes 0..15
+    sbytes = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    s_t = torch.from_numpy(sbytes).view(torch.float8_e4m3fn).float()
+    prod = torch.from_numpy(e2m1)[None, :] * (s_t * torch.tensor(gs))[:, None]   # [scales][16]
+    want = prod.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    codes = np.arange(16, dtype=np.uint8)
+    data = np.tile((codes[0::2] | (codes[1::2] << 4)).astype(np.uint8), (sbytes.size, 1))  # [scales][8]
+    got = nvfp4.workspace_bits(data, sbytes[:, None], float(gs))
+    assert np.array_equal(got, want)
+    assert np.count_nonzero(prod.numpy() != prod.to(torch.bfloat16).float().numpy()) > 0   # rounding happens
+
+
+# ---------------------------------------------------------------------------
+# non-finite elements under the FP32 recipe
+# ---------------------------------------------------------------------------
+
+def _nonfinite_vectors():
+    cases = []
+    with open(os.path.join(GOLDEN, "nvfp4_nonfinite_blocks.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, gs, xs, s, data = [p.strip() for p in line.split("|")]
+            bits = np.array([int(t, 16) for t in xs.split()], np.uint16)
+            cases.append((name, float(gs), bits, int(s, 16), [int(t, 16) for t in data.split()]))
+    return cases
+
+
+def _encode_golden_bits(bits, gs, enc=None):
+    with np.errstate(invalid="ignore", over="ignore"):
+        codes, s = (enc or nvfp4.encode_blocks_fp32)(nvfp4.bf16_to_f64(bits).reshape(1, 16), gs)
+    return int(s[0]), list(nvfp4.pack_nibbles(codes)[0])
+
+
+@pytest.mark.parametrize("case", _nonfinite_vectors(), ids=lambda c: c[0])
+def test_nonfinite_blocks_golden(case):
+    name, gs, bits, s_exp, data_exp = case
+    assert np.float32(gs) == np.float32(1.0) or np.float32(gs) == np.float32(1.0 / 3.0)
+    s, data = _encode_golden_bits(bits, gs)
+    assert s == s_exp, (name, hex(s))
+    assert data == data_exp, (name, [hex(v) for v in data])
+
+
+def test_nonfinite_pin_catches_planted_mistakes():
+    """Two plausible mistakes in the non-finite handling must fail the golden
+    blocks: NaN taking the saturated code 7, and a block maximum that
+    propagates NaN (np.max) instead of ignoring it."""
+    cases = _nonfinite_vectors()
+
+    def nan_code_seven(x, gs):
+        c, s = nvfp4.encode_blocks_fp32(x, gs)
+        return np.where(np.isnan(x), (c & 8) | 7, c).astype(np.uint8), s
+
+    def nan_propagating_max(x, gs):
+        c, s = nvfp4.encode_blocks_fp32(x, gs)
+        amax = np.max(np.abs(x), axis=-1)
+        s = np.where(np.isnan(amax), 0x7F, s).astype(np.uint8)
+        return c, s
+
+    for planted in (nan_code_seven, nan_propagating_max):
+        bad = sum(_encode_golden_bits(bits, gs, planted) != (s_exp, data_exp)
+                  for _, gs, bits, s_exp, data_exp in cases)
+        assert bad > 0, planted.__name__
