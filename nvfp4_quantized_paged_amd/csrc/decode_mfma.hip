@@ -17,8 +17,9 @@
 //    product is exact in f16, so the dequantized K/V are exact.
 //  * QK: A = K (16 tokens x 32 channels per MFMA; one 128-bit load per lane
 //    covers four MFMAs: lane (row r, group g) holds channels
-//    [g*D/4, (g+1)*D/4) of token r), B = q (f16, scaled into f16 range by a
-//    power of two). C[t][h]: lane (h, g) holds tokens 4g..4g+3 of the tile.
+//    [g*D/4, (g+1)*D/4) of token r), B = q (f16, moved into f16's top binade
+//    by a power of two, up or down). C[t][h]: lane (h, g) holds tokens
+//    4g..4g+3 of the tile.
 //  * Softmax in base 2, f32, running max and per-lane sums per head; the
 //    output accumulators are rescaled only when some head's max grows.
 //  * PV contracts over tokens, but a lane holds channels of one token. The
@@ -46,7 +47,6 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer descriptor, 32-bit data format
 // Cache policy of the K/V loads. The NVFP4 stream uses non-temporal loads
@@ -141,9 +141,13 @@ __device__ inline half8_t unpack(const uint32_t* words, uint32_t scale_bits, int
   }
 }
 
+// Two f32 -> packed f16 pair, round to nearest even (v_cvt_pk_f16_f32): the
+// softmax numerators P and the transposed V values go to the PV product
+// without the one-sided error of a round-toward-zero conversion.
 __device__ inline uint32_t pack_f16x2(float a, float b) {
-  const fp16x2_t r = __builtin_amdgcn_cvt_pkrtz(a, b);
-  return __builtin_bit_cast(uint32_t, r);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
 }
 
 __device__ inline half8_t pack_half8(const float4_t& x, const float4_t& y) {
@@ -388,17 +392,19 @@ void decode_partial_mfma_kernel(DecodeParams p) {
     }
     qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
     qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
-    // power-of-two shift keeping the head's largest |q| below 2^15 in f16; the
-    // sign of the logit scale moves into q so that the scale is positive
-    const int qexp = (qmax > 0.0f) ? max(0, (int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 14) : 0;
+    // power-of-two shift bringing the head's largest |q| into [2^14, 2^15), the
+    // top binade of f16, up or down, so small queries keep f16's full precision
+    // instead of becoming subnormals; undone in the logit scale. The sign of the
+    // logit scale moves into q so that the scale is positive.
+    const int qexp = (qmax > 0.0f) ? min(max((int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127 - 14, -126), 113) : 0;
     const float sgn = p.qk_scale < 0.0f ? -1.0f : 1.0f;
-    const float qdown = sgn * __uint_as_float((uint32_t)(127 - qexp) << 23);
+    const float qshift = __builtin_ldexpf(sgn, -qexp);
     half8_t qb[C::kKSteps];
 #pragma unroll
     for (int kk = 0; kk < C::kKSteps; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qb[kk][e] = (_Float16)(qf[kk][e] * qdown);
-    const float cs = fabsf(p.qk_scale) * __uint_as_float((uint32_t)(127 + qexp) << 23);
+      for (int e = 0; e < 8; ++e) qb[kk][e] = (_Float16)(qf[kk][e] * qshift);
+    const float cs = __builtin_ldexpf(fabsf(p.qk_scale), qexp);
 
     // ---- 0/1 selection operands for the V transposes: column n takes A slot (group 2hs + n/8, item n%8)
     half8_t sel[2];

@@ -92,7 +92,7 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
   const int chunk = (int)__builtin_amdgcn_readfirstlane((int)(p.q_row_offsets[b + 1] - q_begin));
   const int qblk = qb_idx * C::kQPerGroup;
   if (qblk >= chunk) return;                                   // uniform over the workgroup
-  const int L = __builtin_amdgcn_readfirstlane(p.prefix_lens[b]);
+  const int L = max(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), 0);   // a negative prefix is empty
   const int64_t kv0 = p.ws_row_offsets[b];
   const int nkeys = L + min(chunk, qblk + C::kQPerGroup);       // keys any query of this workgroup sees
   const int qw = qblk + (wave / C::kHeadWaves) * C::kQPerWave;  // first query of this wave

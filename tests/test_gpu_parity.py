@@ -627,6 +627,33 @@ def test_extend_attention_long_prefix(nk, G, d, sm_sign):
     check_out(out, ref, mass, f"extend long G{G} d{d} sm{sm:+.3f}")
 
 
+def test_extend_attention_negative_prefix_is_empty(nk):
+    """A negative prefix length is taken as an empty prefix: the chunk's
+    queries attend causally to the chunk alone, read from the rows at the
+    sequence's workspace offset; against the oracle with prefix 0."""
+    rng = np.random.default_rng(8)
+    G, Hkv, d = 4, 2, 128
+    chunk = np.array([70, 33], np.int32)
+    prefix = np.array([-5, -100000], np.int32)
+    B = len(chunk)
+    say(f"case extend negative prefix: prefix {prefix.tolist()} chunk {chunk.tolist()}")
+    ws_offs = np.zeros(B + 1, np.int64)
+    ws_offs[1:] = np.cumsum(chunk + 2)
+    rows = int(ws_offs[-1])
+    kb = synth.host_values(rng, (rows, Hkv, d))
+    vb = synth.host_values(rng, (rows, Hkv, d))
+    q_offs = np.zeros(B + 1, np.int64)
+    q_offs[1:] = np.cumsum(chunk)
+    qb = synth.host_values(rng, (int(chunk.sum()), G * Hkv, d))
+    sm = 1.0 / math.sqrt(d)
+    out = nk.nvfp4_extend_attn(synth.to_device_bf16(qb), synth.to_device(q_offs), synth.to_device_bf16(kb),
+                               synth.to_device_bf16(vb), synth.to_device(ws_offs), synth.to_device(prefix), sm)
+    torch.cuda.synchronize()
+    ref, mass = oatt.extend_attention(synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb),
+                                      synth.bf16_bits_to_f64(vb), q_offs, ws_offs, np.zeros(B, np.int32), sm)
+    check_out(out, ref, mass, "extend negative prefix")
+
+
 @pytest.mark.parametrize("case", range(8))
 def test_extend_attention_randomized(nk, case):
     """Seeded random extend problems: batch, query group, KV heads, head_dim,
@@ -790,6 +817,97 @@ def test_decode_global_scale(nk, gs):
     inp = synth.host_uniform_decode(wl)
     say(f"case decode global scale {gs}")
     decode_problem(nk, inp, splits_list=(2,), variants=(None,), gs=gs, label=f"gs{gs:.4g}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_many_splits_against_oracle(nk, d):
+    """Split counts above 64 (the merge's 16-wave branch) up to 1024, so that
+    most splits of the shorter sequence are empty, through the one-call
+    decode and the separate partial + merge with each kernel variant, over the
+    NVFP4 cache and the FP8-E4M3 cache; whole outputs against the oracle."""
+    wl = synth.Workload(94, "many-splits", 2, 10, 2, d, 16, 4096, True, 0)
+    inp = synth.host_uniform_decode(wl)
+    inp.seq_lens[1] = 1000
+    splits = (65, 200, 256, 1024)
+    say(f"case decode many splits: d {d} lens {inp.seq_lens.tolist()} splits {splits}")
+    decode_problem(nk, inp, splits_list=splits, variants=(None, nk.VARIANT_MFMA, nk.VARIANT_VALU),
+                   label=f"many-splits d{d}")
+    H, P = wl.num_kv_heads, wl.page_size
+    kf, vf = f8_pools(nk, inp.num_pages, H, P, d)
+    nk.fp8_kv_quantize(synth.to_device_bf16(inp.k), synth.to_device_bf16(inp.v), synth.to_device(inp.slot_mapping),
+                       kf, vf)
+    kr = np.full((inp.num_pages, H, P, d), SENT, np.uint8)
+    vr = kr.copy()
+    of8.write_cache(kr, inp.k, inp.slot_mapping)
+    of8.write_cache(vr, inp.v, inp.slot_mapping)
+    ref, mass = oatt.paged_decode(inp.q, of8.dequant_cache(kr), of8.dequant_cache(vr), inp.block_tables,
+                                  inp.seq_lens, wl.sm_scale)
+    q, bt, sl = synth.to_device_bf16(inp.q), synth.to_device(inp.block_tables), synth.to_device(inp.seq_lens)
+    for S in splits:
+        out = nk.fp8_paged_decode_attn(q, kf, vf, bt, sl, wl.sm_scale, num_splits=S)
+        torch.cuda.synchronize()
+        check_out(out, ref, mass, f"many-splits d{d} fp8 splits={S}")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_decode_small_queries_with_a_large_key_scale(nk, fmt):
+    """Queries around 1e-6 against keys carried by a tensor scale of 2^16 (the
+    stored K codes are those of ordinary N(0,1) keys): logits of ordinary size
+    from a query far below f16's normal range. The query's power-of-two shift
+    into f16 must go up as well as down, or its elements become f16
+    subnormals with a few bits left. Against the oracle, NVFP4 and FP8."""
+    wl = synth.Workload(89, "small-q", 3, 12, 3, 128, 16, 900, True, 0)
+    inp = synth.host_uniform_decode(wl)
+    H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
+    gk = 2.0 ** 16
+    k_bits = synth.f32_to_bf16_bits((synth.bf16_bits_to_f64(inp.k) * gk).astype(np.float32))    # exact
+    q_bits = synth.f32_to_bf16_bits((synth.bf16_bits_to_f64(inp.q) * 1e-6).astype(np.float32))
+    sm = 16.0 / math.sqrt(d)                                   # logits 16 * 2^16 * 1e-6 ~ 1.05 x the N(0,1) ones
+    say(f"case decode small queries: {fmt}, |q| ~ 1e-6, K global scale 2^16, sm_scale {sm:.3f}")
+    q, bt, sl = synth.to_device_bf16(q_bits), synth.to_device(inp.block_tables), synth.to_device(inp.seq_lens)
+    if fmt == "nvfp4":
+        kp, vp = nv_pools(nk, inp.num_pages, H, P, d)
+        kp.global_scale = gk
+        nk.nvfp4_kv_quantize(synth.to_device_bf16(k_bits), synth.to_device_bf16(inp.v),
+                             synth.to_device(inp.slot_mapping), kp, vp)
+        kd, ks = onv.empty_cache(inp.num_pages, H, P, d, fill=SENT)
+        vd, vs = onv.empty_cache(inp.num_pages, H, P, d, fill=SENT)
+        onv.write_cache(kd, ks, k_bits, inp.slot_mapping, gk)
+        onv.write_cache(vd, vs, inp.v, inp.slot_mapping, 1.0)
+        torch.cuda.synchronize()
+        assert_pool_equal(kp.data, kd, "K data")
+        assert_pool_equal(kp.scale, ks, "K scale")
+        khat, vhat = onv.dequant_cache(kd, ks, gk), onv.dequant_cache(vd, vs, 1.0)
+        run = lambda S, var: _decode_out(nk, nk.nvfp4_paged_decode_attn, nk.nvfp4_paged_decode_partial,
+                                         q, kp, vp, bt, sl, sm, S, var, vp.global_scale)
+    else:
+        kf, vf = f8_pools(nk, inp.num_pages, H, P, d)
+        kf.scale = gk
+        nk.fp8_kv_quantize(synth.to_device_bf16(k_bits), synth.to_device_bf16(inp.v),
+                           synth.to_device(inp.slot_mapping), kf, vf)
+        kr = np.full((inp.num_pages, H, P, d), SENT, np.uint8)
+        vr = kr.copy()
+        of8.write_cache(kr, k_bits, inp.slot_mapping, gk)
+        of8.write_cache(vr, inp.v, inp.slot_mapping)
+        torch.cuda.synchronize()
+        assert_pool_equal(kf.data, kr, "fp8 K")
+        khat, vhat = of8.dequant_cache(kr, gk), of8.dequant_cache(vr)
+        run = lambda S, var: _decode_out(nk, nk.fp8_paged_decode_attn, nk.fp8_paged_decode_partial,
+                                         q, kf, vf, bt, sl, sm, S, var, vf.scale)
+    ref, mass = oatt.paged_decode(q_bits, khat, vhat, inp.block_tables, inp.seq_lens, sm)
+    for S, var in ((0, None), (3, nk.VARIANT_MFMA), (3, nk.VARIANT_VALU)):
+        check_out(run(S, var), ref, mass, f"small-q {fmt} splits={S} variant={var}")
+
+
+def _decode_out(nk, attn, partial, q, kp, vp, bt, sl, sm, S, var, out_scale):
+    if var is None:
+        out = attn(q, kp, vp, bt, sl, sm, num_splits=S)
+    else:
+        ws = partial(q, kp, vp, bt, sl, sm, S, variant=var)
+        out = torch.empty_like(q)
+        nk.nvfp4kv_lse_merge(ws, q.shape[0], q.shape[1], q.shape[2], S, out_scale, out)
+    torch.cuda.synchronize()
+    return out
 
 
 @pytest.mark.parametrize("mag", [3.0e4, 1.0e-5])
@@ -1147,9 +1265,10 @@ def test_full_size_long_context_32k_sampled(nk):
 def test_full_size_extreme_context_1m_sampled(nk):
     """Batch 2, 1M context, 256 splits (the benchmark's launch). Each sampled
     split's normalised partial o/l is checked against the oracle's attention
-    over that split's 4,096 tokens, and the merged output against an fp64
+    over that split's 4,096 tokens; the merged output against an fp64
     log-sum-exp merge of all the kernel's partials (a property that holds at
-    any size)."""
+    any size); and one whole (sequence, KV head) output against the oracle
+    over all 1,048,576 tokens."""
     from synth.workload import build_uniform_workload
     wl = synth.WORKLOADS[4]
     S, G, d = wl.num_splits, wl.group, wl.head_dim
@@ -1186,8 +1305,33 @@ def test_full_size_extreme_context_1m_sampled(nk):
     merged = (po * wgt[..., None]).sum(axis=2) / (pml[..., 1] * wgt).sum(axis=2)[..., None]
     got = out.float().cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - merged) <= 2.0 ** -8 * np.abs(merged) + 1e-6), "merge property"
+    # one whole (sequence, KV head) output against the oracle over all 1,048,576 tokens
+    b, g = 1, 6
+    say(f"  whole slice b {b} g {g}: {wl.context} tokens")
+    ref, mass = _oracle_whole_slice(w, b, g)
+    check_out(out[b, g * G:(g + 1) * G], ref, mass, f"{wl.name} b{b} g{g} whole")
     del w, ws
     torch.cuda.empty_cache()
+
+
+def _oracle_whole_slice(w, b, g, piece=1 << 16):
+    """Oracle decode of one (sequence, KV head) over its whole context: the kept
+    bf16 rows are quantized by the oracle piece by piece (the pool bytes checked
+    against them on the way), then float64 attention over all dequantized tokens."""
+    wl = w.wl
+    G, L, d = wl.group, wl.context, wl.head_dim
+    khat = np.empty((L, 1, d))
+    vhat = np.empty((L, 1, d))
+    for t0 in range(0, L, piece):
+        t1 = min(L, t0 + piece)
+        kb, vb = _sample_rows(w, b, g, t0, t1)
+        rd, rs = onv.quantize_rows(kb)
+        _check_sampled_bytes(w, b, g, t0, t1, rd, rs)
+        vd_, vs_ = onv.quantize_rows(vb)
+        khat[t0:t1] = onv.dequant_rows(rd, rs)
+        vhat[t0:t1] = onv.dequant_rows(vd_, vs_)
+    qb = synth.bf16_tensor_bits(w.q[b, g * G:(g + 1) * G])
+    return oatt.decode_heads(onv.bf16_to_f64(qb), khat, vhat, wl.sm_scale)
 
 
 @pytest.mark.parametrize("idx,batch,fp8", [(6, 15, False), (6, 10, True), (3, 70, False), (4, 1, True)],
