@@ -24,7 +24,9 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *    work is enqueued asynchronously on it; no entry point synchronizes.
  *  - Concurrent calls are allowed on different streams if they write
- *    different buffers. The only global state is a thread-local error text.
+ *    different buffers. The global state is a thread-local error text and
+ *    the static partials array of nvfp4_paged_decode_attn_noalloc (one per
+ *    GPU), which only that entry point uses.
  *  - Every entry point validates its arguments on the host before any HIP
  *    call and returns 0 on success or a negative NVFP4KV_E* code; the text
  *    of the last failure on the calling thread is nvfp4kv_last_error().
@@ -244,6 +246,37 @@ int nvfp4_paged_decode_attn(const nvfp4kv_geom* geom, const void* q,
                             const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
                             float sm_scale, int32_t num_splits, void* workspace,
                             size_t workspace_bytes, void* out, void* stream);
+
+/*
+ * nvfp4_paged_decode_attn_noalloc -- nvfp4_paged_decode_attn for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments and result without
+ * the workspace: the fp32 partials go to a static device array of the
+ * library, nvfp4_paged_decode_noalloc_scratch_bytes() = 32 MiB on each GPU it
+ * runs on (allocated with the code object, held until the process ends). The
+ * call itself allocates nothing and calls no allocating routine.
+ *
+ *   num_splits   1..4096 with batch * num_q_heads * num_splits * (head_dim + 2) * 4
+ *                <= 32 MiB, else NVFP4KV_EWORKSPACE; or 0 for the library's
+ *                count (nvfp4_paged_decode_num_splits), lowered so that the
+ *                partials fit (NVFP4KV_EWORKSPACE if one split does not)
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (on different streams, or from different threads without ordering) race
+ * and give undefined results; serialize them, e.g. on one stream. The array
+ * keeps the last call's partials; every partial a call reads it has written
+ * first, so nothing needs clearing. On the first call on a device the
+ * library looks up the array's device address there (hipGetSymbolAddress);
+ * a failure of that lookup is NVFP4KV_ELAUNCH. Other errors as
+ * nvfp4_paged_decode_attn, checked on the host before any HIP call.
+ */
+int nvfp4_paged_decode_attn_noalloc(const nvfp4kv_geom* geom, const void* q,
+                                    const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                                    const int32_t* block_tables, int32_t max_pages_per_seq,
+                                    const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                    float sm_scale, int32_t num_splits, void* out, void* stream);
+
+/* Size in bytes of the static partials array of nvfp4_paged_decode_attn_noalloc. */
+size_t nvfp4_paged_decode_noalloc_scratch_bytes(void);
 
 /*
  * nvfp4_paged_decode_partial -- phase 1 only: writes the partials of every

@@ -56,6 +56,9 @@ _SIGNATURES = {
                                                c_f32, c_i32, c_vp, c_size, c_vp, c_vp]),
     "nvfp4_paged_decode_partial": (ctypes.c_int, [P_GEOM, c_vp, P_NV, P_NV, c_vp, c_i32, c_vp, c_i32, c_i32,
                                                   c_f32, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "nvfp4_paged_decode_attn_noalloc": (ctypes.c_int, [P_GEOM, c_vp, P_NV, P_NV, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                                       c_f32, c_i32, c_vp, c_vp]),
+    "nvfp4_paged_decode_noalloc_scratch_bytes": (c_size, []),
     "fp8_paged_decode_attn": (ctypes.c_int, [P_GEOM, c_vp, P_F8, P_F8, c_vp, c_i32, c_vp, c_i32, c_i32,
                                              c_f32, c_i32, c_vp, c_size, c_vp, c_vp]),
     "fp8_paged_decode_partial": (ctypes.c_int, [P_GEOM, c_vp, P_F8, P_F8, c_vp, c_i32, c_vp, c_i32, c_i32,
@@ -472,6 +475,25 @@ def nvfp4_paged_decode_attn(q, k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_table
     """Decode attention of q [B][Hq][d] (bf16) over the NVFP4 pools; returns out [B][Hq][d] bf16."""
     return _decode("nvfp4_paged_decode_attn", None, q, k_pool, v_pool, block_tables, seq_lens, sm_scale,
                    num_splits, workspace, out, stream)
+
+
+def nvfp4_paged_decode_attn_noalloc(q, k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables, seq_lens, sm_scale,
+                                    out, num_splits=0, stream=None):
+    """nvfp4_paged_decode_attn with the partials in the library's static scratch
+    array: no workspace, and no allocation by the binding either (out is
+    required)."""
+    B, Hq, d = _decode_args(q, block_tables, seq_lens)
+    g = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, out)
+    _need(out, torch.bfloat16, "out")
+    _check(lib().nvfp4_paged_decode_attn_noalloc(
+        ctypes.byref(g), q.data_ptr(), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()),
+        block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(), B, Hq, float(sm_scale),
+        int(num_splits), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def nvfp4_paged_decode_noalloc_scratch_bytes() -> int:
+    return int(lib().nvfp4_paged_decode_noalloc_scratch_bytes())
 
 
 def fp8_paged_decode_attn(q, k_pool: FP8Pool, v_pool: FP8Pool, block_tables, seq_lens, sm_scale,

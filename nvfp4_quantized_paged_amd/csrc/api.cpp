@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/nvfp4kv.h"
 #include "common.hpp"
 
@@ -85,10 +87,10 @@ struct DecodeCheck {
   int32_t splits;
 };
 
-int check_decode(const nvfp4kv_geom* g, const void* q, const int32_t* block_tables,
-                 int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
-                 float sm_scale, int32_t num_splits, bool allow_auto, void* workspace,
-                 size_t workspace_bytes, const char* fn, DecodeCheck* out) {
+// Shape and scalar checks of a decode call; the workspace is checked apart.
+int check_decode_args(const nvfp4kv_geom* g, const void* q, const int32_t* block_tables,
+                      int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                      float sm_scale, int32_t num_splits, bool allow_auto, const char* fn, DecodeCheck* out) {
   if (!q || !block_tables || !seq_lens) return fail(NVFP4KV_EINVAL, "%s: q, block_tables and seq_lens must be non-NULL", fn);
   if (!aligned16(q)) return fail(NVFP4KV_EALIGN, "%s: q must be 16-byte aligned", fn);
   if (batch < 0 || batch > kGridYZ) return fail(NVFP4KV_EINVAL, "%s: batch %d out of range [0, %d]", fn, batch, kGridYZ);
@@ -107,13 +109,23 @@ int check_decode(const nvfp4kv_geom* g, const void* q, const int32_t* block_tabl
   if (splits < 1 || splits > kMaxSplits)
     return fail(NVFP4KV_EINVAL, "%s: num_splits %d out of range [1, %d]%s", fn, num_splits, kMaxSplits,
                 allow_auto ? " (0 = auto)" : "");
-  const size_t need = nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, g->head_dim, splits);
+  out->group = group;
+  out->splits = splits;
+  return NVFP4KV_OK;
+}
+
+int check_decode(const nvfp4kv_geom* g, const void* q, const int32_t* block_tables,
+                 int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                 float sm_scale, int32_t num_splits, bool allow_auto, void* workspace,
+                 size_t workspace_bytes, const char* fn, DecodeCheck* out) {
+  int rc = check_decode_args(g, q, block_tables, max_pages, seq_lens, batch, num_q_heads, sm_scale, num_splits,
+                             allow_auto, fn, out);
+  if (rc) return rc;
+  const size_t need = nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, g->head_dim, out->splits);
   if (need > 0 && !workspace) return fail(NVFP4KV_EINVAL, "%s: workspace is NULL", fn);
   if (workspace && !aligned16(workspace)) return fail(NVFP4KV_EALIGN, "%s: workspace must be 16-byte aligned", fn);
   if (workspace_bytes < need)
     return fail(NVFP4KV_EWORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
-  out->group = group;
-  out->splits = splits;
   return NVFP4KV_OK;
 }
 
@@ -511,6 +523,79 @@ NVFP4KV_API int nvfp4_paged_decode_attn(const nvfp4kv_geom* geom, const void* q,
   const DecodeParams p = make_decode(geom, q, k_cache->data, k_cache->scale, v_cache->data, v_cache->scale,
                                      block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, c,
                                      sm_scale, k_cache->global_scale, workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_partial(p, geom->head_dim, false, NVFP4KV_VARIANT_AUTO, s);
+  if (e == hipSuccess) e = run_merge(p, geom->head_dim, v_cache->global_scale, out, s);
+  return launched(e, fn);
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free decode: the partial results live in a static device array
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Partial results of nvfp4_paged_decode_attn_noalloc: one array per GPU the
+// library runs on, held until the process ends. In host code `scratch` names a
+// host-side stand-in; the device address comes from hipGetSymbolAddress, once
+// per device, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** ptr, const char* fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NVFP4KV_ELAUNCH, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(NVFP4KV_EUNSUPPORTED, "%s: device %d >= %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(NVFP4KV_ELAUNCH, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return NVFP4KV_OK;
+}
+
+}  // namespace
+
+NVFP4KV_API size_t nvfp4_paged_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+NVFP4KV_API int nvfp4_paged_decode_attn_noalloc(const nvfp4kv_geom* geom, const void* q,
+                                                const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                                                const int32_t* block_tables, int32_t max_pages_per_seq,
+                                                const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                                float sm_scale, int32_t num_splits, void* out, void* stream) {
+  const char* fn = "nvfp4_paged_decode_attn_noalloc";
+  int rc;
+  DecodeCheck c{};
+  if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
+      (rc = check_nvfp4_cache(v_cache, "V", fn)) ||
+      (rc = check_decode_args(geom, q, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, sm_scale,
+                              num_splits, true, fn, &c)))
+    return rc;
+  if (!out) return fail(NVFP4KV_EINVAL, "%s: out is NULL", fn);
+  if (!aligned16(out)) return fail(NVFP4KV_EALIGN, "%s: out must be 16-byte aligned", fn);
+  const size_t per_split = nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, geom->head_dim, 1);
+  if (num_splits == 0 && per_split > 0 && (size_t)c.splits * per_split > kScratchBytes)
+    c.splits = (int32_t)(kScratchBytes / per_split);     // the library's count, lowered to fit
+  const size_t need = (size_t)c.splits * per_split;
+  if (need > kScratchBytes || c.splits < 1)
+    return fail(NVFP4KV_EWORKSPACE, "%s: the partials need %zu bytes (%d splits); the static scratch holds %zu",
+                fn, (size_t)(c.splits < 1 ? 1 : c.splits) * per_split, c.splits < 1 ? 1 : c.splits, kScratchBytes);
+  if (batch == 0) return launched(hipSuccess, fn);
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws, fn))) return rc;
+  const DecodeParams p = make_decode(geom, q, k_cache->data, k_cache->scale, v_cache->data, v_cache->scale,
+                                     block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, c,
+                                     sm_scale, k_cache->global_scale, ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = run_partial(p, geom->head_dim, false, NVFP4KV_VARIANT_AUTO, s);
   if (e == hipSuccess) e = run_merge(p, geom->head_dim, v_cache->global_scale, out, s);

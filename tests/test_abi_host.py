@@ -133,6 +133,31 @@ def test_decode_rejects_bad_arguments(L):
     assert _decode(L, g, B=0, ws=None, ws_bytes=0) == L.OK
 
 
+def _noalloc(L, g, B=1, Hq=4, S=1, q=FAKE, out=FAKE, maxp=16):
+    kc, vc = _nv(L), _nv(L)
+    return L.lib().nvfp4_paged_decode_attn_noalloc(ctypes.byref(g), q, ctypes.byref(kc), ctypes.byref(vc), FAKE,
+                                                   maxp, FAKE, B, Hq, 0.125, S, out, None)
+
+
+def test_noalloc_decode_rejects_partials_past_its_static_scratch(L):
+    """The allocation-free decode keeps its partials in a 32 MiB static array:
+    explicit split counts whose partials exceed it, and shapes where even one
+    split does not fit, are rejected on the host (no HIP call)."""
+    assert L.lib().nvfp4_paged_decode_noalloc_scratch_bytes() == 32 << 20
+    g = _geom(L, H=1, d=64)
+    per_split = 100 * 16 * (64 + 2) * 4                      # batch 100, 16 query heads
+    S = (32 << 20) // per_split + 1
+    assert _noalloc(L, g, B=100, Hq=16, S=S) == L.EWORKSPACE
+    assert "static scratch" in L.last_error()
+    assert _noalloc(L, g, B=65535, Hq=16, S=1) == L.EWORKSPACE            # one split is 276 MB
+    assert _noalloc(L, g, B=65535, Hq=16, S=0) == L.EWORKSPACE            # auto cannot lower below one
+    assert _noalloc(L, g, out=None) == L.EINVAL
+    assert _noalloc(L, g, out=FAKE + 2) == L.EALIGN
+    assert _noalloc(L, g, q=None) == L.EINVAL
+    assert _noalloc(L, g, S=5000) == L.EINVAL
+    assert _noalloc(L, g, B=0) == L.OK                                   # nothing to do, nothing launched
+
+
 def test_partial_rejects_bad_variant_and_auto_splits(L):
     g = _geom(L)
     kc, vc = _nv(L), _nv(L)
