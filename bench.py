@@ -1,28 +1,39 @@
 #!/usr/bin/env python3
 """Benchmark of the NVFP4 paged decode path on one MI355X.
 
-Workload (default): batch 44, 40 query / 8 KV heads, head_dim 128, context
+Headline workload: batch 44, 40 query / 8 KV heads, head_dim 128, context
 32,768, page 64, 32 splits, K/V ~ N(0,1) bf16 with 2% of channels x20 --
 the iso-concurrency long-context point of "Accelerating Long-Context and
 Agentic Inference with NVFP4 KV Cache" (section A4, Fig. 6), with the same
 layer also run over an FP8-E4M3 cache.
 
 One step = quantize-on-write of the step's new token of every sequence into
-the NVFP4 pool (it overwrites the last slot, so the shape stays fixed) +
-split-KV decode partials + log-sum-exp merge. Inputs are resident in HBM
-before timing. Prints ONE JSON line on stdout; diagnostics go to stderr.
+the pool (it overwrites the last slot, so the shape stays fixed) + split-KV
+decode partials + log-sum-exp merge. Inputs are resident in HBM before
+timing.
 
-  value           KV GB/s of the step: (packed + scale bytes) / step time
-  roofline        dominant kernel (decode partial): algorithmic bytes per
-                  launch / mean launch time (HIP events on the launch stream);
-                  also as a fraction of the measured read bandwidth
+Timing method (every figure): after an untimed ramp and the warm-up, each
+timed iteration is preceded by an untimed flush (a 1 GiB write, four times
+the 256 MB last-level cache, then a 1 GiB read of another buffer, so that the
+write's dirty lines are written back before the timed call), so no iteration
+finds its predecessor's data in a cache; each iteration is timed with HIP
+events on the stream the library launches on; the median, minimum and mean
+are reported. Throughput figures use the median unless named otherwise.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+  value           KV GB/s of the headline step: (packed + scale bytes) / median step
+  roofline        dominant kernel (decode partial, NVFP4, headline workload):
+                  (KV + q + out bytes) / its mean launch time; also against the
+                  measured read bandwidth; partial-result bytes reported apart
+  configs         the five workloads (tiny, moderate, 32K, 1M, agentic): NVFP4
+                  and FP8 step and partial-kernel times, KV GB/s, steps/s,
+                  fraction of 8 TB/s, the NVFP4/FP8 step-rate ratio, and the
+                  oracle parity of the same run's outputs
   hbm_read_probe  read bandwidth of the library's plain streaming-read kernel
-                  over 4 GiB (best of a few launch shapes)
   cpu_baseline    the CPU oracle (dequantize + fp64 attention) on a bounded
-                  sample of (sequence, KV head) slices of the same workload
-  fp8, extreme_context_1m, agentic_prefix_reuse
-                  the same step over the FP8 pool, the 1M batch-2 step, and
-                  the agentic prefix-reuse step with per-kernel times
+                  sample of (sequence, KV head) slices of the headline workload,
+                  on all usable host cores and on one
   decode_figures  decode tokens/s of NVFP4 and FP8 at the batch sizes of the
                   page's decode figures (Fig. 6 iso-concurrency: 44 / 10 / 1
                   at 32K / 160K / 1M; Fig. 7 iso-capacity: NVFP4 70 / 15 / 2
@@ -32,6 +43,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -42,23 +54,29 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "NVFP4 paged decode attn: KV GB/s + % HBM roofline; steps/s vs FP8-KV kernel"
 DECODE_SOURCES = ["nvfp4_quantized_paged_amd/csrc/decode_mfma.hip",
                   "nvfp4_quantized_paged_amd/csrc/common.hpp"]
+FLUSH_BYTES = 1 << 30
+TOL_MAX, TOL_MEAN = 2e-2, 2e-3
+PIECE = 1 << 16             # token rows per oracle work item
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kv_bytes(wl, fp8=False):
+def kv_bytes(wl, fp8=False, batch=None):
+    B = wl.batch if batch is None else batch
     per = wl.head_dim if fp8 else wl.head_dim // 2 + wl.head_dim // 16
-    return 2 * wl.batch * wl.context * wl.num_kv_heads * per
+    return 2 * B * wl.context * wl.num_kv_heads * per
 
 
-def io_bytes(wl):
-    return 2 * wl.batch * wl.num_q_heads * wl.head_dim * 2      # q read + out written (bf16)
+def io_bytes(wl, batch=None):
+    B = wl.batch if batch is None else batch
+    return 2 * B * wl.num_q_heads * wl.head_dim * 2      # q read + out written (bf16)
 
 
-def partial_bytes(wl, splits):
-    return wl.batch * wl.num_q_heads * splits * (wl.head_dim + 2) * 4
+def partial_bytes(wl, splits, batch=None):
+    B = wl.batch if batch is None else batch
+    return B * wl.num_q_heads * splits * (wl.head_dim + 2) * 4
 
 
 def source_digest():
@@ -88,6 +106,118 @@ def read_traffic(kernel_tag):
         return None
 
 
+# ---------------------------------------------------------------------------
+# oracle work on the host cores (worker processes; started before the GPU is touched)
+# ---------------------------------------------------------------------------
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def _noop(i):
+    return i
+
+
+def _oracle_quantize_piece(args):
+    """Oracle encode of K and V token rows [n][1][d] (bf16 bits): NVFP4 (data,
+    scale) pairs, or FP8 bytes."""
+    fmt, kb, vb = args
+    if fmt == "fp8":
+        from oracle import fp8 as of8
+        return of8.quantize_rows(kb), of8.quantize_rows(vb)
+    from oracle import nvfp4 as onv
+    return onv.quantize_rows(kb), onv.quantize_rows(vb)
+
+
+def _oracle_rate_worker(args):
+    """CPU baseline work of one process: quantize two (sequence, KV head) slices
+    of the workload, then time the oracle's dequantize + float64 attention over
+    them, alternately, for ~budget_s. Returns (slices, seconds)."""
+    import numpy as np
+
+    import synth
+    from oracle import attention as oatt
+    from oracle import nvfp4 as onv
+    wl_index, seed, budget_s = args
+    wl = synth.WORKLOADS[wl_index]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    gain_k = synth.outlier_mask(rng, 1, wl.head_dim) if wl.outliers else None
+    gain_v = synth.outlier_mask(rng, 1, wl.head_dim) if wl.outliers else None
+    caches = []
+    for _ in range(2):
+        kb = synth.host_values(rng, (wl.context, 1, wl.head_dim), gain_k)
+        vb = synth.host_values(rng, (wl.context, 1, wl.head_dim), gain_v)
+        caches.append(onv.quantize_rows(kb) + onv.quantize_rows(vb))
+    slices, elapsed = 0, 0.0
+    while elapsed < budget_s and slices < 100000:
+        kd, ks, vd, vs = caches[slices % 2]
+        qb = synth.host_values(rng, (wl.group, wl.head_dim))
+        t = time.perf_counter()
+        oatt.decode_heads(onv.bf16_to_f64(qb), onv.dequant_rows(kd, ks), onv.dequant_rows(vd, vs), wl.sm_scale)
+        elapsed += time.perf_counter() - t
+        slices += 1
+    return slices, elapsed
+
+
+def usable_cpus():
+    return len(os.sched_getaffinity(0))
+
+
+def make_pool(workers):
+    """Worker processes for the oracle, all started now (before any GPU call),
+    one BLAS thread each. Their map() keeps the order of its inputs."""
+    import multiprocessing
+    pool = multiprocessing.get_context("spawn").Pool(processes=workers, initializer=_worker_init)
+    pool.map(_noop, range(workers), chunksize=1)
+    return pool
+
+
+def cpu_baseline(wl, budget_s=12.0, pool=None, workers=1):
+    """The oracle (dequantize + fp64 attention) on (sequence, KV head) slices
+    of the workload: in this process on one thread, and, given a pool, on
+    `workers` processes at once (one thread each)."""
+    from threadpoolctl import threadpool_limits
+    per_slice = wl.context * (wl.head_dim // 2 + wl.head_dim // 16) * 2
+    step_bytes = kv_bytes(wl)
+    with threadpool_limits(limits=1):
+        slices, elapsed = _oracle_rate_worker((wl.index, wl.seed, budget_s))
+    gbs1 = slices * per_slice / elapsed / 1e9
+    single = {"value": round(gbs1, 5), "unit": "GB/s", "cores": 1,
+              "sample": f"{slices} slices, {elapsed:.1f}s on 1 thread",
+              "steps_per_s": round(gbs1 * 1e9 / step_bytes, 6)}
+    res = {
+        "value": single["value"], "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"(sequence, KV head) slices of {wl.name}: oracle NVFP4 dequantize + float64 softmax "
+                  f"attention of {wl.group} query heads over {wl.context} tokens each; {slices} slices in "
+                  f"{elapsed:.1f}s on 1 thread (BLAS limited to 1)",
+        "steps_per_s": single["steps_per_s"],
+        "host_cpus": os.cpu_count(), "host_cpus_usable": usable_cpus(), "blas_threads": 1,
+        "single_core": single,
+    }
+    if pool is not None and workers > 1:
+        t0 = time.perf_counter()
+        runs = pool.map(_oracle_rate_worker, [(wl.index, wl.seed + 17 * (i + 1), budget_s)
+                                              for i in range(workers)], chunksize=1)
+        wall = time.perf_counter() - t0
+        gbs = sum(s * per_slice / e for s, e in runs) / 1e9
+        n = sum(s for s, _ in runs)
+        res.update({
+            "value": round(gbs, 5), "cores": workers,
+            "sample": f"(sequence, KV head) slices of {wl.name}: oracle NVFP4 dequantize + float64 softmax "
+                      f"attention of {wl.group} query heads over {wl.context} tokens each; {n} slices on "
+                      f"{workers} processes at once (one thread each), ~{budget_s:.0f}s of timed work per "
+                      f"process ({wall:.1f}s wall with setup); rate = sum of the processes' rates",
+            "steps_per_s": round(gbs * 1e9 / step_bytes, 6),
+            "all_cores": {"value": round(gbs, 5), "cores": workers, "slices": n},
+        })
+    return res
+
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
 RAMP_S = 0.5
 
 
@@ -104,15 +234,67 @@ def ramp(fn, seconds=RAMP_S):
         torch.cuda.synchronize()
 
 
+class Flush:
+    """Untimed cache flush before each timed iteration: a 1 GiB write, then a
+    1 GiB read of another buffer with cached loads (the library's streaming
+    read kernel). The write evicts the previous iteration's data; the read
+    makes the caches write back the dirty lines of the write before the timed
+    call starts instead of during it, and leaves them holding clean, unrelated
+    lines."""
+
+    def __init__(self, nk):
+        import torch
+        self.nk = nk
+        self.wbuf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.rbuf = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.wbuf.fill_(self.n & 0xFF)
+        self.nk.hbm_read_probe(self.rbuf, 2048, 0, self.sink)
+
+
+def time_flushed(fn, iters, warmup, flush, ramp_s=RAMP_S):
+    """Median / minimum / mean duration of `iters` calls of fn, each preceded by
+    the flush, timed with HIP events on the launch stream (torch's current
+    stream, which the binding passes to the library)."""
+    import torch
+    if ramp_s > 0:
+        ramp(fn, ramp_s)
+    for _ in range(warmup):
+        flush()
+        fn()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        flush()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"median_ms": round(statistics.median(ms), 5), "min_ms": round(ms[0], 5),
+            "mean_ms": round(sum(ms) / len(ms), 5), "iters": iters, "wall_s": round(wall, 4)}
+
+
+# ---------------------------------------------------------------------------
+# uniform-context decode workloads
+# ---------------------------------------------------------------------------
+
 class Bench:
-    def __init__(self, nk, wl, fp8, variant, batch=None):
+    def __init__(self, nk, wl, fp8, variant, batch=None, keep_bf16=False):
         import torch
         from synth.workload import build_uniform_workload
         self.torch = torch
         self.nk, self.wl, self.fp8, self.variant = nk, wl, fp8, variant
         self.batch = B = wl.batch if batch is None else batch
         t = time.time()
-        self.w = build_uniform_workload(nk, wl, fp8=fp8, batch=B)
+        self.w = build_uniform_workload(nk, wl, fp8=fp8, batch=B, keep_bf16=keep_bf16)
         log(f"[bench] built {'fp8' if fp8 else 'nvfp4'} {wl.name} batch {B} in {time.time() - t:.1f}s")
         H, d, P, L = wl.num_kv_heads, wl.head_dim, wl.page_size, wl.context
         g = torch.Generator(device="cuda")
@@ -144,57 +326,135 @@ class Bench:
         self.partial()
         self.merge()
 
-    def time_steps(self, steps, warmup):
+    def parity(self, pool, samples):
+        """Oracle check of this run's outputs (the step has run: the new token
+        sits in the last slot): for each sampled (sequence, KV head), the pool
+        bytes of every token against the oracle's encode of the bf16 rows, and
+        the decode output against the oracle's float64 attention."""
+        import numpy as np
+        import synth
+        from oracle import attention as oatt
+        from oracle import fp8 as of8
+        from oracle import nvfp4 as onv
         torch = self.torch
-        ramp(self.step)
-        for _ in range(warmup):
-            self.step()
+        self.step()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            self.step()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
-
-    def time_partial(self, launches):
-        """Mean duration of the decode-partial kernel, HIP events on its stream."""
-        torch = self.torch
-        stream = torch.cuda.current_stream()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
-        self.partial()
-        for a, b in ev:
-            a.record(stream)
-            self.partial()
-            b.record(stream)
-        torch.cuda.synchronize()
-        ms = [a.elapsed_time(b) for a, b in ev]
-        return sum(ms) / len(ms) / 1e3, min(ms) / 1e3
+        wl, w = self.wl, self.w
+        G, L, P, d = wl.group, wl.context, wl.page_size, wl.head_dim
+        fmt = "fp8" if self.fp8 else "nvfp4"
+        bt = w.bt.cpu().numpy()
+        got_all = self.out.float().cpu().numpy().astype(np.float64)
+        errs, raws, bytes_exact = [], [], True
+        t0 = time.time()
+        for b, g in samples:
+            k_rows = synth.bf16_tensor_bits(w.k_bf16[b, :, g])[:, None, :]
+            v_rows = synth.bf16_tensor_bits(w.v_bf16[b, :, g])[:, None, :]
+            k_rows[L - 1, 0] = synth.bf16_tensor_bits(self.k_new[b, g])
+            v_rows[L - 1, 0] = synth.bf16_tensor_bits(self.v_new[b, g])
+            jobs = [(fmt, k_rows[t:t + PIECE], v_rows[t:t + PIECE]) for t in range(0, L, PIECE)]
+            parts = pool.map(_oracle_quantize_piece, jobs, chunksize=1) if pool is not None else \
+                [_oracle_quantize_piece(j) for j in jobs]
+            t = np.arange(L)
+            pages = torch.from_numpy(bt[b][t // P].astype(np.int64)).cuda()
+            offs = torch.from_numpy(t % P).cuda()
+            if self.fp8:
+                kr = np.concatenate([p[0] for p in parts])
+                vr = np.concatenate([p[1] for p in parts])
+                bytes_exact &= np.array_equal(w.kp.data[pages, g, offs].cpu().numpy(), kr[:, 0])
+                bytes_exact &= np.array_equal(w.vp.data[pages, g, offs].cpu().numpy(), vr[:, 0])
+                khat, vhat = of8.dequant_cache(kr, w.kp.scale), of8.dequant_cache(vr, w.vp.scale)
+            else:
+                kd = np.concatenate([p[0][0] for p in parts])
+                ks = np.concatenate([p[0][1] for p in parts])
+                vd = np.concatenate([p[1][0] for p in parts])
+                vs = np.concatenate([p[1][1] for p in parts])
+                for pool_t, ref in ((w.kp.data, kd), (w.kp.scale, ks), (w.vp.data, vd), (w.vp.scale, vs)):
+                    bytes_exact &= np.array_equal(pool_t[pages, g, offs].cpu().numpy(), ref[:, 0])
+                khat, vhat = onv.dequant_rows(kd, ks), onv.dequant_rows(vd, vs)
+            qb = synth.bf16_tensor_bits(w.q[b, g * G:(g + 1) * G])
+            ref, mass = oatt.decode_heads(onv.bf16_to_f64(qb), khat, vhat, wl.sm_scale)
+            raw = np.abs(got_all[b, g * G:(g + 1) * G] - ref)
+            errs.append(raw / np.maximum(1.0, mass))
+            raws.append(raw)
+        e, raw = np.concatenate([x.ravel() for x in errs]), np.concatenate([x.ravel() for x in raws])
+        ok = bool(bytes_exact and e.max() <= TOL_MAX and e.mean() <= TOL_MEAN)
+        res = {"samples": f"{len(samples)} whole (sequence, KV head) outputs over all {L} tokens "
+                          f"({len(samples) * G} query heads), and the pool bytes of those tokens",
+               "bytes_exact": bool(bytes_exact), "max_e": float(f"{e.max():.4g}"), "mean_e": float(f"{e.mean():.4g}"),
+               "raw_max_abs": float(f"{raw.max():.4g}"), "raw_mean_abs": float(f"{raw.mean():.4g}"),
+               "tolerance": "e = |gpu - oracle| / max(1, sum_t p_t |v_t|): max <= 2e-2, mean <= 2e-3",
+               "pass": ok, "oracle_s": round(time.time() - t0, 1)}
+        log(f"[bench] parity {fmt} {wl.name} B{self.batch}: bytes exact {bytes_exact}, max e {e.max():.3e} "
+            f"mean e {e.mean():.3e} ({time.time() - t0:.1f}s)")
+        return res
 
     def free(self):
         del self.w, self.ws, self.out
         self.torch.cuda.empty_cache()
 
 
-def decode_figures(nk, variant, steps, warmup, measured):
+def _samples(wl, B, which):
+    H = wl.num_kv_heads
+    if which == "all":
+        return [(b, g) for b in range(B) for g in range(H)]
+    if which == "two":
+        return [(0, 0), (B - 1, H - 1)]
+    return [(B - 1, H - 2 if H > 1 else 0)]
+
+
+def uniform_config(nk, wl, variant, iters, warmup, flush, pool, parity_samples, formats=("nvfp4", "fp8"),
+                   batch=None):
+    """One uniform-context workload over the NVFP4 and FP8 caches: the whole
+    step and the partial kernel alone, each timed as time_flushed does, and
+    the same run's parity."""
+    B = wl.batch if batch is None else batch
+    res = {"workload": wl.name, "batch": B, "context": wl.context, "num_q_heads": wl.num_q_heads,
+           "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "page_size": wl.page_size,
+           "outliers": wl.outliers}
+    for fmt in formats:
+        fp8 = fmt == "fp8"
+        bch = Bench(nk, wl, fp8, variant, batch=B, keep_bf16=parity_samples is not None)
+        step = time_flushed(bch.step, iters, warmup, flush)
+        part = time_flushed(bch.partial, iters, warmup, flush, ramp_s=0.2)
+        kvb = kv_bytes(wl, fp8, B)
+        io = io_bytes(wl, B)
+        t = step["median_ms"] / 1e3
+        tp = part["median_ms"] / 1e3
+        r = {"num_splits": bch.S, "step": step, "partial": part,
+             "kv_gbs": round(kvb / t / 1e9, 1), "steps_per_s": round(1.0 / t, 2),
+             "hbm_roofline_frac": round((kvb + io) / t / 1e9 / HBM_PEAK_GBS, 4),
+             "partial_hbm_roofline_frac": round((kvb + io) / tp / 1e9 / HBM_PEAK_GBS, 4),
+             "kv_bytes": kvb, "q_out_bytes": io, "partial_bytes_written": partial_bytes(wl, bch.S, B)}
+        if parity_samples is not None:
+            r["parity"] = bch.parity(pool, _samples(wl, B, parity_samples))
+        log(f"[bench] {fmt} {wl.name} B{B}: step median {step['median_ms']:.4f} ms min {step['min_ms']:.4f}, "
+            f"partial median {part['median_ms']:.4f} ms, {r['kv_gbs']} GB/s KV")
+        res[fmt] = r
+        bch.free()
+    if "nvfp4" in res and "fp8" in res:
+        res["nvfp4_over_fp8_steps"] = round(res["fp8"]["step"]["median_ms"] / res["nvfp4"]["step"]["median_ms"], 3)
+    return res
+
+
+def decode_figures(nk, variant, iters, warmup, flush, measured):
     """Kernel-level decode throughput at the batch sizes of the NVFP4 page's
     decode figures: iso-concurrency (Fig. 6, both caches at the same batch)
     and iso-capacity (Fig. 7, each cache at the batch it fits in the same
     memory), at 32K, 160K and 1M context. One step = quantize the new token
-    + decode partial + merge; decode tokens/s = batch / step time. Steps
-    already timed by the main benchmark are reused from `measured`."""
+    + decode partial + merge; decode tokens/s = batch / median step time.
+    Steps already timed are reused from `measured`."""
     import synth
 
     def run(idx, batch, fp8):
         key = (idx, batch, fp8)
         if key not in measured:
             b = Bench(nk, synth.WORKLOADS[idx], fp8, variant, batch=batch)
-            measured[key] = (b.time_steps(steps, warmup), b.S)
+            measured[key] = (time_flushed(b.step, iters, warmup, flush, ramp_s=0.2)["median_ms"] / 1e3, b.S)
             b.free()
         t, S = measured[key]
         wl = synth.WORKLOADS[idx]
-        kv = 2 * batch * wl.context * wl.num_kv_heads * (wl.head_dim if fp8 else wl.head_dim // 2 + wl.head_dim // 16)
         return {"batch": batch, "num_splits": S, "ms_per_step": round(t * 1e3, 4),
-                "decode_tokens_per_s": round(batch / t, 1), "kv_gbs": round(kv / t / 1e9, 1)}
+                "decode_tokens_per_s": round(batch / t, 1), "kv_gbs": round(kv_bytes(wl, fp8, batch) / t / 1e9, 1)}
     out = {"iso_concurrency": {}, "iso_capacity": {}}
     for name, (idx, batch) in synth.ISO_CONCURRENCY.items():
         nv, f8 = run(idx, batch, False), run(idx, batch, True)
@@ -209,75 +469,137 @@ def decode_figures(nk, variant, steps, warmup, measured):
     return out
 
 
-def time_calls(calls, steps, warmup):
-    """Whole-sequence time of `calls` per step (wall clock, synchronised) and each
-    call's mean duration from HIP events on the launch stream."""
+# ---------------------------------------------------------------------------
+# agentic prefix reuse
+# ---------------------------------------------------------------------------
+
+def agentic_parity(nk, w, out, pool, seqs=(0, 37)):
+    """Oracle check of the agentic step's outputs for sampled sequences: the
+    pool bytes of every token (shared prefix, private tokens, the new chunk),
+    the workspace rows (bit-exact) and the decode output."""
+    import numpy as np
     import torch
-    ramp(lambda: [f() for _, f in calls], seconds=0.2)
-    for _ in range(warmup):
-        for _, f in calls:
-            f()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        for _, f in calls:
-            f()
-    torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / steps
-    stream = torch.cuda.current_stream()
-    per = {}
-    for name, f in calls:
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for a, b in ev:
-            a.record(stream)
-            f()
-            b.record(stream)
-        torch.cuda.synchronize()
-        per[name] = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
-    return t_step, per
+    import synth
+    from oracle import attention as oatt
+    from oracle import nvfp4 as onv
+    wl = w.wl
+    H, P, G, C = wl.num_kv_heads, wl.page_size, wl.group, wl.chunk
+    offs = w.ws_row_offsets.cpu().numpy()
+    got = out.float().cpu().numpy().astype(np.float64)
+    errs, raws, exact = [], [], True
+    t0 = time.time()
+    for b in seqs:
+        L = int(w.host_cached_lens[b])
+        kb = np.concatenate([synth.bf16_tensor_bits(w.k_shared), synth.bf16_tensor_bits(w.k_private[b]),
+                             synth.bf16_tensor_bits(w.k_chunk[b * C:(b + 1) * C])])
+        vb = np.concatenate([synth.bf16_tensor_bits(w.v_shared), synth.bf16_tensor_bits(w.v_private[b]),
+                             synth.bf16_tensor_bits(w.v_chunk[b * C:(b + 1) * C])])
+        step = max(1, PIECE // H)
+        jobs = [("nvfp4", kb[t:t + step], vb[t:t + step]) for t in range(0, L + C, step)]
+        parts = pool.map(_oracle_quantize_piece, jobs, chunksize=1) if pool is not None else \
+            [_oracle_quantize_piece(j) for j in jobs]
+        kd = np.concatenate([p[0][0] for p in parts])
+        ks = np.concatenate([p[0][1] for p in parts])
+        vd = np.concatenate([p[1][0] for p in parts])
+        vs = np.concatenate([p[1][1] for p in parts])
+        t = np.arange(L + C)
+        pages = torch.from_numpy(w.host_bt[b][t // P].astype(np.int64)).cuda()
+        offp = torch.from_numpy(t % P).cuda()
+        for pool_t, ref in ((w.kp.data, kd), (w.kp.scale, ks), (w.vp.data, vd), (w.vp.scale, vs)):
+            exact &= np.array_equal(pool_t[pages, :, offp].cpu().numpy(), ref)
+        khat, vhat = onv.dequant_rows(kd, ks), onv.dequant_rows(vd, vs)
+        exact &= np.array_equal(synth.bf16_tensor_bits(w.k_ws[offs[b]:offs[b] + L]), oatt.f64_to_bf16_exact(khat[:L]))
+        exact &= np.array_equal(synth.bf16_tensor_bits(w.v_ws[offs[b]:offs[b] + L]), oatt.f64_to_bf16_exact(vhat[:L]))
+        qb = onv.bf16_to_f64(synth.bf16_tensor_bits(w.q[b]))
+        ref, mass = oatt.decode_heads(qb, khat, vhat, wl.sm_scale)
+        raw = np.abs(got[b] - ref)
+        errs.append((raw / np.maximum(1.0, mass)).ravel())
+        raws.append(raw.ravel())
+    e, raw = np.concatenate(errs), np.concatenate(raws)
+    res = {"samples": f"sequences {list(seqs)}: pool bytes of all their tokens, their workspace rows, "
+                      f"their decode outputs",
+           "bytes_exact": bool(exact), "max_e": float(f"{e.max():.4g}"), "mean_e": float(f"{e.mean():.4g}"),
+           "raw_max_abs": float(f"{raw.max():.4g}"), "raw_mean_abs": float(f"{raw.mean():.4g}"),
+           "pass": bool(exact and e.max() <= TOL_MAX and e.mean() <= TOL_MEAN), "oracle_s": round(time.time() - t0, 1)}
+    log(f"[bench] parity agentic: bytes and workspace exact {exact}, max e {e.max():.3e} mean e {e.mean():.3e}")
+    return res
 
 
-def agentic(nk, wl, steps, warmup):
+def extend_parity(w, qx, ox, q_offs_host, b=5, last=4):
+    """Oracle check of the extend output: the last `last` queries of sequence b,
+    as an extend problem whose prefix is the cached prefix plus the chunk
+    tokens before them (the same keys and positions)."""
+    import numpy as np
+    import synth
+    from oracle import attention as oatt
+    wl = w.wl
+    C, L = wl.chunk, int(w.host_cached_lens[b])
+    off = int(w.ws_row_offsets[b].item())
+    n = L + C
+    kw = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(w.k_ws[off:off + n]))
+    vw = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(w.v_ws[off:off + n]))
+    r0 = int(q_offs_host[b]) + C - last
+    q = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(qx[r0:r0 + last]))
+    ref, mass = oatt.extend_attention(q, kw, vw, np.array([0, last]), np.array([0, n]),
+                                      np.array([n - last], np.int32), wl.sm_scale)
+    got = ox[r0:r0 + last].float().cpu().numpy().astype(np.float64)
+    raw = np.abs(got - ref)
+    e = raw / np.maximum(1.0, mass)
+    return {"samples": f"the last {last} chunk queries of sequence {b} (all {wl.num_q_heads} heads, {n - last + 1}.."
+                       f"{n} keys)", "max_e": float(f"{e.max():.4g}"), "mean_e": float(f"{e.mean():.4g}"),
+            "raw_max_abs": float(f"{raw.max():.4g}"), "pass": bool(e.max() <= TOL_MAX and e.mean() <= TOL_MEAN)}
+
+
+def agentic(nk, wl, iters, warmup, flush, pool, parity=True):
     """The prefix-reuse step (quantize the new chunk, dequantize every cached
-    prefix into the workspace, decode all sequences): whole-step time and
-    each kernel's mean duration from HIP events on the launch stream. Run
-    twice: with bf16 chunk and workspace (the workload definition) and with
-    the pages' FP8 types (FP8 chunk quantized to NVFP4 and copied into an FP8
-    workspace in one pass, FP8 workspace)."""
+    prefix into the workspace, decode all sequences): the whole step and each
+    kernel alone, timed as time_flushed does. Run twice: with bf16 chunk and
+    workspace (the workload definition) and with the pages' FP8 types (FP8
+    chunk quantized to NVFP4 and copied into an FP8 workspace in one pass,
+    FP8 workspace). Then extend attention over the workspace and the
+    calibration absmax, outside the step."""
     import numpy as np
     import torch
     from synth.workload import agentic_bytes, build_agentic_workload
     t = time.time()
-    w = build_agentic_workload(nk, wl)
+    w = build_agentic_workload(nk, wl, keep_bf16=parity)
     log(f"[bench] built agentic workload in {time.time() - t:.1f}s")
     B, Hq, d, H, C = wl.batch, wl.num_q_heads, wl.head_dim, wl.num_kv_heads, wl.chunk
     S = nk.nvfp4_paged_decode_num_splits(B, H, w.bt.shape[1], wl.page_size)
     ws = nk.decode_workspace(B, Hq, d, S)
     out = torch.empty_like(w.q)
-    decode = ("decode", lambda: nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale,
-                                                           num_splits=S, workspace=ws, out=out))
-    calls = [
-        ("quantize", lambda: nk.nvfp4_kv_quantize(w.k_chunk, w.v_chunk, w.slot_chunk, w.kp, w.vp)),
-        ("dequant_workspace", lambda: nk.nvfp4_kv_dequant_workspace(w.kp, w.vp, w.bt, w.cached_lens,
-                                                                    w.ws_row_offsets, w.k_ws, w.v_ws)),
-        decode,
-    ]
-    t_step, per = time_calls(calls, steps, warmup)
+    quant = lambda: nk.nvfp4_kv_quantize(w.k_chunk, w.v_chunk, w.slot_chunk, w.kp, w.vp)
+    deq = lambda: nk.nvfp4_kv_dequant_workspace(w.kp, w.vp, w.bt, w.cached_lens, w.ws_row_offsets, w.k_ws, w.v_ws)
+    decode = lambda: nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale,
+                                                num_splits=S, workspace=ws, out=out)
+
+    def step():
+        quant()
+        deq()
+        decode()
     by = agentic_bytes(w)
+    ts = time_flushed(step, iters, warmup, flush, ramp_s=0.2)
+    tq = time_flushed(quant, iters, warmup, flush, ramp_s=0.1)
+    td = time_flushed(deq, iters, warmup, flush, ramp_s=0.1)
+    tc = time_flushed(decode, iters, warmup, flush, ramp_s=0.1)
+    med = lambda r: r["median_ms"] / 1e3
     res = {
-        "ms_per_step": round(t_step * 1e3, 4), "steps_per_s": round(1.0 / t_step, 2), "num_splits": S,
-        "quantize": {"ms": round(per["quantize"] * 1e3, 4),
-                     "gbs": round((by["quant_read"] + by["quant_write"]) / per["quantize"] / 1e9, 1)},
-        "dequant_workspace": {"ms": round(per["dequant_workspace"] * 1e3, 4),
-                              "gbs_unique": round((by["dequant_read_unique"] + by["dequant_write"])
-                                                  / per["dequant_workspace"] / 1e9, 1),
-                              "write_gbs": round(by["dequant_write"] / per["dequant_workspace"] / 1e9, 1)},
-        "decode": {"ms": round(per["decode"] * 1e3, 4),
-                   "kv_gbs_logical": round(by["decode_read_logical"] / per["decode"] / 1e9, 1),
-                   "kv_gbs_unique": round(by["decode_read_unique"] / per["decode"] / 1e9, 1)},
+        "workload": wl.name, "batch": B, "len_min": wl.len_min, "len_max": wl.len_max,
+        "shared_prefix": wl.shared_prefix, "chunk": C, "num_splits": S,
+        "step": ts, "steps_per_s": round(1.0 / med(ts), 2),
+        "quantize": {**tq, "gbs": round((by["quant_read"] + by["quant_write"]) / med(tq) / 1e9, 1)},
+        "dequant_workspace": {**td, "gbs_unique": round((by["dequant_read_unique"] + by["dequant_write"]) / med(td) / 1e9, 1),
+                              "write_gbs": round(by["dequant_write"] / med(td) / 1e9, 1)},
+        "decode": {**tc, "kv_gbs_logical": round(by["decode_read_logical"] / med(tc) / 1e9, 1),
+                   "kv_gbs_unique": round(by["decode_read_unique"] / med(tc) / 1e9, 1)},
         "bytes": by,
     }
-    log(f"[bench] agentic step {t_step * 1e3:.3f} ms: " + ", ".join(f"{k} {v * 1e3:.3f} ms" for k, v in per.items()))
+    log(f"[bench] agentic step {ts['median_ms']:.4f} ms: quantize {tq['median_ms']:.4f}, workspace "
+        f"{td['median_ms']:.4f}, decode {tc['median_ms']:.4f} ms")
+    if parity:
+        step()
+        torch.cuda.synchronize()
+        res["parity"] = agentic_parity(nk, w, out, pool)
 
     # the pages' path-2 types: FP8 chunk and FP8 workspace
     k8 = w.k_chunk.to(torch.float8_e4m3fn).view(torch.uint8)
@@ -288,118 +610,65 @@ def agentic(nk, wl, steps, warmup):
     offs = w.ws_row_offsets.cpu().numpy()
     chunk_rows = np.concatenate([offs[b] + w.host_cached_lens[b] + np.arange(C) for b in range(B)]).astype(np.int64)
     ws_rows = torch.from_numpy(chunk_rows).cuda()
-    calls8 = [
-        ("quantize", lambda: nk.nvfp4_kv_quantize_fp8(k8, v8, w.slot_chunk, w.kp, w.vp, 1.0, 1.0, ws_rows, kws8, vws8)),
-        ("dequant_workspace", lambda: nk.nvfp4_kv_dequant_workspace_fp8(w.kp, w.vp, w.bt, w.cached_lens,
-                                                                        w.ws_row_offsets, kws8, vws8)),
-        decode,
-    ]
-    t8, per8 = time_calls(calls8, steps, warmup)
+    quant8 = lambda: nk.nvfp4_kv_quantize_fp8(k8, v8, w.slot_chunk, w.kp, w.vp, 1.0, 1.0, ws_rows, kws8, vws8)
+    deq8 = lambda: nk.nvfp4_kv_dequant_workspace_fp8(w.kp, w.vp, w.bt, w.cached_lens, w.ws_row_offsets, kws8, vws8)
+
+    def step8():
+        quant8()
+        deq8()
+        decode()
+    ts8 = time_flushed(step8, iters, warmup, flush, ramp_s=0.2)
+    tq8 = time_flushed(quant8, iters, warmup, flush, ramp_s=0.1)
+    td8 = time_flushed(deq8, iters, warmup, flush, ramp_s=0.1)
     q_rd = by["quant_read"] // 2                        # FP8 chunk: one byte per element
     q_wr = by["quant_write"] + q_rd                     # NVFP4 + the chunk copied into the workspace
     dq_wr = by["dequant_write"] // 2
     res["fp8_path2"] = {
-        "ms_per_step": round(t8 * 1e3, 4), "steps_per_s": round(1.0 / t8, 2),
-        "quantize_with_chunk_copy": {"ms": round(per8["quantize"] * 1e3, 4),
-                                     "gbs": round((q_rd + q_wr) / per8["quantize"] / 1e9, 1)},
-        "dequant_workspace_fp8": {"ms": round(per8["dequant_workspace"] * 1e3, 4),
-                                  "gbs_unique": round((by["dequant_read_unique"] + dq_wr)
-                                                      / per8["dequant_workspace"] / 1e9, 1),
-                                  "write_gbs": round(dq_wr / per8["dequant_workspace"] / 1e9, 1)},
-        "decode": {"ms": round(per8["decode"] * 1e3, 4)},
+        "step": ts8, "steps_per_s": round(1.0 / med(ts8), 2),
+        "quantize_with_chunk_copy": {**tq8, "gbs": round((q_rd + q_wr) / med(tq8) / 1e9, 1)},
+        "dequant_workspace_fp8": {**td8, "gbs_unique": round((by["dequant_read_unique"] + dq_wr) / med(td8) / 1e9, 1),
+                                  "write_gbs": round(dq_wr / med(td8) / 1e9, 1)},
     }
-    log(f"[bench] agentic fp8 path-2 step {t8 * 1e3:.3f} ms: "
-        + ", ".join(f"{k} {v * 1e3:.3f} ms" for k, v in per8.items()))
+    log(f"[bench] agentic fp8 path-2 step {ts8['median_ms']:.4f} ms: quantize {tq8['median_ms']:.4f}, "
+        f"workspace {td8['median_ms']:.4f} ms")
 
     # extend attention of the chunk over the bf16 workspace (path 2's consumer), not part of the step:
     # the chunk's K/V go to the workspace rows after each prefix, then its queries attend causally
-    crow = torch.from_numpy(np.concatenate([offs[b] + w.host_cached_lens[b] + np.arange(C)
-                                            for b in range(B)]).astype(np.int64)).cuda()
+    deq()
+    crow = torch.from_numpy(chunk_rows).cuda()
     w.k_ws[crow] = w.k_chunk
     w.v_ws[crow] = w.v_chunk
     g = torch.Generator(device="cuda")
     g.manual_seed(wl.seed + 2000)
     qx = torch.randn((B * C, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
-    q_offs = torch.arange(0, B * C + 1, C, dtype=torch.int64, device="cuda")
+    q_offs_host = np.arange(0, B * C + 1, C, dtype=np.int64)
+    q_offs = torch.from_numpy(q_offs_host).cuda()
     ox = torch.empty_like(qx)
     ext = lambda: nk.nvfp4_extend_attn(qx, q_offs, w.k_ws, w.v_ws, w.ws_row_offsets, w.cached_lens, wl.sm_scale,
                                        max_chunk=C, out=ox)
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        ext()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        ext()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_ext = e0.elapsed_time(e1) / steps / 1e3
+    te = time_flushed(ext, max(5, iters // 3), 2, flush, ramp_s=0.0)
     Lc = w.host_cached_lens.astype(np.float64)
     flops = 4.0 * d * Hq * float(np.sum(C * Lc + C * (C + 1) / 2.0))
-    res["extend_attention"] = {"ms": round(t_ext * 1e3, 4), "tflops": round(flops / t_ext / 1e12, 1),
-                               "bf16_mfma_peak_frac": round(flops / t_ext / 2.5e15, 4), "flops": flops}
-    log(f"[bench] extend attention {t_ext * 1e3:.3f} ms, {flops / t_ext / 1e12:.1f} TFLOP/s")
+    res["extend_attention"] = {**te, "tflops": round(flops / med(te) / 1e12, 1),
+                               "bf16_mfma_peak_frac": round(flops / med(te) / 2.5e15, 4), "flops": flops}
+    log(f"[bench] extend attention {te['median_ms']:.3f} ms, {flops / med(te) / 1e12:.1f} TFLOP/s")
+    if parity:
+        res["extend_attention"]["parity"] = extend_parity(w, qx, ox, q_offs_host)
 
     # global-scale calibration of the chunk (absmax of K and V), not part of the step
     amax = torch.zeros(2, dtype=torch.float32, device="cuda")
     cal = lambda: (nk.nvfp4_kv_absmax(w.k_chunk, amax[0:1]), nk.nvfp4_kv_absmax(w.v_chunk, amax[1:2]))
-    for _ in range(warmup):
-        cal()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        cal()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_cal = e0.elapsed_time(e1) / steps / 1e3
-    res["absmax_calibration"] = {"ms": round(t_cal * 1e3, 4), "gbs": round(by["quant_read"] / t_cal / 1e9, 1)}
-    log(f"[bench] absmax calibration {t_cal * 1e3:.3f} ms")
+    tcal = time_flushed(cal, iters, warmup, flush, ramp_s=0.1)
+    res["absmax_calibration"] = {**tcal, "gbs": round(by["quant_read"] / med(tcal) / 1e9, 1)}
+    log(f"[bench] absmax calibration {tcal['median_ms']:.4f} ms")
     del w, ws, out, kws8, vws8, qx, ox
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The oracle (dequantize + fp64 attention) on (sequence, KV head) slices of
-    the workload, single-threaded, until ~budget_s of work."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    import synth
-    from oracle import attention as oatt
-    from oracle import nvfp4 as onv
-
-    rng = np.random.Generator(np.random.PCG64(wl.seed))
-    gain_k = synth.outlier_mask(rng, 1, wl.head_dim) if wl.outliers else None
-    gain_v = synth.outlier_mask(rng, 1, wl.head_dim) if wl.outliers else None
-    caches = []
-    for _ in range(2):                                # two distinct slices, quantized before timing
-        kb = synth.host_values(rng, (wl.context, 1, wl.head_dim), gain_k)
-        vb = synth.host_values(rng, (wl.context, 1, wl.head_dim), gain_v)
-        caches.append(onv.quantize_rows(kb) + onv.quantize_rows(vb))
-    slices, elapsed = 0, 0.0
-    with threadpool_limits(limits=1):
-        while elapsed < budget_s and slices < 10000:
-            kd, ks, vd, vs = caches[slices % len(caches)]
-            qb = synth.host_values(rng, (wl.group, wl.head_dim))
-            t = time.perf_counter()
-            kh = onv.dequant_rows(kd, ks)
-            vh = onv.dequant_rows(vd, vs)
-            oatt.decode_heads(onv.bf16_to_f64(qb), kh, vh, wl.sm_scale)
-            elapsed += time.perf_counter() - t
-            slices += 1
-    per_slice = wl.context * (wl.head_dim // 2 + wl.head_dim // 16) * 2
-    gbs = slices * per_slice / elapsed / 1e9
-    step_bytes = kv_bytes(wl)
-    return {
-        "value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"{slices} (sequence, KV head) slices of {wl.name}: oracle NVFP4 dequantize + float64 "
-                  f"softmax attention of {wl.group} query heads over {wl.context} tokens each, "
-                  f"{elapsed:.1f}s on 1 thread (BLAS limited to 1)",
-        "steps_per_s": round(gbs * 1e9 / step_bytes, 6),
-        "host_cpus": os.cpu_count(), "host_cpus_usable": len(os.sched_getaffinity(0)), "blas_threads": 1,
-    }
-
+# ---------------------------------------------------------------------------
+# read ceiling
+# ---------------------------------------------------------------------------
 
 def read_probe(nk, reps=10):
     """Achievable HBM read bandwidth: the library's streaming-read kernel over a 4 GiB buffer (far
@@ -429,16 +698,19 @@ def read_probe(nk, reps=10):
     return {"gbs": best["gbs"], "bytes": 4 << 30, "best": best, "runs": runs}
 
 
+# ---------------------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=30, help="timed iterations of each figure")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--variant", choices=["auto", "valu", "mfma", "mfma_lut"], default="auto")
     ap.add_argument("--only", choices=["nvfp4", "fp8", "agentic", "all"], default="all",
                     help="nvfp4 / fp8: only that 32K decode step; agentic: only the prefix-reuse step with "
                          "its extend attention and calibration (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle checks of the outputs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -446,6 +718,10 @@ def main():
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path runs on a single "
               f"MI355X; see the sharding notes in the design document)", file=sys.stderr)
         sys.exit(2)
+
+    parity = not args.no_parity and args.only in ("all", "agentic")
+    workers = min(16, usable_cpus())
+    pool = make_pool(workers) if (parity or (not args.no_cpu_baseline and args.only == "all")) else None
 
     import torch
     import nvfp4_quantized_paged_amd as nk
@@ -464,35 +740,38 @@ def main():
     nk.lib()
     variant = {"auto": nk.VARIANT_AUTO, "valu": nk.VARIANT_VALU, "mfma": nk.VARIANT_MFMA,
                "mfma_lut": nk.VARIANT_MFMA_LUT}[args.variant]
+    flush = Flush(nk)
+    iters, warmup = args.steps, args.warmup
     wl = synth.WORKLOADS[3]
     if args.only == "agentic":
-        res = agentic(nk, synth.WORKLOADS[5], max(5, args.steps // 2), args.warmup)
+        res = agentic(nk, synth.WORKLOADS[5], iters, warmup, flush, pool, parity=parity)
         print(json.dumps({"agentic_prefix_reuse": res}), flush=True)
         return
-    if args.only == "fp8":
-        f8 = Bench(nk, wl, True, variant)
-        t8 = f8.time_steps(args.steps, args.warmup)
-        log(f"[bench] fp8 step {t8 * 1e3:.3f} ms")
-        print(json.dumps({"fp8_ms_per_step": round(t8 * 1e3, 4)}))
+    if args.only in ("nvfp4", "fp8"):
+        r = uniform_config(nk, wl, variant, iters, warmup, flush, None, None, formats=(args.only,))
+        print(json.dumps(r), flush=True)
         return
 
-    nv = Bench(nk, wl, False, variant)
-    t_step = nv.time_steps(args.steps, args.warmup)
-    t_part, t_part_min = nv.time_partial(max(10, args.steps))
-    log(f"[bench] nvfp4 step {t_step * 1e3:.3f} ms, partial mean {t_part * 1e3:.3f} ms min {t_part_min * 1e3:.3f} ms")
-    S = nv.S
-    nv.free()
-
-    kvb = kv_bytes(wl)
+    # headline: the 32K workload, NVFP4 and FP8, same-run parity
+    c3 = uniform_config(nk, wl, variant, iters, warmup, flush, pool, "two" if parity else None)
+    nv = c3["nvfp4"]
+    t_step = nv["step"]["median_ms"] / 1e3
+    kvb, io = kv_bytes(wl), io_bytes(wl)
+    alg = kvb + io
+    t_part = nv["partial"]["mean_ms"] / 1e3
+    achieved = alg / t_part / 1e9
     result = {
         "metric": METRIC,
         "value": round(kvb / t_step / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": iters,
+        "warmup": warmup,
         "warmup_ramp_s": RAMP_S,
         "ms_per_step": round(t_step * 1e3, 4),
+        "ms_per_step_min": nv["step"]["min_ms"],
+        "timing": "median of the timed steps, each preceded by an untimed flush (1 GiB write, then 1 GiB "
+                  "read of another buffer); HIP events on the launch stream",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -500,53 +779,56 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: batch {wl.batch}, {wl.num_q_heads} q / {wl.num_kv_heads} kv heads, "
                                f"head_dim {wl.head_dim}, context {wl.context}, page {wl.page_size}, "
-                               f"{S} splits, 2% outlier channels x20, NVFP4 KV (E2M1 + E4M3/16, global scale 1.0)",
-                   "batch": wl.batch, "context": wl.context, "num_splits": S},
-        "steps_per_s": round(1.0 / t_step, 2),
-        "hbm_roofline_frac": round((kvb + io_bytes(wl)) / t_step / 1e9 / HBM_PEAK_GBS, 4),
+                               f"{nv['num_splits']} splits, 2% outlier channels x20, NVFP4 KV (E2M1 + E4M3/16, "
+                               f"global scale 1.0)",
+                   "batch": wl.batch, "context": wl.context, "num_splits": nv["num_splits"]},
+        "steps_per_s": nv["steps_per_s"],
+        "hbm_roofline_frac": nv["hbm_roofline_frac"],
+        "fp8_steps_per_s": c3["fp8"]["steps_per_s"],
+        "nvfp4_over_fp8_steps": c3["nvfp4_over_fp8_steps"],
     }
-    alg = kvb + wl.batch * wl.num_q_heads * wl.head_dim * 2 + partial_bytes(wl, S)
-    achieved = alg / t_part / 1e9
     result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_partial_nvfp4_32k"),
-                          "kernel": "decode_partial (NVFP4)", "algorithmic_bytes_per_launch": alg,
-                          "mean_launch_ms": round(t_part * 1e3, 4)}
+                          "frac": round(achieved / HBM_PEAK_GBS, 4),
+                          "traffic": read_traffic("decode_partial_nvfp4_32k"),
+                          "kernel": "decode_partial (NVFP4)",
+                          "algorithmic_bytes_per_launch": alg,
+                          "algorithmic_bytes": "packed KV + block scales + q + out (bf16)",
+                          "partial_bytes_written": nv["partial_bytes_written"],
+                          "mean_launch_ms": nv["partial"]["mean_ms"], "median_launch_ms": nv["partial"]["median_ms"],
+                          "min_launch_ms": nv["partial"]["min_ms"]}
     probe = read_probe(nk)
     result["roofline"]["measured_read_gbs"] = probe["gbs"]
     result["roofline"]["frac_of_measured_read"] = round(achieved / probe["gbs"], 4)
     result["hbm_read_probe"] = probe
 
     if args.only == "all":
-        f8 = Bench(nk, wl, True, variant)
-        t8 = f8.time_steps(args.steps, args.warmup)
-        f8.free()
-        result["fp8"] = {"ms_per_step": round(t8 * 1e3, 4), "steps_per_s": round(1.0 / t8, 2),
-                         "kv_gbs": round(kv_bytes(wl, True) / t8 / 1e9, 2),
-                         "hbm_roofline_frac": round((kv_bytes(wl, True) + io_bytes(wl)) / t8 / 1e9 / HBM_PEAK_GBS, 4)}
-        result["nvfp4_over_fp8_steps"] = round(t8 / t_step, 3)
-        log(f"[bench] fp8 step {t8 * 1e3:.3f} ms")
-
-        wl4 = synth.WORKLOADS[4]
-        b4 = Bench(nk, wl4, False, variant)
-        t4 = b4.time_steps(max(5, args.steps // 2), args.warmup)
-        b4.free()
-        result["extreme_context_1m"] = {
-            "ms_per_step": round(t4 * 1e3, 4), "steps_per_s": round(1.0 / t4, 2),
-            "kv_gbs": round(kv_bytes(wl4) / t4 / 1e9, 2),
-            "hbm_roofline_frac": round((kv_bytes(wl4) + io_bytes(wl4)) / t4 / 1e9 / HBM_PEAK_GBS, 4),
-            "num_splits": wl4.num_splits}
-        log(f"[bench] 1m step {t4 * 1e3:.3f} ms")
-
-        result["agentic_prefix_reuse"] = agentic(nk, synth.WORKLOADS[5], max(5, args.steps // 2), args.warmup)
-
-        measured = {(3, wl.batch, False): (t_step, S), (3, wl.batch, True): (t8, S),
-                    (4, wl4.batch, False): (t4, wl4.num_splits)}
-        result["decode_figures"] = decode_figures(nk, variant, max(5, args.steps // 2), args.warmup, measured)
+        ps = lambda which: which if parity else None
+        configs = {
+            "tiny": uniform_config(nk, synth.WORKLOADS[1], variant, iters, warmup, flush, pool, ps("all")),
+            "moderate_batch": uniform_config(nk, synth.WORKLOADS[2], variant, iters, warmup, flush, pool, ps("all")),
+            "long_context_32k": c3,
+            "extreme_context_1m": uniform_config(nk, synth.WORKLOADS[4], variant, iters, warmup, flush, pool,
+                                                 ps("one")),
+            "agentic_prefix_reuse": agentic(nk, synth.WORKLOADS[5], iters, warmup, flush, pool, parity=parity),
+        }
+        result["configs"] = configs
+        c4 = configs["extreme_context_1m"]
+        measured = {(3, wl.batch, False): (t_step, nv["num_splits"]),
+                    (3, wl.batch, True): (c3["fp8"]["step"]["median_ms"] / 1e3, c3["fp8"]["num_splits"]),
+                    (4, synth.WORKLOADS[4].batch, False): (c4["nvfp4"]["step"]["median_ms"] / 1e3,
+                                                          c4["nvfp4"]["num_splits"])}
+        result["decode_figures"] = decode_figures(nk, variant, iters, warmup, flush, measured)
+        result["parity_all_pass"] = all(
+            c[f]["parity"]["pass"] for c in configs.values() for f in ("nvfp4", "fp8") if f in c and "parity" in c[f]
+        ) and configs["agentic_prefix_reuse"].get("parity", {"pass": True})["pass"] if parity else None
 
     if not args.no_cpu_baseline:
         t = time.time()
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, pool=pool, workers=workers)
         log(f"[bench] cpu baseline {time.time() - t:.1f}s")
+    if pool is not None:
+        pool.close()
+        pool.join()
     print(json.dumps(result), flush=True)
 
 
