@@ -364,7 +364,7 @@ float nvfp4_global_scale_from_absmax(float amax);
  *                   are rows ws_row_offsets[b] + j, j < prefix_lens[b] + chunk_b
  *                   (the prefix from nvfp4_kv_dequant_workspace, then the chunk)
  *   ws_row_offsets  device int64 [batch + 1]
- *   prefix_lens     device int32 [batch]
+ *   prefix_lens     device int32 [batch]; a negative value is taken as 0
  *   max_chunk       >= every chunk length (sizes the grid); 0 is a no-op
  *   sm_scale        logit scale (finite, either sign)
  *   out             device bf16 [q rows][num_q_heads][head_dim]
