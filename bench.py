@@ -303,7 +303,12 @@ class Bench:
         self.v_new = torch.randn((B, H, d), generator=g, device="cuda").to(torch.bfloat16)
         last = L - 1
         self.slots_new = (self.w.bt[:, last // P].to(torch.int64) * P + last % P).contiguous()
-        self.S = wl.num_splits or nk.nvfp4_paged_decode_num_splits(B, H, self.w.bt.shape[1], P)
+        # the workload's split count at its own batch; at another batch (the decode figures) it is kept
+        # if it still fills one round of the kernel's resident waves (3 per SIMD for NVFP4, 2 for FP8:
+        # 3072 / 2048 items), else the library's automatic count
+        self.S = wl.num_splits
+        if not self.S or (B != wl.batch and B * H * self.S < (2048 if fp8 else 3072)):
+            self.S = nk.nvfp4_paged_decode_num_splits(B, H, self.w.bt.shape[1], P)
         self.ws = nk.decode_workspace(B, wl.num_q_heads, d, self.S)
         self.out = torch.empty_like(self.w.q)
 

@@ -23,14 +23,19 @@
 //  * Softmax in base 2, f32, running max and per-lane sums per head; the
 //    output accumulators are rescaled only when some head's max grows.
 //  * PV contracts over tokens, but a lane holds channels of one token. The
-//    token-major operand is made on the matrix unit: multiplying the V tile
-//    by a 0/1 selection matrix returns it transposed in the MFMA output
-//    layout (lane (c, g) = tokens 4g..4g+3 of channel c), exactly (one
-//    nonzero product per output). Two such outputs, packed to f16, are the A
-//    operand of O^T[c][h] += V^T[c][t] P[t][h], and the softmax output C of
-//    the same two tiles is already the B operand in the same lane: the only
+//    unpacked f16 V rows of two tiles are written to the wave's LDS (token
+//    rows, padded), and gfx950's transposing LDS read (ds_read_b64_tr_b16)
+//    returns them as the A operand of O^T[c][h] += V^T[c][t] P[t][h]: lane
+//    (c, g) receives tokens 4g..4g+3 of channel c from each tile. The softmax
+//    output C of the same two tiles is already the B operand in the same
+//    lane order. (An earlier form transposed V on the matrix unit by a 0/1
+//    operand: twice the MFMAs and 16 more conversions per tile; the partials
+//    are bit-identical, measured on MI355X: agentic decode 101 -> 93 us, 1M
+//    batch-1 252 -> 236 us, 32K and 1M batch-2 unchanged.) The other
 //    cross-lane step in the loop is the softmax's maximum over the four lane
-//    rows of a head (two VALU row swaps), and no LDS is used.
+//    rows of a head (two VALU row swaps).
+//  * Grid: KV head fastest, so the waves of one split read the adjacent
+//    head slices of the same pages side by side.
 //  * Loads: buffer loads with a fixed per-lane offset and a scalar offset
 //    (page from the block table, clamped into the pool), so no vector ALU
 //    goes into addressing. Pools below 2 GiB use one descriptor per array,
@@ -47,6 +52,19 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// LDS rows of unpacked V: D halfs plus 16 of padding, so that the four rows one transposing read
+// touches per 16-lane group start 32 bytes apart in the banks
+template <int D>
+struct VPitch {
+  static constexpr int kHalfs = D + 16;
+};
+
+__device__ inline __attribute__((address_space(3))) v4i16* lds_ptr(_Float16* p) {
+  return (__attribute__((address_space(3))) v4i16*)(p);
+}
 
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer descriptor, 32-bit data format
 // Cache policy of the K/V loads. The NVFP4 stream uses non-temporal loads
@@ -262,7 +280,7 @@ struct Acc {
 // One chunk: QK, online softmax, PV. `cs` > 0 maps raw scores to base-2 logits.
 template <int D, bool FP8, int T, bool LUT>
 __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D, FP8> (&cur)[Cfg<D, FP8, T>::kTiles],
-                                     const half8_t (&qb)[Cfg<D, FP8, T>::kKSteps], const half8_t (&sel)[2], float cs,
+                                     const half8_t (&qb)[Cfg<D, FP8, T>::kKSteps], _Float16* vl, float cs,
                                      Acc<D>& a) {
   using C = Cfg<D, FP8, T>;
   const int grp = lane >> 4;
@@ -321,22 +339,30 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
     for (int c = 0; c < C::kCTiles; ++c) a.o[c] *= alpha;
   }
 
-  // ---- PV over pairs of tiles (32 tokens = one MFMA K)
+  // ---- PV over pairs of tiles (32 tokens = one MFMA K). The unpacked V rows of the two tiles go
+  // to the wave's LDS rows (token-major); gfx950's transposing read returns them as the A operand of
+  // O^T = V^T P: in each 16-lane group kg, lane L names row 4kg + L/4 and channels 16ct + 4(L%4) .. +3,
+  // and lane i receives channel 16ct + i of rows 4kg .. 4kg + 3.
+  const int r = lane & 15;
+  const int kg = lane >> 4;
 #pragma unroll
   for (int t = 0; t < C::kTiles; t += 2) {
     const half8_t pb = pack_half8(float4_t{sc[t][0], sc[t][1], sc[t][2], sc[t][3]},
                                   float4_t{sc[t + 1][0], sc[t + 1][1], sc[t + 1][2], sc[t + 1][3]});
 #pragma unroll
-    for (int kk = 0; kk < C::kKSteps; ++kk) {
-      const half8_t va = unpack<D, FP8, LUT>(cur[t].v, cur[t].vs, kk);
-      const half8_t vb = unpack<D, FP8, LUT>(cur[t + 1].v, cur[t + 1].vs, kk);
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const float4_t zero = float4_t{0.f, 0.f, 0.f, 0.f};
-        const float4_t da = mfma(va, sel[hs], zero);     // tile t,   transposed
-        const float4_t db = mfma(vb, sel[hs], zero);     // tile t+1, transposed
-        a.o[2 * kk + hs] = mfma(pack_half8(da, db), pb, a.o[2 * kk + hs]);
+      for (int kk = 0; kk < C::kKSteps; ++kk) {
+        const half8_t v = unpack<D, FP8, LUT>(cur[t + tt].v, cur[t + tt].vs, kk);
+        *reinterpret_cast<half8_t*>(vl + (16 * tt + r) * VPitch<D>::kHalfs + grp * C::kChanPerGroup + 8 * kk) = v;
       }
+    const int rd = (4 * kg + (r >> 2)) * VPitch<D>::kHalfs + 4 * (r & 3);
+#pragma unroll
+    for (int ct = 0; ct < C::kCTiles; ++ct) {
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr(vl + rd + 16 * ct));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr(vl + 16 * VPitch<D>::kHalfs + rd + 16 * ct));
+      const half8_t va = __builtin_bit_cast(half8_t, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      a.o[ct] = mfma(va, pb, a.o[ct]);
     }
   }
 }
@@ -345,7 +371,7 @@ template <int D, bool FP8, int T, int W, bool PW, bool LUT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(W)))
 void decode_partial_mfma_kernel(DecodeParams p) {
   using C = Cfg<D, FP8, T>;
-  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;   // KV heads of one split run side by side
   const int lane = threadIdx.x;
   const int col = lane & 15;        // head (QK/PV columns) or channel (transpose columns)
   const int grp = lane >> 4;        // lane group
@@ -359,6 +385,10 @@ void decode_partial_mfma_kernel(DecodeParams p) {
   const Item it{p.block_tables + (int64_t)b * p.max_pages, g, min(L, t0 + per)};
   const int64_t qh0 = (int64_t)b * p.num_q_heads + (int64_t)g * G;
 
+  // LDS: the unpacked V rows of a chunk in the loop, the partial results at the end
+  constexpr int kVlHalfs = 32 * VPitch<D>::kHalfs;
+  constexpr int kStageHalfs = 16 * D * 2;
+  __shared__ __attribute__((aligned(16))) _Float16 vl[kVlHalfs > kStageHalfs ? kVlHalfs : kStageHalfs];
   Acc<D> a;
 #pragma unroll
   for (int c = 0; c < C::kCTiles; ++c) a.o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -406,47 +436,34 @@ void decode_partial_mfma_kernel(DecodeParams p) {
       for (int e = 0; e < 8; ++e) qb[kk][e] = (_Float16)(qf[kk][e] * qshift);
     const float cs = __builtin_ldexpf(fabsf(p.qk_scale), qexp);
 
-    // ---- 0/1 selection operands for the V transposes: column n takes A slot (group 2hs + n/8, item n%8)
-    half8_t sel[2];
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sel[hs][e] = (grp == 2 * hs + (col >> 3) && e == (col & 7)) ? (_Float16)1.0f : (_Float16)0.0f;
-
     // three register buffers: compute one chunk while the next two are in flight.
     // The loop runs whole rotations only (no exit in the middle): every path
     // back to the loop head has issued the same loads in the same order, so the
     // compiler's wait before each chunk leaves the other two chunks in flight.
     int ts = t0;
     for (; ts + 2 * C::kChunk < it.t1; ts += 3 * C::kChunk) {
-      process_chunk<D, FP8, T, LUT>(it, ts, lane, b0, qb, sel, cs, a);
+      process_chunk<D, FP8, T, LUT>(it, ts, lane, b0, qb, vl, cs, a);
       load_chunk<D, FP8, T, PW>(p, it, ts + 3 * C::kChunk, lane, b0);
-      process_chunk<D, FP8, T, LUT>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
+      process_chunk<D, FP8, T, LUT>(it, ts + C::kChunk, lane, b1, qb, vl, cs, a);
       load_chunk<D, FP8, T, PW>(p, it, ts + 4 * C::kChunk, lane, b1);
-      process_chunk<D, FP8, T, LUT>(it, ts + 2 * C::kChunk, lane, b2, qb, sel, cs, a);
+      process_chunk<D, FP8, T, LUT>(it, ts + 2 * C::kChunk, lane, b2, qb, vl, cs, a);
       load_chunk<D, FP8, T, PW>(p, it, ts + 5 * C::kChunk, lane, b2);
     }
     // at most two chunks remain, already loaded
-    if (ts < it.t1) process_chunk<D, FP8, T, LUT>(it, ts, lane, b0, qb, sel, cs, a);
-    if (ts + C::kChunk < it.t1) process_chunk<D, FP8, T, LUT>(it, ts + C::kChunk, lane, b1, qb, sel, cs, a);
+    if (ts < it.t1) process_chunk<D, FP8, T, LUT>(it, ts, lane, b0, qb, vl, cs, a);
+    if (ts + C::kChunk < it.t1) process_chunk<D, FP8, T, LUT>(it, ts + C::kChunk, lane, b1, qb, vl, cs, a);
   }
 
   // ---- partial results. The accumulators sit in lane (head col, channel group grp) order;
   // they go through LDS so that each store instruction writes whole rows of the output,
   // with non-temporal stores (measured on MI355X, long-context-32k: 297 -> 281 us; the
   // per-lane scattered 16-byte stores cost 9% of the kernel).
-  __shared__ float4_t stage[16 * D / 4];
+  float4_t* stage = reinterpret_cast<float4_t*>(vl);
   float lt = a.l + __shfl_xor(a.l, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
   if (col < G) {
 #pragma unroll
-    for (int kk = 0; kk < C::kKSteps; ++kk)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const int ch = (2 * hs + (grp >> 1)) * C::kChanPerGroup + 8 * kk + 4 * (grp & 1);
-        stage[(col * D + ch) / 4] = a.o[2 * kk + hs];
-      }
+    for (int ct = 0; ct < C::kCTiles; ++ct) stage[(col * D + 16 * ct + 4 * grp) / 4] = a.o[ct];
   }
   __syncthreads();
   for (int e = lane; e < G * D / 4; e += 64) {
@@ -465,7 +482,7 @@ void decode_partial_mfma_kernel(DecodeParams p) {
 
 template <int D, bool FP8, int T, int W, bool LUT = false>
 hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
-  dim3 grid(p.num_splits, p.num_kv_heads, p.batch);
+  dim3 grid(p.num_kv_heads, p.num_splits, p.batch);
   // buffer offsets and bounds are 32-bit: whole-pool descriptors only below 2 GiB per array
   const int64_t pool_bytes = (int64_t)p.num_pages * p.num_kv_heads * p.page_size * Cfg<D, FP8, T>::kRowBytes;
   if (pool_bytes <= INT32_MAX)

@@ -16,12 +16,14 @@
 // online softmax per column, and reuses the softmax output in its C layout as
 // the B operand of O^T = V^T P^T. A workgroup (8 waves) holds the G query heads
 // of one KV head times enough query tiles; each 64-key block of K and V is
-// staged once in LDS and read by all of them: K row-major, V transposed, so the
-// A operand of the PV product is two 8-byte LDS reads and no transpose runs on
-// the matrix unit. The next block is loaded into registers while the current
-// one is computed and written to the second of two LDS buffers (one barrier
-// per block). Row pitches are padded so the lanes of one read spread over the
-// LDS banks.
+// staged once in LDS, both row-major, and read by all of them. The A operand
+// of the PV product (V^T) comes from gfx950's transposing LDS read
+// (ds_read_b64_tr_b16, two per operand), so V is staged exactly like K: no
+// byte permutes and no transposing stores (outputs bit-identical to the earlier
+// form that stored V^T; measured on MI355X, agentic chunk 4.00 -> 3.89 ms).
+// The next block is loaded into registers while the current one is computed
+// and written to the second of two LDS buffers (one barrier per block). Row
+// pitches are padded so the lanes of one read spread over the LDS banks.
 #include "common.hpp"
 
 namespace nvfp4kv {
@@ -33,6 +35,12 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+__device__ inline __attribute__((address_space(3))) v4i16* lds4(const __bf16* p) {
+  return (__attribute__((address_space(3))) v4i16*)(p);
+}
 
 constexpr int kKB = 64;                    // keys per LDS block
 constexpr int kRsrcWord3 = 0x00020000;     // gfx9 raw buffer descriptor, 32-bit data format
@@ -54,12 +62,10 @@ struct ExtCfg {
   static constexpr int kWaves = kHeadWaves * kWQ;
   static constexpr int kQPerWave = 16 * kQT;
   static constexpr int kQPerGroup = kQPerWave * kWQ;
-  static constexpr int kKPitch = D + 8;             // K row pitch (bf16): 16-byte reads of 16 rows spread over banks
-  // V^T row pitch (bf16): 34 dwords, so the 16 rows of an operand read (16 lanes of 8 bytes per
-  // LDS cycle) fall on distinct bank pairs; the 4-key chunks of row r are stored XOR-swizzled by
-  // (r >> 4) & 3, which spreads the transposing stores (16 rows four apart per cycle) over all
-  // banks and is a constant for every operand read
-  static constexpr int kVPitch = kKB + 4;
+  // K and V rows (bf16) padded to D + 16: the 16 rows of a K operand read (8 lanes of 16 bytes per
+  // LDS cycle) and the 4 rows x 32 bytes of a transposing V read (16 lanes of 8 bytes) start 32
+  // bytes apart in the banks
+  static constexpr int kKPitch = D + 16;
   static constexpr int kKSteps = D / 32;
   static constexpr int kCTiles = D / 16;
 };
@@ -76,7 +82,7 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
   constexpr int NT = C::kNT;
   // two LDS buffers: block j is read from buffer j % 2 while block j + 1 is written to the other
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kKB * C::kKPitch];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * C::kVPitch];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][kKB * C::kKPitch];
   // Workgroup w runs on XCD w % 8; tiles are renumbered so that the query blocks of
   // one (sequence, KV head), which read the same keys, are consecutive on one XCD.
   const int nwg = (int)gridDim.x;
@@ -140,27 +146,21 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
   // along the channels so that a wave reads whole rows), transposed with byte permutes and
   // stored as four 8-byte pieces of V^T rows.
   constexpr int kThreads = 64 * C::kWaves;
-  constexpr int kKPieces = kKB * D / 8, kVQuads = kKB / 4 * D / 4;
+  constexpr int kKPieces = kKB * D / 8;
   constexpr int kKPer = (kKPieces + kThreads - 1) / kThreads;
-  constexpr int kVPer = (kVQuads + kThreads - 1) / kThreads;
   u32x4_t kreg[kKPer];
-  u32x2_t vreg[kVPer][4];
+  u32x4_t vreg[kKPer];
   // A block's rows are read through a buffer descriptor based at its first row (head g) that
   // covers only the block's keys below nkeys: rows past them read as zeros (and are masked).
   // The per-thread offsets within a block are fixed.
   const uint32_t rs_bytes = (uint32_t)(p.num_kv_heads * D * 2);  // bytes between workspace rows
   const char* kseq = reinterpret_cast<const char*>(p.k + (kv0 * p.num_kv_heads + g) * D);
   const char* vseq = reinterpret_cast<const char*>(p.v + (kv0 * p.num_kv_heads + g) * D);
-  uint32_t koff[kKPer], voff[kVPer];
+  uint32_t koff[kKPer];
 #pragma unroll
   for (int i = 0; i < kKPer; ++i) {
     const uint32_t piece = threadIdx.x + i * kThreads;
     koff[i] = piece / (D / 8) * rs_bytes + piece % (D / 8) * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < kVPer; ++i) {
-    const uint32_t quad = threadIdx.x + i * kThreads;
-    voff[i] = 4 * (quad / (D / 4)) * rs_bytes + quad % (D / 4) * 8;
   }
   auto load_block = [&](int k0) {
     const int nrec = (int)(min(nkeys - k0, kKB) * rs_bytes);
@@ -173,11 +173,9 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
       if (kKPieces % kThreads == 0 || (int)threadIdx.x + i * kThreads < kKPieces)
         kreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff[i], 0, 0));
 #pragma unroll
-    for (int i = 0; i < kVPer; ++i)
-      if (kVQuads % kThreads == 0 || (int)threadIdx.x + i * kThreads < kVQuads)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vreg[i][j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(voff[i] + j * rs_bytes), 0, 0));
+    for (int i = 0; i < kKPer; ++i)
+      if (kKPieces % kThreads == 0 || (int)threadIdx.x + i * kThreads < kKPieces)
+        vreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)koff[i], 0, 0));
   };
   auto store_block = [&](int buf) {
 #pragma unroll
@@ -186,28 +184,14 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
       if (kKPieces % kThreads == 0 || piece < kKPieces) {
         const int kr = piece / (D / 8), c8 = piece % (D / 8);
         *reinterpret_cast<u32x4_t*>(&k_lds[buf][kr * C::kKPitch + c8 * 8]) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kVPer; ++i) {
-      const int quad = threadIdx.x + i * kThreads;
-      if (kVQuads % kThreads == 0 || quad < kVQuads) {
-        const int c4 = quad % (D / 4), kq = quad / (D / 4);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          // channel 4c4 + c of keys 4kq .. 4kq + 3: 16-bit half (c & 1) of word c / 2 of each key's piece
-          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-          const int wd = c >> 1;
-          const u32x2_t out = {__builtin_amdgcn_perm(vreg[i][1][wd], vreg[i][0][wd], sel),
-                               __builtin_amdgcn_perm(vreg[i][3][wd], vreg[i][2][wd], sel)};
-          *reinterpret_cast<u32x2_t*>(&vt_lds[buf][(4 * c4 + c) * C::kVPitch + 4 * (kq ^ ((c4 >> 2) & 3))]) = out;
-        }
+        *reinterpret_cast<u32x4_t*>(&vt_lds[buf][kr * C::kKPitch + c8 * 8]) = vreg[i];
       }
     }
   };
 
-  // element offset of this lane's 4-key chunk within a 16-key tile of a V^T row, per swizzle value
-  const int vswz[4] = {4 * (grp ^ 0), 4 * (grp ^ 1), 4 * (grp ^ 2), 4 * (grp ^ 3)};
+  // transposing V reads: in 16-lane group grp, lane col names key row 4grp + col / 4 of a 16-key tile
+  // and channels 16c + 4(col % 4) .. +3; lane col receives channel 16c + col of keys 4grp .. 4grp + 3
+  const int vtr = (4 * grp + (col >> 2)) * C::kKPitch + 4 * (col & 3);
 
   load_block(0);
   store_block(0);
@@ -301,11 +285,9 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
       }
 #pragma unroll
       for (int c = 0; c < C::kCTiles; ++c) {
-        // row 16c + col: chunk 4t + grp sits at 4t + (grp ^ (c & 3))
-        const __bf16* vrow = &vl[(16 * c + col) * C::kVPitch] + vswz[c & 3];
-        const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * t);
-        const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vrow + 16 * (t + 1));
-        const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds4(vl + 16 * t * C::kKPitch + vtr + 16 * c));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds4(vl + 16 * (t + 1) * C::kKPitch + vtr + 16 * c));
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
         for (int n = 0; n < NT; ++n) o[n][c] = mfma_bf16(a, pb[n], o[n][c]);
       }
