@@ -211,7 +211,7 @@ int nvfp4_kv_dequant_workspace_fp8(const nvfp4kv_geom* geom, const nvfp4kv_cache
  * nvfp4_paged_decode_num_splits -- the library's split count for a batch when
  *   the caller passes num_splits = 0 (depends on sizes only: as many splits
  *   as keep batch * num_kv_heads * splits within 3072 work items, one round
- *   of the chip's resident wave slots, at least 1, at most one split per 256
+ *   of the chip's resident wave slots, at least 1, at most one split per 128
  *   tokens of the longest possible sequence, max_pages_per_seq * page_size).
  * nvfp4_paged_decode_workspace_bytes -- bytes of the fp32 partials:
  *   batch * num_q_heads * num_splits * (head_dim + 2) * 4.

@@ -53,14 +53,15 @@ def test_exported_symbols_are_only_the_abi(L):
 
 
 def test_split_heuristic_and_workspace_size(L):
-    # at most 3072 items (at least one split), at most one split per 256 tokens of the longest sequence
+    # at most 3072 items (at least one split), at most one split per 128 tokens of the longest sequence
     assert L.nvfp4_paged_decode_num_splits(44, 8, 512, 64) == 8
     assert L.nvfp4_paged_decode_num_splits(2, 8, 16384, 64) == 192
     assert L.nvfp4_paged_decode_num_splits(64, 8, 657, 16) == 6
     assert L.nvfp4_paged_decode_num_splits(10, 8, 2560, 64) == 38
     assert L.nvfp4_paged_decode_num_splits(512, 8, 64, 16) == 1
-    assert L.nvfp4_paged_decode_num_splits(8, 8, 256, 16) == 16
-    assert L.nvfp4_paged_decode_num_splits(1, 1, 16, 16) == 1
+    assert L.nvfp4_paged_decode_num_splits(8, 8, 256, 16) == 32        # 4096 tokens: the 128-token cap
+    assert L.nvfp4_paged_decode_num_splits(2, 1, 10, 16) == 2          # 160 tokens
+    assert L.nvfp4_paged_decode_num_splits(1, 1, 16, 16) == 2
     assert L.nvfp4_paged_decode_workspace_bytes(44, 40, 128, 32) == 44 * 40 * 32 * 130 * 4
     assert L.nvfp4_paged_decode_workspace_bytes(0, 40, 128, 32) == 0
 
