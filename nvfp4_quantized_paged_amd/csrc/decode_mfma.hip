@@ -20,8 +20,10 @@
 //    [g*D/4, (g+1)*D/4) of token r), B = q (f16, moved into f16's top binade
 //    by a power of two, up or down). C[t][h]: lane (h, g) holds tokens
 //    4g..4g+3 of the tile.
-//  * Softmax in base 2, f32, running max and per-lane sums per head; the
-//    output accumulators are rescaled only when some head's max grows.
+//  * Softmax in base 2, f32, running max per head; the denominators are row
+//    sums of the same f16 numerators the PV product uses, taken on the
+//    matrix unit (an all-ones A operand); the output accumulators and the
+//    denominators are rescaled only when some head's max grows.
 //  * PV contracts over tokens, but a lane holds channels of one token. The
 //    unpacked f16 V rows of two tiles are written to the wave's LDS (token
 //    rows, padded), and gfx950's transposing LDS read (ds_read_b64_tr_b16)
@@ -274,7 +276,8 @@ __device__ inline float max_over_rows(float v) {
 template <int D>
 struct Acc {
   float4_t o[D / 16];
-  float m, l;
+  float4_t ls;      // softmax denominators: row sums of the packed numerators (four equal entries)
+  float m;
 };
 
 // One chunk: QK, online softmax, PV. `cs` > 0 maps raw scores to base-2 logits.
@@ -325,18 +328,14 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
   const float mnew = fmaxf(a.m, cmax * cs);
   const float alpha = __builtin_amdgcn_exp2f(a.m - mnew);
   a.m = mnew;
-  float psum = 0.0f;
 #pragma unroll
   for (int t = 0; t < C::kTiles; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[t][i] = __builtin_amdgcn_exp2f(fmaf(sc[t][i], cs, -mnew));
-      psum += sc[t][i];
-    }
-  a.l = a.l * alpha + psum;
+    for (int i = 0; i < 4; ++i) sc[t][i] = __builtin_amdgcn_exp2f(fmaf(sc[t][i], cs, -mnew));
   if (__ballot(alpha != 1.0f)) {
 #pragma unroll
     for (int c = 0; c < C::kCTiles; ++c) a.o[c] *= alpha;
+    a.ls *= alpha;
   }
 
   // ---- PV over pairs of tiles (32 tokens = one MFMA K). The unpacked V rows of the two tiles go
@@ -364,6 +363,12 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
       const half8_t va = __builtin_bit_cast(half8_t, v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       a.o[ct] = mfma(va, pb, a.o[ct]);
     }
+    // the denominators from the same packed numerators: an all-ones A operand sums the 32 tokens of
+    // every head column on the matrix unit (measured on MI355X: 0.3-1.4% faster than VALU sums of
+    // the unpacked values, output errors unchanged)
+    const half8_t ones = {(_Float16)1, (_Float16)1, (_Float16)1, (_Float16)1,
+                          (_Float16)1, (_Float16)1, (_Float16)1, (_Float16)1};
+    a.ls = mfma(ones, pb, a.ls);
   }
 }
 
@@ -392,8 +397,8 @@ void decode_partial_mfma_kernel(DecodeParams p) {
   Acc<D> a;
 #pragma unroll
   for (int c = 0; c < C::kCTiles; ++c) a.o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  a.ls = float4_t{0.f, 0.f, 0.f, 0.f};
   a.m = -INFINITY;
-  a.l = 0.0f;
 
   if (t0 < it.t1) {
     // The prologue's K/V loads are complete once q has arrived (q is loaded
@@ -459,8 +464,7 @@ void decode_partial_mfma_kernel(DecodeParams p) {
   // with non-temporal stores (measured on MI355X, long-context-32k: 297 -> 281 us; the
   // per-lane scattered 16-byte stores cost 9% of the kernel).
   float4_t* stage = reinterpret_cast<float4_t*>(vl);
-  float lt = a.l + __shfl_xor(a.l, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  const float lt = a.ls[0];
   if (col < G) {
 #pragma unroll
     for (int ct = 0; ct < C::kCTiles; ++ct) stage[(col * D + 16 * ct + 4 * grp) / 4] = a.o[ct];
