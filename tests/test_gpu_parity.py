@@ -1065,6 +1065,23 @@ def test_lengths_past_the_block_table_are_clamped(nk):
     for b_ in range(wl.batch):   # the 8 rows after each prefix keep their fill
         tail = results[1][0][b_ * (reach + 8) + reach:(b_ + 1) * (reach + 8)]
         assert bool((tail == -7.0).all())
+    # the FP8 workspace (two rows per wave): clamped lengths, and an odd prefix whose last wave
+    # has its second row past the end; rows past each prefix keep their fill
+    odd = torch.full((wl.batch,), reach - 1, dtype=torch.int32, device="cuda")
+    results8 = []
+    for lens in (at, past, odd):
+        kws = torch.full((rows, H, d), 0x55, dtype=torch.uint8, device="cuda")
+        vws = torch.full_like(kws, 0x55)
+        nk.nvfp4_kv_dequant_workspace_fp8(kp, vp, bt, lens, offs, kws, vws)
+        torch.cuda.synchronize()
+        results8.append((kws, vws))
+    for i in range(2):
+        assert torch.equal(results8[0][i], results8[1][i])
+        for b_ in range(wl.batch):
+            r0 = b_ * (reach + 8)
+            assert bool((results8[1][i][r0 + reach:r0 + reach + 8] == 0x55).all())
+            assert torch.equal(results8[2][i][r0:r0 + reach - 1], results8[0][i][r0:r0 + reach - 1])
+            assert bool((results8[2][i][r0 + reach - 1:r0 + reach + 8] == 0x55).all())
 
 
 def test_binding_rejects_mismatched_device_tensors(nk):
