@@ -9,7 +9,10 @@ layer also run over an FP8-E4M3 cache.
 
 One step = quantize-on-write of the step's new token of every sequence into
 the pool (it overwrites the last slot, so the shape stays fixed) + split-KV
-decode partials + log-sum-exp merge. Inputs are resident in HBM before
+decode partials + log-sum-exp merge. The library's decode-with-append call
+does the first two in one kernel (the wave whose split holds the new token
+encodes and stores it); the same step as separate launches (quantize kernel,
+partial kernel, merge) is timed beside it. Inputs are resident in HBM before
 timing.
 
 Timing method (every figure): after an untimed ramp and the warm-up, each
@@ -18,14 +21,18 @@ the 256 MB last-level cache, then a 1 GiB read of another buffer, so that the
 write's dirty lines are written back before the timed call), so no iteration
 finds its predecessor's data in a cache; each iteration is timed with HIP
 events on the stream the library launches on; the median, minimum and mean
-are reported. Throughput figures use the median unless named otherwise.
+are reported. Throughput figures use the median unless named otherwise. The
+fused step, the separate launches and the partial kernel of a workload are
+timed in interleaved rounds (one iteration of each per round), so that they
+see the same GPU state.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 
   value           KV GB/s of the headline step: (packed + scale bytes) / median step
-  roofline        dominant kernel (decode partial, NVFP4, headline workload):
-                  (KV + q + out bytes) / its mean launch time; also against the
-                  measured read bandwidth; partial-result bytes reported apart
+  roofline        dominant kernel (the decode partial kernel with the new token
+                  appended, NVFP4, headline workload): (KV + q + out + new-token
+                  bytes) / its mean launch time; also against the measured read
+                  bandwidth; partial-result bytes reported apart
   configs         the five workloads (tiny, moderate, 32K, 1M, agentic): NVFP4
                   and FP8 step and partial-kernel times, KV GB/s, steps/s,
                   fraction of 8 TB/s, the NVFP4/FP8 step-rate ratio, and the
@@ -53,7 +60,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "NVFP4 paged decode attn: KV GB/s + % HBM roofline; steps/s vs FP8-KV kernel"
 DECODE_SOURCES = ["nvfp4_quantized_paged_amd/csrc/decode_mfma.hip",
-                  "nvfp4_quantized_paged_amd/csrc/common.hpp"]
+                  "nvfp4_quantized_paged_amd/csrc/common.hpp",
+                  "nvfp4_quantized_paged_amd/csrc/encode.hpp"]
 FLUSH_BYTES = 1 << 30
 TOL_MAX, TOL_MEAN = 2e-2, 2e-3
 PIECE = 1 << 16             # token rows per oracle work item
@@ -72,6 +80,14 @@ def kv_bytes(wl, fp8=False, batch=None):
 def io_bytes(wl, batch=None):
     B = wl.batch if batch is None else batch
     return 2 * B * wl.num_q_heads * wl.head_dim * 2      # q read + out written (bf16)
+
+
+def new_token_bytes(wl, fp8=False, batch=None):
+    """The step's new token of every sequence: bf16 K and V rows read, their
+    encoded bytes written."""
+    B = wl.batch if batch is None else batch
+    per = wl.head_dim if fp8 else wl.head_dim // 2 + wl.head_dim // 16
+    return 2 * B * wl.num_kv_heads * (2 * wl.head_dim + per)
 
 
 def partial_bytes(wl, splits, batch=None):
@@ -282,6 +298,43 @@ def time_flushed(fn, iters, warmup, flush, ramp_s=RAMP_S):
             "mean_ms": round(sum(ms) / len(ms), 5), "iters": iters, "wall_s": round(wall, 4)}
 
 
+def time_flushed_interleaved(fns, iters, warmup, flush, ramp_s=0.2):
+    """time_flushed for several calls at once: each timed round runs every call
+    of `fns` (name -> callable) once, each after its own flush, so that a slow
+    drift of the GPU's state over the first second after a workload is built
+    (clocks, translation caches) weighs on all of them alike rather than on
+    whichever happens to be timed first. Returns name -> the time_flushed
+    figures."""
+    import torch
+    for fn in fns.values():
+        if ramp_s > 0:
+            ramp(fn, ramp_s)
+    for _ in range(warmup):
+        for fn in fns.values():
+            flush()
+            fn()
+    stream = torch.cuda.current_stream()
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+          for k in fns}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(iters):
+        for k, fn in fns.items():
+            a, b = ev[k][i]
+            flush()
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    out = {}
+    for k in fns:
+        ms = sorted(a.elapsed_time(b) for a, b in ev[k])
+        out[k] = {"median_ms": round(statistics.median(ms), 5), "min_ms": round(ms[0], 5),
+                  "mean_ms": round(sum(ms) / len(ms), 5), "iters": iters, "wall_s": round(wall / len(fns), 4)}
+    return out
+
+
 # ---------------------------------------------------------------------------
 # uniform-context decode workloads
 # ---------------------------------------------------------------------------
@@ -321,12 +374,31 @@ class Bench:
         f(self.w.q, self.w.kp, self.w.vp, self.w.bt, self.w.sl, self.wl.sm_scale, self.S,
           variant=self.variant, workspace=self.ws)
 
+    def partial_append(self):
+        """The step's partial kernel: the partials with the new token appended by the kernel."""
+        if self.variant == self.nk.VARIANT_VALU:
+            return self.partial()
+        f = self.nk.fp8_paged_decode_append_partial if self.fp8 else self.nk.nvfp4_paged_decode_append_partial
+        f(self.w.q, self.k_new, self.v_new, self.w.kp, self.w.vp, self.w.bt, self.w.sl, self.wl.sm_scale, self.S,
+          workspace=self.ws)
+
     def merge(self):
         scale = self.w.vp.scale if self.fp8 else self.w.vp.global_scale
         self.nk.nvfp4kv_lse_merge(self.ws, self.batch, self.wl.num_q_heads, self.wl.head_dim, self.S,
                                   scale, self.out)
 
     def step(self):
+        """One decode step: each sequence's new token quantized into its pool slot by the decode
+        kernel itself (quantize-on-write fused into the partial kernel), the partials, the merge.
+        The VALU variant has no fused form and runs the separate step."""
+        if self.variant == self.nk.VARIANT_VALU:
+            return self.step_separate()
+        f = self.nk.fp8_paged_decode_append_attn if self.fp8 else self.nk.nvfp4_paged_decode_append_attn
+        f(self.w.q, self.k_new, self.v_new, self.w.kp, self.w.vp, self.w.bt, self.w.sl, self.wl.sm_scale,
+          num_splits=self.S, workspace=self.ws, out=self.out)
+
+    def step_separate(self):
+        """The same step as three launches: the quantize kernel, the partial kernel, the merge."""
         self.quantize()
         self.partial()
         self.merge()
@@ -410,8 +482,9 @@ def _samples(wl, B, which):
 def uniform_config(nk, wl, variant, iters, warmup, flush, pool, parity_samples, formats=("nvfp4", "fp8"),
                    batch=None):
     """One uniform-context workload over the NVFP4 and FP8 caches: the whole
-    step and the partial kernel alone, each timed as time_flushed does, and
-    the same run's parity."""
+    step, the same step as separate launches, the step's partial kernel alone
+    (with the append) and the partial kernel without the append, timed in
+    interleaved rounds, and the same run's parity."""
     B = wl.batch if batch is None else batch
     res = {"workload": wl.name, "batch": B, "context": wl.context, "num_q_heads": wl.num_q_heads,
            "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "page_size": wl.page_size,
@@ -419,21 +492,26 @@ def uniform_config(nk, wl, variant, iters, warmup, flush, pool, parity_samples, 
     for fmt in formats:
         fp8 = fmt == "fp8"
         bch = Bench(nk, wl, fp8, variant, batch=B, keep_bf16=parity_samples is not None)
-        step = time_flushed(bch.step, iters, warmup, flush)
-        part = time_flushed(bch.partial, iters, warmup, flush, ramp_s=0.2)
+        tt = time_flushed_interleaved({"step": bch.step, "separate": bch.step_separate,
+                                       "partial": bch.partial_append, "partial_plain": bch.partial},
+                                      iters, warmup, flush)
+        step, step_sep, part, part_plain = tt["step"], tt["separate"], tt["partial"], tt["partial_plain"]
         kvb = kv_bytes(wl, fp8, B)
-        io = io_bytes(wl, B)
+        io = io_bytes(wl, B) + new_token_bytes(wl, fp8, B)
         t = step["median_ms"] / 1e3
         tp = part["median_ms"] / 1e3
-        r = {"num_splits": bch.S, "step": step, "partial": part,
+        r = {"num_splits": bch.S, "step": step, "step_separate": step_sep, "partial": part,
+             "partial_without_append": part_plain,
              "kv_gbs": round(kvb / t / 1e9, 1), "steps_per_s": round(1.0 / t, 2),
              "hbm_roofline_frac": round((kvb + io) / t / 1e9 / HBM_PEAK_GBS, 4),
              "partial_hbm_roofline_frac": round((kvb + io) / tp / 1e9 / HBM_PEAK_GBS, 4),
              "kv_bytes": kvb, "q_out_bytes": io, "partial_bytes_written": partial_bytes(wl, bch.S, B)}
         if parity_samples is not None:
             r["parity"] = bch.parity(pool, _samples(wl, B, parity_samples))
-        log(f"[bench] {fmt} {wl.name} B{B}: step median {step['median_ms']:.4f} ms min {step['min_ms']:.4f}, "
-            f"partial median {part['median_ms']:.4f} ms, {r['kv_gbs']} GB/s KV")
+        log(f"[bench] {fmt} {wl.name} B{B}: step median {step['median_ms']:.4f} ms min {step['min_ms']:.4f} "
+            f"(separate launches {step_sep['median_ms']:.4f}), partial median {part['median_ms']:.4f} ms "
+            f"(without the append {part_plain['median_ms']:.4f}), "
+            f"{r['kv_gbs']} GB/s KV")
         res[fmt] = r
         bch.free()
     if "nvfp4" in res and "fp8" in res:
@@ -445,7 +523,7 @@ def decode_figures(nk, variant, iters, warmup, flush, measured):
     """Kernel-level decode throughput at the batch sizes of the NVFP4 page's
     decode figures: iso-concurrency (Fig. 6, both caches at the same batch)
     and iso-capacity (Fig. 7, each cache at the batch it fits in the same
-    memory), at 32K, 160K and 1M context. One step = quantize the new token
+    memory), at 32K, 160K and 1M context. One step = append the new token
     + decode partial + merge; decode tokens/s = batch / median step time.
     Steps already timed are reused from `measured`."""
     import synth
@@ -724,6 +802,20 @@ def main():
               f"MI355X; see the sharding notes in the design document)", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        # no worker pool here: under a counter-collecting profiler every worker process would
+        # load the profiler's tool as well
+        import torch
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+        return
+
     parity = not args.no_parity and args.only in ("all", "agentic")
     workers = min(16, usable_cpus())
     pool = make_pool(workers) if (parity or (not args.no_cpu_baseline and args.only == "all")) else None
@@ -733,15 +825,6 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.copy_calibration:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
-        return
     nk.lib()
     variant = {"auto": nk.VARIANT_AUTO, "valu": nk.VARIANT_VALU, "mfma": nk.VARIANT_MFMA,
                "mfma_lut": nk.VARIANT_MFMA_LUT}[args.variant]
@@ -761,7 +844,7 @@ def main():
     c3 = uniform_config(nk, wl, variant, iters, warmup, flush, pool, "two" if parity else None)
     nv = c3["nvfp4"]
     t_step = nv["step"]["median_ms"] / 1e3
-    kvb, io = kv_bytes(wl), io_bytes(wl)
+    kvb, io = kv_bytes(wl), io_bytes(wl) + new_token_bytes(wl)
     alg = kvb + io
     t_part = nv["partial"]["mean_ms"] / 1e3
     achieved = alg / t_part / 1e9
@@ -795,9 +878,10 @@ def main():
     result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(achieved / HBM_PEAK_GBS, 4),
                           "traffic": read_traffic("decode_partial_nvfp4_32k"),
-                          "kernel": "decode_partial (NVFP4)",
+                          "kernel": "decode_partial with the new token appended (NVFP4)",
                           "algorithmic_bytes_per_launch": alg,
-                          "algorithmic_bytes": "packed KV + block scales + q + out (bf16)",
+                          "algorithmic_bytes": "packed KV + block scales + q + out (bf16) + the new token "
+                                               "(bf16 K/V rows in, encoded bytes out)",
                           "partial_bytes_written": nv["partial_bytes_written"],
                           "mean_launch_ms": nv["partial"]["mean_ms"], "median_launch_ms": nv["partial"]["median_ms"],
                           "min_launch_ms": nv["partial"]["min_ms"]}

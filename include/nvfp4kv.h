@@ -248,6 +248,51 @@ int nvfp4_paged_decode_attn(const nvfp4kv_geom* geom, const void* q,
                             size_t workspace_bytes, void* out, void* stream);
 
 /*
+ * nvfp4_paged_decode_append_attn -- one decode step with the step's new token:
+ * quantize-on-write of each sequence's new K/V (section A2, paths 1 and 3) fused
+ * into the decode. The result, and every pool byte, equal those of
+ * nvfp4_kv_quantize of k_new/v_new into the slot of position seq_lens[b] - 1
+ * (block_tables[b][(seq_lens[b] - 1) / page_size] * page_size + the position's
+ * offset in its page) followed by nvfp4_paged_decode_attn with the same arguments.
+ *
+ *   k_new, v_new device bf16, row b (num_kv_heads * d elements) at element
+ *                b * new_stride: sequence b's new token; 16-byte aligned
+ *   new_stride   elements between rows, >= num_kv_heads * d and a multiple of 8
+ *   seq_lens     include the new token; a sequence with seq_lens[b] = 0, or above
+ *                max_pages_per_seq * page_size, or whose new token's block-table
+ *                entry lies outside [0, num_pages), appends nothing (as
+ *                nvfp4_kv_quantize skips a slot outside the pool) and decodes as
+ *                nvfp4_paged_decode_attn does
+ *   other arguments as nvfp4_paged_decode_attn
+ * The new token's slot must not be read by another sequence of the same call
+ * (pages shared between sequences hold earlier tokens only): the wave that
+ * appends a token stores it and reads it back; another sequence could read the
+ * slot as it was before the call or after.
+ */
+int nvfp4_paged_decode_append_attn(const nvfp4kv_geom* geom, const void* q, const void* k_new,
+                                   const void* v_new, int64_t new_stride, const nvfp4kv_cache* k_cache,
+                                   const nvfp4kv_cache* v_cache, const int32_t* block_tables,
+                                   int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                   int32_t num_q_heads, float sm_scale, int32_t num_splits,
+                                   void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/*
+ * nvfp4_paged_decode_append_partial -- nvfp4_paged_decode_append_attn without
+ * the merge: appends the new tokens as that call does and writes the partials
+ * into `workspace` as nvfp4_paged_decode_partial does (same layout; the same
+ * bytes as nvfp4_kv_quantize of the new tokens followed by
+ * nvfp4_paged_decode_partial with the MFMA kernel); nvfp4kv_lse_merge with the V
+ * global scale then gives nvfp4_paged_decode_append_attn's output. num_splits
+ * must be >= 1.
+ */
+int nvfp4_paged_decode_append_partial(const nvfp4kv_geom* geom, const void* q, const void* k_new,
+                                      const void* v_new, int64_t new_stride, const nvfp4kv_cache* k_cache,
+                                      const nvfp4kv_cache* v_cache, const int32_t* block_tables,
+                                      int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                      int32_t num_q_heads, float sm_scale, int32_t num_splits,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_paged_decode_attn_noalloc -- nvfp4_paged_decode_attn for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc. Same arguments and result without
@@ -316,6 +361,20 @@ int fp8_paged_decode_attn(const nvfp4kv_geom* geom, const void* q, const fp8kv_c
                           int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
                           int32_t num_q_heads, float sm_scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+int fp8_paged_decode_append_attn(const nvfp4kv_geom* geom, const void* q, const void* k_new,
+                                 const void* v_new, int64_t new_stride, const fp8kv_cache* k_cache,
+                                 const fp8kv_cache* v_cache, const int32_t* block_tables,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                 int32_t num_q_heads, float sm_scale, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+int fp8_paged_decode_append_partial(const nvfp4kv_geom* geom, const void* q, const void* k_new,
+                                    const void* v_new, int64_t new_stride, const fp8kv_cache* k_cache,
+                                    const fp8kv_cache* v_cache, const int32_t* block_tables,
+                                    int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                    int32_t num_q_heads, float sm_scale, int32_t num_splits,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 int fp8_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,
                              const fp8kv_cache* k_cache, const fp8kv_cache* v_cache,

@@ -61,6 +61,16 @@ _SIGNATURES = {
     "nvfp4_paged_decode_noalloc_scratch_bytes": (c_size, []),
     "fp8_paged_decode_attn": (ctypes.c_int, [P_GEOM, c_vp, P_F8, P_F8, c_vp, c_i32, c_vp, c_i32, c_i32,
                                              c_f32, c_i32, c_vp, c_size, c_vp, c_vp]),
+    "nvfp4_paged_decode_append_attn": (ctypes.c_int, [P_GEOM, c_vp, c_vp, c_vp, c_i64, P_NV, P_NV, c_vp, c_i32,
+                                                      c_vp, c_i32, c_i32, c_f32, c_i32, c_vp, c_size, c_vp,
+                                                      c_vp]),
+    "fp8_paged_decode_append_attn": (ctypes.c_int, [P_GEOM, c_vp, c_vp, c_vp, c_i64, P_F8, P_F8, c_vp, c_i32,
+                                                    c_vp, c_i32, c_i32, c_f32, c_i32, c_vp, c_size, c_vp,
+                                                    c_vp]),
+    "nvfp4_paged_decode_append_partial": (ctypes.c_int, [P_GEOM, c_vp, c_vp, c_vp, c_i64, P_NV, P_NV, c_vp, c_i32,
+                                                         c_vp, c_i32, c_i32, c_f32, c_i32, c_vp, c_size, c_vp]),
+    "fp8_paged_decode_append_partial": (ctypes.c_int, [P_GEOM, c_vp, c_vp, c_vp, c_i64, P_F8, P_F8, c_vp, c_i32,
+                                                       c_vp, c_i32, c_i32, c_f32, c_i32, c_vp, c_size, c_vp]),
     "fp8_paged_decode_partial": (ctypes.c_int, [P_GEOM, c_vp, P_F8, P_F8, c_vp, c_i32, c_vp, c_i32, c_i32,
                                                 c_f32, c_i32, c_i32, c_vp, c_size, c_vp]),
     "nvfp4kv_lse_merge": (ctypes.c_int, [c_vp, c_size, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_vp]),
@@ -500,6 +510,65 @@ def fp8_paged_decode_attn(q, k_pool: FP8Pool, v_pool: FP8Pool, block_tables, seq
                           num_splits=0, workspace=None, out=None, stream=None):
     return _decode("fp8_paged_decode_attn", None, q, k_pool, v_pool, block_tables, seq_lens, sm_scale,
                    num_splits, workspace, out, stream)
+
+
+def _append_decode(fn_name, q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, sm_scale, num_splits,
+                   workspace, out, stream, merge=True):
+    B, Hq, d = _decode_args(q, block_tables, seq_lens)
+    g = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, out if merge else None)
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, torch.bfloat16, name)
+        if t.dim() != 3 or tuple(t.shape[1:]) != (g.num_kv_heads, d) or t.shape[0] != B:
+            raise ValueError(f"{name} must be [batch][num_kv_heads][head_dim] = [{B}][{g.num_kv_heads}][{d}], "
+                             f"got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{name}: the heads of a row must be contiguous")
+    if k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must have the same row stride")
+    splits = _resolve_splits(num_splits, B, g, block_tables.shape[1]) if merge else num_splits
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, d, splits, q.device)
+    args = [ctypes.byref(g), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), int(k_new.stride(0)),
+            ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()), block_tables.data_ptr(),
+            block_tables.shape[1], seq_lens.data_ptr(), B, Hq, float(sm_scale), splits, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size()]
+    if not merge:
+        _check(getattr(lib(), fn_name)(*args, _stream(stream)))
+        return workspace
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.bfloat16, "out")
+    _check(getattr(lib(), fn_name)(*args, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def nvfp4_paged_decode_append_attn(q, k_new, v_new, k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables, seq_lens,
+                                   sm_scale, num_splits=0, workspace=None, out=None, stream=None):
+    """One decode step with each sequence's new token (k_new, v_new: [B][Hkv][d] bf16, at position
+    seq_lens[b] - 1) quantized into its pool slot by the decode kernel itself; the same pool bytes
+    and output as nvfp4_kv_quantize into those slots followed by nvfp4_paged_decode_attn."""
+    return _append_decode("nvfp4_paged_decode_append_attn", q, k_new, v_new, k_pool, v_pool, block_tables,
+                          seq_lens, sm_scale, num_splits, workspace, out, stream)
+
+
+def fp8_paged_decode_append_attn(q, k_new, v_new, k_pool: FP8Pool, v_pool: FP8Pool, block_tables, seq_lens,
+                                 sm_scale, num_splits=0, workspace=None, out=None, stream=None):
+    return _append_decode("fp8_paged_decode_append_attn", q, k_new, v_new, k_pool, v_pool, block_tables,
+                          seq_lens, sm_scale, num_splits, workspace, out, stream)
+
+
+def nvfp4_paged_decode_append_partial(q, k_new, v_new, k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables,
+                                      seq_lens, sm_scale, num_splits, workspace=None, stream=None):
+    """nvfp4_paged_decode_append_attn without the merge: appends the new tokens and returns the
+    workspace holding the partials (as nvfp4_paged_decode_partial lays them out)."""
+    return _append_decode("nvfp4_paged_decode_append_partial", q, k_new, v_new, k_pool, v_pool, block_tables,
+                          seq_lens, sm_scale, num_splits, workspace, None, stream, merge=False)
+
+
+def fp8_paged_decode_append_partial(q, k_new, v_new, k_pool: FP8Pool, v_pool: FP8Pool, block_tables, seq_lens,
+                                    sm_scale, num_splits, workspace=None, stream=None):
+    return _append_decode("fp8_paged_decode_append_partial", q, k_new, v_new, k_pool, v_pool, block_tables,
+                          seq_lens, sm_scale, num_splits, workspace, None, stream, merge=False)
 
 
 def nvfp4_paged_decode_partial(q, k_pool, v_pool, block_tables, seq_lens, sm_scale, num_splits,

@@ -155,6 +155,7 @@ DecodeParams make_decode(const nvfp4kv_geom* g, const void* q, const uint8_t* kd
   p.num_kv_heads = g->num_kv_heads;
   p.group = c.group;
   p.page_size = g->page_size;
+  page_divisor(g->page_size, p.page_mul, p.page_sh);
   p.num_splits = c.splits;
   p.num_pages = g->num_pages;
   p.qk_scale = sm_scale * gs_k * 1.4426950408889634f;
@@ -529,6 +530,134 @@ NVFP4KV_API int nvfp4_paged_decode_attn(const nvfp4kv_geom* geom, const void* q,
   hipError_t e = run_partial(p, geom->head_dim, false, NVFP4KV_VARIANT_AUTO, s);
   if (e == hipSuccess) e = run_merge(p, geom->head_dim, v_cache->global_scale, out, s);
   return launched(e, fn);
+}
+
+// ---------------------------------------------------------------------------
+// decode step with the new token appended (quantize-on-write fused into the decode kernel)
+// ---------------------------------------------------------------------------
+
+namespace {
+
+int check_new_tokens(const nvfp4kv_geom* g, const void* k_new, const void* v_new, int64_t new_stride,
+                     int32_t batch, const char* fn) {
+  if (batch == 0) return NVFP4KV_OK;
+  if (!k_new || !v_new) return fail(NVFP4KV_EINVAL, "%s: k_new and v_new must be non-NULL", fn);
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(NVFP4KV_EALIGN, "%s: k_new and v_new must be 16-byte aligned", fn);
+  if (new_stride < (int64_t)g->num_kv_heads * g->head_dim || new_stride % 8 != 0)
+    return fail(NVFP4KV_EINVAL, "%s: new_stride %lld must be at least num_kv_heads * head_dim (%d) and a multiple of 8",
+                fn, (long long)new_stride, g->num_kv_heads * g->head_dim);
+  return NVFP4KV_OK;
+}
+
+void set_append(DecodeParams& p, const void* k_new, const void* v_new, int64_t new_stride, float gs_k, float gs_v,
+                bool quot, uint8_t* kd, uint8_t* ks, uint8_t* vd, uint8_t* vs) {
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.new_stride = new_stride;
+  p.gs_k = gs_k;
+  p.gs_v = gs_v;
+  p.quot = quot ? 1 : 0;
+  p.kd_w = kd;
+  p.ks_w = ks;
+  p.vd_w = vd;
+  p.vs_w = vs;
+}
+
+// The fused append step over either cache type: checks, the partial kernel with the append, and
+// (merge) the log-sum-exp merge into out. Partial only: num_splits must be explicit.
+template <bool FP8, typename Cache>
+int append_decode(const char* fn, bool merge, const nvfp4kv_geom* geom, const void* q, const void* k_new,
+                  const void* v_new, int64_t new_stride, const Cache* k_cache, const Cache* v_cache,
+                  const int32_t* block_tables, int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                  int32_t num_q_heads, float sm_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                  void* out, void* stream) {
+  int rc;
+  DecodeCheck c{};
+  if constexpr (FP8) {
+    if ((rc = check_geom(geom, fn)) || (rc = check_fp8_cache(k_cache, "K", fn)) ||
+        (rc = check_fp8_cache(v_cache, "V", fn)))
+      return rc;
+  } else {
+    if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
+        (rc = check_nvfp4_cache(v_cache, "V", fn)))
+      return rc;
+  }
+  if ((rc = check_decode(geom, q, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, sm_scale,
+                         num_splits, merge, workspace, workspace_bytes, fn, &c)) ||
+      (rc = check_new_tokens(geom, k_new, v_new, new_stride, batch, fn)))
+    return rc;
+  if (merge && !out) return fail(NVFP4KV_EINVAL, "%s: out is NULL", fn);
+  if (merge && !aligned16(out)) return fail(NVFP4KV_EALIGN, "%s: out must be 16-byte aligned", fn);
+  DecodeParams p;
+  float out_scale;
+  if constexpr (FP8) {
+    p = make_decode(geom, q, k_cache->data, nullptr, v_cache->data, nullptr, block_tables, max_pages_per_seq,
+                    seq_lens, batch, num_q_heads, c, sm_scale, k_cache->scale, workspace);
+    set_append(p, k_new, v_new, new_stride, k_cache->scale, v_cache->scale, false, k_cache->data, nullptr,
+               v_cache->data, nullptr);
+    out_scale = v_cache->scale;
+  } else {
+    p = make_decode(geom, q, k_cache->data, k_cache->scale, v_cache->data, v_cache->scale, block_tables,
+                    max_pages_per_seq, seq_lens, batch, num_q_heads, c, sm_scale, k_cache->global_scale,
+                    workspace);
+    set_append(p, k_new, v_new, new_stride, k_cache->global_scale, v_cache->global_scale,
+               pow2_in_range(k_cache->global_scale) && pow2_in_range(v_cache->global_scale), k_cache->data,
+               k_cache->scale, v_cache->data, v_cache->scale);
+    out_scale = v_cache->global_scale;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_partial(p, geom->head_dim, FP8, NVFP4KV_VARIANT_MFMA, s);
+  if (e == hipSuccess && merge) e = run_merge(p, geom->head_dim, out_scale, out, s);
+  return launched(e, fn);
+}
+
+}  // namespace
+
+NVFP4KV_API int nvfp4_paged_decode_append_attn(const nvfp4kv_geom* geom, const void* q, const void* k_new,
+                                               const void* v_new, int64_t new_stride,
+                                               const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                                               const int32_t* block_tables, int32_t max_pages_per_seq,
+                                               const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                               float sm_scale, int32_t num_splits, void* workspace,
+                                               size_t workspace_bytes, void* out, void* stream) {
+  return append_decode<false>("nvfp4_paged_decode_append_attn", true, geom, q, k_new, v_new, new_stride, k_cache,
+                              v_cache, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, sm_scale,
+                              num_splits, workspace, workspace_bytes, out, stream);
+}
+
+NVFP4KV_API int nvfp4_paged_decode_append_partial(const nvfp4kv_geom* geom, const void* q, const void* k_new,
+                                                  const void* v_new, int64_t new_stride,
+                                                  const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                                                  const int32_t* block_tables, int32_t max_pages_per_seq,
+                                                  const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                                  float sm_scale, int32_t num_splits, void* workspace,
+                                                  size_t workspace_bytes, void* stream) {
+  return append_decode<false>("nvfp4_paged_decode_append_partial", false, geom, q, k_new, v_new, new_stride,
+                              k_cache, v_cache, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads,
+                              sm_scale, num_splits, workspace, workspace_bytes, nullptr, stream);
+}
+
+NVFP4KV_API int fp8_paged_decode_append_attn(const nvfp4kv_geom* geom, const void* q, const void* k_new,
+                                             const void* v_new, int64_t new_stride, const fp8kv_cache* k_cache,
+                                             const fp8kv_cache* v_cache, const int32_t* block_tables,
+                                             int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                             int32_t num_q_heads, float sm_scale, int32_t num_splits,
+                                             void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  return append_decode<true>("fp8_paged_decode_append_attn", true, geom, q, k_new, v_new, new_stride, k_cache,
+                             v_cache, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, sm_scale,
+                             num_splits, workspace, workspace_bytes, out, stream);
+}
+
+NVFP4KV_API int fp8_paged_decode_append_partial(const nvfp4kv_geom* geom, const void* q, const void* k_new,
+                                                const void* v_new, int64_t new_stride, const fp8kv_cache* k_cache,
+                                                const fp8kv_cache* v_cache, const int32_t* block_tables,
+                                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t batch,
+                                                int32_t num_q_heads, float sm_scale, int32_t num_splits,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
+  return append_decode<true>("fp8_paged_decode_append_partial", false, geom, q, k_new, v_new, new_stride,
+                             k_cache, v_cache, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads,
+                             sm_scale, num_splits, workspace, workspace_bytes, nullptr, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -7,6 +7,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace nvfp4kv {
@@ -14,6 +15,30 @@ namespace nvfp4kv {
 constexpr int kBlock = 16;   // elements per E4M3 block scale
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Division by the page size P (P >= 2) as a multiply-high and a shift, exact for dividends
+// 0 <= t < 2^31 (host side). With l = ceil(log2 P) and mul = ceil(2^(31+l) / P) < 2^32,
+// mul = (2^(31+l) + e) / P with 0 <= e < P <= 2^l, so t mul / 2^(31+l) exceeds t / P by
+// t e / (P 2^(31+l)) < 1 / P, which never reaches the next integer: the quotient is
+// floor(t mul / 2^(31+l)) = umulhi(t, mul) >> (l - 1).
+inline void page_divisor(int32_t P, uint32_t& mul, int32_t& sh) {
+  int l = 0;
+  while ((1LL << l) < P) ++l;
+  const unsigned long long num = 1ULL << (31 + l);
+  mul = (uint32_t)((num + (unsigned long long)P - 1) / (unsigned long long)P);
+  sh = l - 1;
+}
+
+__device__ inline int page_of(int t, uint32_t mul, int sh) {
+  return (int)(__umulhi((uint32_t)t, mul) >> sh);
+}
+
+// A tensor scale for which the NVFP4 encoder may take the quotient route: a power of two in the
+// range where the quotients of bf16 or scaled FP8 sources stay exact enough (host side).
+inline bool pow2_in_range(float s) {
+  int e;
+  return s > 0.0f && frexpf(s, &e) == 0.5f && e >= -32 && e <= 33;
+}
 
 // ---------------------------------------------------------------------------
 // scalar conversions
@@ -144,6 +169,19 @@ struct DecodeParams {
   int32_t max_pages, batch, num_q_heads, num_kv_heads, group, page_size, num_splits;
   int32_t num_pages;        // pool size: page indices are clamped into [0, num_pages)
   float qk_scale;           // sm_scale * K global scale * log2(e)
+  uint32_t page_mul;        // token index t (0 <= t < 2^31) to page: t / page_size == umulhi(t, page_mul) >> page_sh
+  int32_t page_sh;
+  // Fused append (k_new non-null): each sequence's new token, at position seq_len - 1, is encoded
+  // into its pool slot by the wave whose split holds it, which then reads it back with its chunk.
+  const uint16_t* k_new;    // [B] rows of Hkv * D bf16, new_stride elements apart
+  const uint16_t* v_new;
+  int64_t new_stride;
+  float gs_k, gs_v;         // K and V tensor scales (NVFP4) or per-tensor scales (FP8)
+  int32_t quot;             // NVFP4: both tensor scales are powers of two (quotient encode route)
+  uint8_t* kd_w;            // the same pool arrays as kd, ks, vd, vs, written by the append
+  uint8_t* ks_w;
+  uint8_t* vd_w;
+  uint8_t* vs_w;
 };
 
 struct ExtendParams {

@@ -45,7 +45,7 @@
 //    descriptor per page slice (bounds: the slice), because buffer offsets
 //    are 32-bit. Registers hold three chunks of 32 tokens: one computing,
 //    two in flight.
-#include "common.hpp"
+#include "encode.hpp"
 
 namespace nvfp4kv {
 
@@ -180,6 +180,7 @@ __device__ inline half8_t pack_half8(const float4_t& x, const float4_t& y) {
 struct Item {
   const int32_t* bt;     // block-table row of the sequence
   int g, t1;
+  int tn;                // fused append: position of the new token if this item holds it, else -1
 };
 
 // PW: pool-wide descriptors (pool of one array < 2 GiB), else per page slice.
@@ -201,11 +202,17 @@ __device__ inline void load_tile(const DecodeParams& p, const Item& it, int tok0
   tok0 = __builtin_amdgcn_readfirstlane(min(tok0, (it.t1 - 1) & ~15));
   {
     const int P = p.page_size;
-    int page = __builtin_amdgcn_readfirstlane(it.bt[tok0 / P]);
+    // a scalar load through the constant address space (the kernel never writes the table; with the
+    // fused append's stores in the kernel the compiler could not prove that, would load it per lane,
+    // and its wait would drain the chunks in flight)
+    typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+    const int pi = page_of(tok0, p.page_mul, p.page_sh);            // tok0 / P
+    const int in_page = tok0 - pi * P;                                // tok0 mod P
+    int page = __builtin_amdgcn_readfirstlane(((const_i32_ptr)it.bt)[pi]);
     page = min(max(page, 0), p.num_pages - 1);
     const int64_t slice = ((int64_t)page * p.num_kv_heads + it.g) * P;     // first row of the (page, head) slice
     const int64_t rows = PW ? (int64_t)p.num_pages * p.num_kv_heads * P : P;  // rows the descriptor covers
-    const int soff = (int)(((PW ? slice : 0) + tok0 % P) * C::kRowBytes);
+    const int soff = (int)(((PW ? slice : 0) + in_page) * C::kRowBytes);
     const int voff = (int)((uint32_t)(r * C::kRowBytes + grp * C::kLaneBytes) | oob);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.kd + (PW ? 0 : slice) * C::kRowBytes), (short)0, (int)(rows * C::kRowBytes), kRsrcWord3);
@@ -237,11 +244,14 @@ __device__ inline void load_tile(const DecodeParams& p, const Item& it, int tok0
           (void*)(p.ks + (PW ? 0 : slice) * nb), (short)0, (int)(rows * nb), kRsrcWord3);
       const __amdgpu_buffer_rsrc_t sv = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.vs + (PW ? 0 : slice) * nb), (short)0, (int)(rows * nb), kRsrcWord3);
-      const int so = (int)(((PW ? slice : 0) + tok0 % P) * nb);
+      const int so = (int)(((PW ? slice : 0) + in_page) * nb);
       if constexpr (D == 128) {
-        const int lo = (int)((uint32_t)(r * nb + 2 * grp) | oob);
-        raw.ks = __builtin_amdgcn_raw_buffer_load_b16(sk, lo, so, C::kStream);
-        raw.vs = __builtin_amdgcn_raw_buffer_load_b16(sv, lo, so, C::kStream);
+        // the aligned word that holds the lane's two scale bytes (bytes 2 (grp mod 2) and up; the
+        // consumer shifts them down): a 16-bit load would need a zero-extension, which the compiler
+        // schedules right after the load, waiting for the chunks in flight
+        const int lo = (int)((uint32_t)(r * nb + 4 * (grp >> 1)) | oob);
+        raw.ks = __builtin_amdgcn_raw_buffer_load_b32(sk, lo, so, C::kStream);
+        raw.vs = __builtin_amdgcn_raw_buffer_load_b32(sv, lo, so, C::kStream);
       } else {
         const int lo = (int)((uint32_t)(r * nb + grp) | oob);
         raw.ks = __builtin_amdgcn_raw_buffer_load_b8(sk, lo, so, C::kStream);
@@ -288,13 +298,16 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
   using C = Cfg<D, FP8, T>;
   const int grp = lane >> 4;
 
+  // NVFP4 at D = 128: the lane's two scale bytes sit at bit 16 (grp mod 2) of its scale words
+  const uint32_t ssh = (D == 128 && !FP8) ? 16u * (uint32_t)(grp & 1) : 0u;
+
   // ---- QK: raw scores, lane (head, rows 4grp..4grp+3) of every tile
   float sc[C::kTiles][4];
 #pragma unroll
   for (int t = 0; t < C::kTiles; ++t) {
     float4_t c4 = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < C::kKSteps; ++kk) c4 = mfma(unpack<D, FP8, LUT>(cur[t].k, cur[t].ks, kk), qb[kk], c4);
+    for (int kk = 0; kk < C::kKSteps; ++kk) c4 = mfma(unpack<D, FP8, LUT>(cur[t].k, cur[t].ks >> ssh, kk), qb[kk], c4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[t][i] = c4[i];
   }
@@ -352,7 +365,7 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int kk = 0; kk < C::kKSteps; ++kk) {
-        const half8_t v = unpack<D, FP8, LUT>(cur[t + tt].v, cur[t + tt].vs, kk);
+        const half8_t v = unpack<D, FP8, LUT>(cur[t + tt].v, cur[t + tt].vs >> ssh, kk);
         *reinterpret_cast<half8_t*>(vl + (16 * tt + r) * VPitch<D>::kHalfs + grp * C::kChanPerGroup + 8 * kk) = v;
       }
     const int rd = (4 * kg + (r >> 2)) * VPitch<D>::kHalfs + 4 * (r & 3);
@@ -372,7 +385,70 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
   }
 }
 
-template <int D, bool FP8, int T, int W, bool PW, bool LUT>
+// Fused append, run by the whole wave whose split holds the new token tn: lanes 0..31 take K and
+// lanes 32..63 take V of head g, D/32 consecutive channels each, so one 16-element block spans
+// 16/(D/32) neighbouring lanes, which combine their magnitude maxima by shuffles. The encoders are
+// the quantize kernels' own (same scale, same codes); each lane stores its codes, the first lane
+// of a block its scale byte.
+template <int D, bool FP8>
+__device__ inline void append_token(const DecodeParams& p, const Item& it, int b, int lane) {
+  constexpr int kC = D / 32;                    // channels per lane: 4 or 2
+  constexpr int kSpan = kBlock / kC;            // lanes per 16-element block: 4 or 8
+  const bool isv = lane >= 32;
+  const int ch = (lane & 31) * kC;
+  // (unsigned widenings and a plain division here: this runs once, and sharing the loop's 64-bit
+  // forms of the same parameters would make the compiler lose their 32-bit range inside the loop)
+  const uint32_t P = (uint32_t)p.page_size;
+  typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+  const int page = min(max(((const_i32_ptr)it.bt)[(uint32_t)it.tn / P], 0), p.num_pages - 1);  // valid when tn >= 0
+  const uint64_t row = ((uint64_t)(uint32_t)page * (uint32_t)p.num_kv_heads + (uint32_t)it.g) * P + (uint32_t)it.tn % P;
+
+  const uint16_t* src = (isv ? p.v_new : p.k_new) + (int64_t)b * p.new_stride + (int64_t)it.g * D + ch;
+  float x[kC];
+  if constexpr (kC == 4) {
+    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
+    x[0] = __uint_as_float(w << 16);
+    x[1] = __uint_as_float(w & 0xFFFF0000u);
+  }
+  const float gs = isv ? p.gs_v : p.gs_k;
+  if constexpr (FP8) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < kC; ++e) w |= fp8_encode_one(x[e], gs) << (8 * e);
+    uint8_t* dst = (isv ? p.vd_w : p.kd_w) + row * D + ch;
+    if constexpr (kC == 4) *reinterpret_cast<uint32_t*>(dst) = w;
+    else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+  } else {
+    // block maxima on the magnitude bit patterns, over all elements and over the non-NaN ones
+    uint32_t bmax = 0, mfin = 0;
+#pragma unroll
+    for (int e = 0; e < kC; ++e) {
+      const uint32_t m = __float_as_uint(x[e]) & 0x7FFFFFFFu;
+      bmax = max(bmax, m);
+      mfin = max(mfin, m > 0x7F800000u ? 0u : m);
+    }
+#pragma unroll
+    for (int o = 1; o < kSpan; o <<= 1) {
+      bmax = max(bmax, (uint32_t)__shfl_xor((int)bmax, o, 64));
+      mfin = max(mfin, (uint32_t)__shfl_xor((int)mfin, o, 64));
+    }
+    BlockScale k = nvfp4_block_scale<true>(bmax, __uint_as_float(bmax > 0x7F800000u ? mfin : bmax), gs);
+    if (!p.quot) k.quot = false;                 // the tensor scales allow the compares only
+    const uint32_t codes = nvfp4_codes<kC>(x, k);
+    uint8_t* dst = (isv ? p.vd_w : p.kd_w) + row * (D / 2) + ch / 2;
+    if constexpr (kC == 4) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)codes;
+    else *dst = (uint8_t)codes;
+    if ((lane & (kSpan - 1)) == 0) (isv ? p.vs_w : p.ks_w)[row * (D / kBlock) + ch / kBlock] = (uint8_t)k.sbyte;
+  }
+}
+
+template <int D, bool FP8, int T, int W, bool PW, bool LUT, bool APPEND>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(W)))
 void decode_partial_mfma_kernel(DecodeParams p) {
   using C = Cfg<D, FP8, T>;
@@ -384,10 +460,21 @@ void decode_partial_mfma_kernel(DecodeParams p) {
   const int S = p.num_splits;
   const int P = p.page_size;
   // wave-uniform (keeps offsets scalar); tokens past the table's reach are not read
-  const int L = min(__builtin_amdgcn_readfirstlane(p.seq_lens[b]), p.max_pages * P);
+  const int Lraw = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+  const int L = min(Lraw, p.max_pages * P);
   const int per = ceil_div(ceil_div(L, S), P) * P;
   const int t0 = j * per;
-  const Item it{p.block_tables + (int64_t)b * p.max_pages, g, min(L, t0 + per)};
+  // the new token (fused append) sits at position L - 1 of a sequence within the table's reach,
+  // in a valid page (the quantize kernels skip a slot outside the pool, and so does the append)
+  int tn = -1;
+  if constexpr (APPEND) {
+    if (Lraw >= 1 && Lraw == L && t0 <= L - 1 && L - 1 < t0 + per) {
+      typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+      const int pg = ((const_i32_ptr)(p.block_tables + (int64_t)b * p.max_pages))[(L - 1) / P];
+      if (pg >= 0 && pg < p.num_pages) tn = L - 1;
+    }
+  }
+  const Item it{p.block_tables + (int64_t)b * p.max_pages, g, min(L, t0 + per), tn};
   const int64_t qh0 = (int64_t)b * p.num_q_heads + (int64_t)g * G;
 
   // LDS: the unpacked V rows of a chunk in the loop, the partial results at the end
@@ -404,6 +491,18 @@ void decode_partial_mfma_kernel(DecodeParams p) {
     // The prologue's K/V loads are complete once q has arrived (q is loaded
     // after them and the load counter is in order), so the loop below starts
     // from a state with nothing outstanding and the same on every iteration.
+    // Fused append, in the one wave per (sequence, KV head) that holds the new token. Its loads and
+    // stores complete inside the branch, so nothing of them is outstanding on either path into the
+    // chunk pipeline below, and the wave then reads the new token back with its chunk, after the
+    // stores have completed; no stale copy can sit in the CU's cache (it starts the kernel empty,
+    // and only this wave reads the token's page, since splits are page-aligned and pages shared
+    // with other sequences hold earlier tokens only).
+    if constexpr (APPEND) {
+      if (it.tn >= 0) {                                            // wave-uniform
+        append_token<D, FP8>(p, it, b, lane);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    }
     TileRaw<D, FP8> b0[C::kTiles], b1[C::kTiles], b2[C::kTiles];
     load_chunk<D, FP8, T, PW>(p, it, t0, lane, b0);
     load_chunk<D, FP8, T, PW>(p, it, t0 + C::kChunk, lane, b1);
@@ -489,10 +588,14 @@ hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.num_kv_heads, p.num_splits, p.batch);
   // buffer offsets and bounds are 32-bit: whole-pool descriptors only below 2 GiB per array
   const int64_t pool_bytes = (int64_t)p.num_pages * p.num_kv_heads * p.page_size * Cfg<D, FP8, T>::kRowBytes;
-  if (pool_bytes <= INT32_MAX)
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, true, LUT>), grid, dim3(64), 0, s, p);
-  else
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, false, LUT>), grid, dim3(64), 0, s, p);
+  const bool pw = pool_bytes <= INT32_MAX;
+  if (p.k_new) {
+    if (pw) hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, true, LUT, true>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, false, LUT, true>), grid, dim3(64), 0, s, p);
+  } else {
+    if (pw) hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, true, LUT, false>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, false, LUT, false>), grid, dim3(64), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -159,6 +159,49 @@ def test_noalloc_decode_rejects_partials_past_its_static_scratch(L):
     assert _noalloc(L, g, B=0) == L.OK                                   # nothing to do, nothing launched
 
 
+def _append(L, g, fp8=False, knew=FAKE, vnew=FAKE, stride=64, B=1, S=1, out=FAKE, ws_bytes=1 << 20, partial=False):
+    name = ("fp8" if fp8 else "nvfp4") + ("_paged_decode_append_partial" if partial else "_paged_decode_append_attn")
+    f = getattr(L.lib(), name)
+    if fp8:
+        kc, vc = L.FP8CacheDesc(FAKE, 1.0), L.FP8CacheDesc(FAKE, 1.0)
+    else:
+        kc, vc = _nv(L), _nv(L)
+    args = [ctypes.byref(g), FAKE, knew, vnew, stride, ctypes.byref(kc), ctypes.byref(vc), FAKE, 16, FAKE, B, 4,
+            0.125, S, FAKE, ws_bytes]
+    return f(*(args if partial else args + [out]), None)
+
+
+def test_append_decode_rejects_bad_new_tokens(L):
+    """The decode step with the new token validates the new-token rows on the
+    host (no HIP call): present, 16-byte aligned, rows at least Hkv * d
+    elements apart and a multiple of 8."""
+    g = _geom(L, H=1, d=64)
+    for fp8 in (False, True):
+        assert _append(L, g, fp8, knew=None) == L.EINVAL
+        assert _append(L, g, fp8, vnew=None) == L.EINVAL
+        assert _append(L, g, fp8, knew=FAKE + 2) == L.EALIGN
+        assert _append(L, g, fp8, stride=63) == L.EINVAL                # below Hkv * d
+        assert _append(L, g, fp8, stride=68) == L.EINVAL                # not a multiple of 8
+        assert "new_stride" in L.last_error()
+        assert _append(L, g, fp8, out=None) == L.EINVAL
+        assert _append(L, g, fp8, S=5000) == L.EINVAL
+        assert _append(L, g, fp8, ws_bytes=16) == L.EWORKSPACE
+        assert _append(L, g, fp8, B=0, knew=None, vnew=None) == L.OK   # nothing to do, nothing launched
+
+
+def test_append_partial_rejects_bad_arguments(L):
+    """The append step without the merge checks what the full step checks,
+    except the output, and needs an explicit split count."""
+    g = _geom(L, H=1, d=64)
+    for fp8 in (False, True):
+        assert _append(L, g, fp8, partial=True, S=0) == L.EINVAL
+        assert _append(L, g, fp8, partial=True, knew=None) == L.EINVAL
+        assert _append(L, g, fp8, partial=True, vnew=FAKE + 8) == L.EALIGN
+        assert _append(L, g, fp8, partial=True, stride=68) == L.EINVAL
+        assert _append(L, g, fp8, partial=True, ws_bytes=16) == L.EWORKSPACE
+        assert _append(L, g, fp8, partial=True, B=0, knew=None, vnew=None) == L.OK
+
+
 def test_partial_rejects_bad_variant_and_auto_splits(L):
     g = _geom(L)
     kc, vc = _nv(L), _nv(L)

@@ -1146,6 +1146,157 @@ def test_fp8_decode_moderate(nk):
         check_out(out, ref, mass, f"fp8 variant={var}")
 
 
+def _append_case(nk, fmt, d, G, P, gs, S, seed, special=False, partial=False):
+    """Pools holding each sequence's earlier tokens, a block table over a page
+    permutation, the step's new token per sequence, and lengths that cover an
+    empty sequence, one token, page boundaries, odd lengths, a length past the
+    table's reach and a new token whose table entry is outside the pool.
+    special: the new tokens also hold NaN, infinities, signed zeros, bf16
+    subnormals and values near the bf16 maximum, in blocks of their own and
+    mixed with finite values at every lane position of a block.
+    partial: the two sides stop at the partials (workspaces returned in place
+    of the outputs): quantize + the MFMA partial kernel against the append
+    partial."""
+    rng = np.random.default_rng(seed)
+    H, B = 2, 8
+    Hq = H * G
+    lens = [0, 1, P, P + 1, 3 * P - 1, 5 * P + 7, 2 * P + 3, 4 * P]
+    max_pages = (max(lens) + P - 1) // P + 1
+    reach = max_pages * P
+    lens[7] = reach + 5                                  # past the table: nothing appended, clamped decode
+    num_pages = B * max_pages + 3
+    perm = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    perm[6, (lens[6] - 1) // P] = num_pages + 4          # the new token's page is outside the pool
+    bt = torch.from_numpy(perm).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    # earlier tokens: positions 0 .. L - 2 of every sequence (within the table and the pool)
+    slots, rows = [], []
+    for b, L in enumerate(lens):
+        for t in range(min(L, reach) - 1):
+            if perm[b, t // P] < num_pages:
+                slots.append(int(perm[b, t // P]) * P + t % P)
+    T = len(slots)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    k_old = (torch.randn((T, H, d), generator=gen, device="cuda") * 3).to(torch.bfloat16)
+    v_old = (torch.randn((T, H, d), generator=gen, device="cuda") * 3).to(torch.bfloat16)
+    k_new = (torch.randn((B, H, d), generator=gen, device="cuda") * 3).to(torch.bfloat16)
+    v_new = (torch.randn((B, H, d), generator=gen, device="cuda") * 3).to(torch.bfloat16)
+    k_new[2, 0, :16] = 0.0                               # an all-zero block
+    v_new[3, 1, 5] = 1e30                                # a block scale that saturates
+    if special:
+        nan, inf = float("nan"), float("inf")
+        for b in range(B):
+            for h in range(H):
+                for t in (k_new, v_new):
+                    row = t[b, h]
+                    blk = (b + 2 * h + (t is v_new)) % (d // 16)
+                    pos = (3 * b + h) % 16
+                    kind = (b + h + (t is v_new)) % 6
+                    if kind == 0:
+                        row[16 * blk + pos] = nan                    # NaN among finite values
+                    elif kind == 1:
+                        row[16 * blk:16 * blk + 16] = nan            # a block of NaN only
+                    elif kind == 2:
+                        row[16 * blk + pos] = inf if b % 2 else -inf  # an infinity
+                        row[16 * blk + (pos + 5) % 16] = nan
+                    elif kind == 3:
+                        row[16 * blk:16 * blk + 16] = 1e-39          # bf16 subnormals
+                        row[16 * blk + pos] = -0.0
+                    elif kind == 4:
+                        row[16 * blk + pos] = 3.3e38                 # near the bf16 maximum
+                    else:
+                        row[16 * blk:16 * blk + 16] = -0.0           # negative zeros only
+    q = torch.randn((B, Hq, d), generator=gen, device="cuda").to(torch.bfloat16)
+    if fmt == "nvfp4":
+        mk = lambda: nv_pools(nk, num_pages, H, P, d, gs)
+        quant, attn, app = nk.nvfp4_kv_quantize, nk.nvfp4_paged_decode_attn, nk.nvfp4_paged_decode_append_attn
+    else:
+        mk = lambda: f8_pools(nk, num_pages, H, P, d, scale=gs)
+        quant, attn, app = nk.fp8_kv_quantize, nk.fp8_paged_decode_attn, nk.fp8_paged_decode_append_attn
+    kA, vA = mk()
+    if T:
+        quant(k_old, v_old, torch.tensor(slots, dtype=torch.int64, device="cuda"), kA, vA)
+    kB, vB = mk()
+    for dst, src in ((kB, kA), (vB, vA)):
+        dst.data.copy_(src.data)
+        if fmt == "nvfp4":
+            dst.scale.copy_(src.scale)
+    # the composition: quantize each new token into the slot of position L - 1, then decode
+    new_slots = []
+    for b, L in enumerate(lens):
+        if 1 <= L <= reach:
+            new_slots.append(int(perm[b, (L - 1) // P]) * P + (L - 1) % P)
+        else:
+            new_slots.append(-1)
+    quant(k_new, v_new, torch.tensor(new_slots, dtype=torch.int64, device="cuda"), kA, vA)
+    if partial:
+        if fmt == "nvfp4":
+            part, app_part = nk.nvfp4_paged_decode_partial, nk.nvfp4_paged_decode_append_partial
+        else:
+            part, app_part = nk.fp8_paged_decode_partial, nk.fp8_paged_decode_append_partial
+        outA = part(q, kA, vA, bt, sl, 0.125, S, variant=nk.VARIANT_MFMA)
+        outB = app_part(q, k_new, v_new, kB, vB, bt, sl, 0.125, S)
+    else:
+        outA = attn(q, kA, vA, bt, sl, 0.125, num_splits=S)
+        outB = app(q, k_new, v_new, kB, vB, bt, sl, 0.125, num_splits=S)
+    torch.cuda.synchronize()
+    return (kA, vA, outA), (kB, vB, outB)
+
+
+@pytest.mark.parametrize("fmt,d,G,P,gs,S", [
+    ("nvfp4", 128, 5, 64, 1.0, 0), ("nvfp4", 128, 5, 16, 1.0, 3), ("nvfp4", 128, 4, 48, 1.0 / 3.0, 2),
+    ("nvfp4", 64, 8, 16, 2.0, 1), ("nvfp4", 64, 1, 32, 0.3, 5), ("nvfp4", 128, 16, 16, 0.25, 7),
+    ("fp8", 128, 5, 64, 1.0, 0), ("fp8", 64, 4, 16, 0.5, 3), ("fp8", 128, 8, 48, 0.3, 2),
+])
+def test_decode_append_matches_quantize_then_decode(nk, fmt, d, G, P, gs, S):
+    """The decode step with the new token encoded by the decode kernel leaves
+    every pool byte and the output equal, bit for bit, to quantize-on-write of
+    the new tokens into their slots followed by the decode."""
+    say(f"case append {fmt} d{d} G{G} P{P} gs {gs} splits {S}")
+    (kA, vA, outA), (kB, vB, outB) = _append_case(nk, fmt, d, G, P, gs, S, seed=700 + d + G + P)
+    assert torch.equal(kA.data, kB.data) and torch.equal(vA.data, vB.data)
+    if fmt == "nvfp4":
+        assert torch.equal(kA.scale, kB.scale) and torch.equal(vA.scale, vB.scale)
+    assert torch.equal(outA, outB)
+
+
+@pytest.mark.parametrize("fmt,d,G,P,gs,S", [("nvfp4", 128, 5, 64, 1.0, 4), ("nvfp4", 64, 4, 48, 0.3, 2),
+                                             ("fp8", 128, 8, 16, 0.5, 3), ("fp8", 64, 2, 32, 1.0, 1)])
+def test_decode_append_partial_then_merge(nk, fmt, d, G, P, gs, S):
+    """The append step without the merge: pool bytes and fp32 partials equal,
+    bit for bit, quantize-on-write followed by the MFMA partial kernel, and the
+    merge of those partials gives the full append step's output."""
+    say(f"case append partial {fmt} d{d} G{G} P{P} gs {gs} splits {S}")
+    (kA, vA, wsA), (kB, vB, wsB) = _append_case(nk, fmt, d, G, P, gs, S, seed=800 + d + G + P, partial=True)
+    assert torch.equal(kA.data, kB.data) and torch.equal(vA.data, vB.data)
+    if fmt == "nvfp4":
+        assert torch.equal(kA.scale, kB.scale) and torch.equal(vA.scale, vB.scale)
+    assert torch.equal(wsA, wsB)
+    # the full step (and the separate calls) on the same inputs
+    (_, _, outA), (_, _, outB) = _append_case(nk, fmt, d, G, P, gs, S, seed=800 + d + G + P)
+    B, Hq = outA.shape[0], outA.shape[1]
+    merged = nk.nvfp4kv_lse_merge(wsB, B, Hq, d, S, vB.global_scale if fmt == "nvfp4" else vB.scale,
+                                  torch.empty_like(outB))
+    torch.cuda.synchronize()
+    assert torch.equal(merged, outB) and torch.equal(outA, outB)
+
+
+@pytest.mark.parametrize("fmt,d,gs", [("nvfp4", 128, 1.0), ("nvfp4", 64, 0.5), ("nvfp4", 128, 0.3),
+                                       ("nvfp4", 64, 3.0), ("fp8", 128, 1.0), ("fp8", 64, 0.3)])
+def test_decode_append_special_values(nk, fmt, d, gs):
+    """New tokens with NaN, infinities, signed zeros, subnormals and values near
+    the bf16 maximum: the appended pool bytes equal quantize-on-write's, bit for
+    bit (both the quotient and the compare encode routes), and so do the
+    outputs' bit patterns (NaN included)."""
+    say(f"case append special values {fmt} d{d} gs {gs}")
+    (kA, vA, outA), (kB, vB, outB) = _append_case(nk, fmt, d, 4, 16, gs, 3, seed=900 + d, special=True)
+    assert torch.equal(kA.data, kB.data) and torch.equal(vA.data, vB.data)
+    if fmt == "nvfp4":
+        assert torch.equal(kA.scale, kB.scale) and torch.equal(vA.scale, vB.scale)
+    assert torch.equal(outA.view(torch.int16), outB.view(torch.int16))
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
 def test_decode_pool_above_2gib(nk, fmt):
     """Pools of more than 2 GiB per array (buffer offsets are 32-bit, so the
