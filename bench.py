@@ -92,7 +92,7 @@ def new_token_bytes(wl, fp8=False, batch=None):
 
 def partial_bytes(wl, splits, batch=None):
     B = wl.batch if batch is None else batch
-    return B * wl.num_q_heads * splits * (wl.head_dim + 2) * 4
+    return B * wl.num_q_heads * splits * (wl.head_dim * 2 + 8)      # f16 o / l, fp32 (m, l)
 
 
 def source_digest():

@@ -205,16 +205,16 @@ int nvfp4_kv_dequant_workspace_fp8(const nvfp4kv_geom* geom, const nvfp4kv_cache
  * Split-KV decode. Each (sequence b, KV head g, split j) item attends the G =
  * num_q_heads / Hkv query heads h = g*G .. g*G+G-1 to the tokens
  * [j*C, min(L_b, (j+1)*C)) with C = ceil(ceil(L_b / num_splits) / P) * P
- * (page-aligned), producing an unnormalised partial (m, l, o[d]); a second
- * kernel merges the splits by log-sum-exp. Query head h reads KV head h / G.
+ * (page-aligned), producing a partial (m, l, o[d] / l); a second kernel merges
+ * the splits by log-sum-exp. Query head h reads KV head h / G.
  *
  * nvfp4_paged_decode_num_splits -- the library's split count for a batch when
  *   the caller passes num_splits = 0 (depends on sizes only: as many splits
  *   as keep batch * num_kv_heads * splits within 3072 work items, one round
  *   of the chip's resident wave slots, at least 1, at most one split per 128
  *   tokens of the longest possible sequence, max_pages_per_seq * page_size).
- * nvfp4_paged_decode_workspace_bytes -- bytes of the fp32 partials:
- *   batch * num_q_heads * num_splits * (head_dim + 2) * 4.
+ * nvfp4_paged_decode_workspace_bytes -- bytes of the partials:
+ *   batch * num_q_heads * num_splits * (head_dim * 2 + 8).
  */
 int32_t nvfp4_paged_decode_num_splits(int32_t batch, int32_t num_kv_heads,
                                       int32_t max_pages_per_seq, int32_t page_size);
@@ -296,12 +296,12 @@ int nvfp4_paged_decode_append_partial(const nvfp4kv_geom* geom, const void* q, c
  * nvfp4_paged_decode_attn_noalloc -- nvfp4_paged_decode_attn for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc. Same arguments and result without
- * the workspace: the fp32 partials go to a static device array of the
+ * the workspace: the partials go to a static device array of the
  * library, nvfp4_paged_decode_noalloc_scratch_bytes() = 32 MiB on each GPU it
  * runs on (allocated with the code object, held until the process ends). The
  * call itself allocates nothing and calls no allocating routine.
  *
- *   num_splits   1..4096 with batch * num_q_heads * num_splits * (head_dim + 2) * 4
+ *   num_splits   1..4096 with batch * num_q_heads * num_splits * (head_dim * 2 + 8)
  *                <= 32 MiB, else NVFP4KV_EWORKSPACE; or 0 for the library's
  *                count (nvfp4_paged_decode_num_splits), lowered so that the
  *                partials fit (NVFP4KV_EWORKSPACE if one split does not)
@@ -325,9 +325,12 @@ size_t nvfp4_paged_decode_noalloc_scratch_bytes(void);
 
 /*
  * nvfp4_paged_decode_partial -- phase 1 only: writes the partials of every
- * (b, h, split) into `workspace` (layout: fp32 o [batch][Hq][num_splits][d]
+ * (b, h, split) into `workspace` (layout: f16 u [batch][Hq][num_splits][d]
  * followed by fp32 (m, l) [batch][Hq][num_splits][2]; m is in base-2 logit
- * units, l = sum of 2^(logit2 - m); an empty split has m = -inf, l = 0).
+ * units, l = sum of 2^(logit2 - m), u = sum of 2^(logit2 - m) v / l rounded
+ * to f16 (nearest even), the split's softmax-weighted mean of the dequantized
+ * V rows before the V tensor scale, so |u| <= 6 * 448; an empty split has
+ * m = -inf, l = 0, u = 0).
  * `variant` selects the kernel (NVFP4KV_VARIANT_*). num_splits must be >= 1.
  */
 int nvfp4_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,

@@ -593,9 +593,10 @@ def nvfp4kv_lse_merge(workspace, batch, num_q_heads, head_dim, num_splits, out_s
 
 
 def split_partials(workspace: torch.Tensor, batch, num_q_heads, head_dim, num_splits):
-    """Views (o [B][Hq][S][d], ml [B][Hq][S][2]) of a decode workspace's fp32 partials."""
-    f = workspace.view(torch.float32)
+    """Views (u [B][Hq][S][d] f16, ml [B][Hq][S][2] fp32) of a decode workspace's partials:
+    u is each split's o / l, (m, l) its base-2 maximum logit and softmax denominator."""
+    raw = workspace.view(torch.uint8)
     n = batch * num_q_heads * num_splits * head_dim
-    o = f[:n].view(batch, num_q_heads, num_splits, head_dim)
-    ml = f[n:n + batch * num_q_heads * num_splits * 2].view(batch, num_q_heads, num_splits, 2)
-    return o, ml
+    u = raw[:2 * n].view(torch.float16).view(batch, num_q_heads, num_splits, head_dim)
+    ml = raw[2 * n:2 * n + 8 * batch * num_q_heads * num_splits].view(torch.float32)
+    return u, ml.view(batch, num_q_heads, num_splits, 2)

@@ -147,8 +147,8 @@ DecodeParams make_decode(const nvfp4kv_geom* g, const void* q, const uint8_t* kd
   p.vs = vs;
   p.block_tables = bt;
   p.seq_lens = seq_lens;
-  p.part_o = static_cast<float*>(workspace);
-  p.part_ml = p.part_o + (size_t)batch * hq * c.splits * g->head_dim;
+  p.part_o = static_cast<_Float16*>(workspace);
+  p.part_ml = reinterpret_cast<float*>(p.part_o + (size_t)batch * hq * c.splits * g->head_dim);
   p.max_pages = max_pages;
   p.batch = batch;
   p.num_q_heads = hq;
@@ -318,7 +318,8 @@ NVFP4KV_API int32_t nvfp4_paged_decode_num_splits(int32_t batch, int32_t num_kv_
 NVFP4KV_API size_t nvfp4_paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                                       int32_t head_dim, int32_t num_splits) {
   if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
-  return (size_t)batch * num_q_heads * num_splits * (head_dim + 2) * sizeof(float);
+  // f16 o / l per (sequence, query head, split, channel), then fp32 (m, l)
+  return (size_t)batch * num_q_heads * num_splits * ((size_t)head_dim * 2 + 2 * sizeof(float));
 }
 
 NVFP4KV_API int nvfp4_kv_quantize(const nvfp4kv_geom* geom, const void* k, const void* v,
@@ -795,8 +796,8 @@ NVFP4KV_API int nvfp4kv_lse_merge(const void* workspace, size_t workspace_bytes,
   if (workspace_bytes < need)
     return fail(NVFP4KV_EWORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
   MergeParams m{};
-  m.part_o = static_cast<const float*>(workspace);
-  m.part_ml = m.part_o + (size_t)batch * num_q_heads * num_splits * head_dim;
+  m.part_o = static_cast<const _Float16*>(workspace);
+  m.part_ml = reinterpret_cast<const float*>(m.part_o + (size_t)batch * num_q_heads * num_splits * head_dim);
   m.batch = batch;
   m.num_q_heads = num_q_heads;
   m.head_dim = head_dim;

@@ -164,8 +164,8 @@ struct DecodeParams {
   const uint8_t* vs;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* part_o;            // [B][Hq][S][D]
-  float* part_ml;           // [B][Hq][S][2]
+  _Float16* part_o;         // [B][Hq][S][D] f16: each split's o / l (0 for an empty split)
+  float* part_ml;           // [B][Hq][S][2]: (m, l)
   int32_t max_pages, batch, num_q_heads, num_kv_heads, group, page_size, num_splits;
   int32_t num_pages;        // pool size: page indices are clamped into [0, num_pages)
   float qk_scale;           // sm_scale * K global scale * log2(e)
@@ -197,7 +197,7 @@ struct ExtendParams {
 };
 
 struct MergeParams {
-  const float* part_o;
+  const _Float16* part_o;   // as DecodeParams
   const float* part_ml;
   int32_t batch, num_q_heads, head_dim, num_splits;
   float out_scale;

@@ -207,8 +207,11 @@ __global__ __launch_bounds__(64) void decode_partial_valu_kernel(DecodeParams p)
     if (h < G) {
       const float lt = wave_sum(l[h]);
       const int64_t idx = (qh0 + h) * S + j;
-      if (lane < D / 2) {
-        *reinterpret_cast<float2*>(p.part_o + idx * D + 2 * lane) = make_float2(acc0[h], acc1[h]);
+      if (lane < D / 2) {   // o / l in f16, as the MFMA kernel writes it
+        const float il = lt > 0.0f ? 1.0f / lt : 0.0f;
+        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<half2_t*>(p.part_o + idx * D + 2 * lane) =
+            half2_t{(_Float16)(acc0[h] * il), (_Float16)(acc1[h] * il)};
       }
       if (lane == 0) {
         p.part_ml[idx * 2] = m[h];

@@ -3,6 +3,8 @@
 // The pages describe no split-KV scheme; the merge is the standard identity
 // that recombines softmax partials: with per-split (m_j, l_j, o_j) in base-2
 // logit units, M = max_j m_j, out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j.
+// The partials hold u_j = o_j / l_j in f16, so the weight of row j is
+// 2^(m_j - M) l_j.
 // The V tensor-level scale is applied here, as the scaling parameter of the
 // PV product ("Accelerating Long-Context and Agentic Inference with NVFP4 KV
 // Cache", section A2, decode-kernel paragraph, Fig. 3). Empty splits (l = 0)
@@ -11,7 +13,7 @@
 // One workgroup per (sequence, query head): 4 waves when there are at most 64
 // splits, else 16. Wave w owns splits j = w (mod waves). Before the weights
 // are known, each wave already loads its first eight partial rows (coalesced
-// 8-byte loads per lane: channels 2*lane, 2*lane+1), so the row latency
+// 4-byte loads per lane: channels 2*lane, 2*lane+1), so the row latency
 // overlaps the (m, l) loads and the two block reductions (M, then the
 // denominator); further rows stream eight at a time. The waves' sums are
 // combined through LDS.
@@ -49,14 +51,15 @@ __device__ inline float block_sum(float v, float* red) {
 }
 
 template <int D>
-__device__ inline void load_row(const float* o, int S, int j, int lane, float (&v)[D / 64]) {
-  const float* row = o + (int64_t)min(j, S - 1) * D + (D / 64) * lane;   // j >= S: any row, weight 0
+__device__ inline void load_row(const _Float16* o, int S, int j, int lane, float (&v)[D / 64]) {
+  const _Float16* row = o + (int64_t)min(j, S - 1) * D + (D / 64) * lane;   // j >= S: any row, weight 0
   if constexpr (D == 128) {
-    const float2 t = *reinterpret_cast<const float2*>(row);
-    v[0] = t.x;
-    v[1] = t.y;
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    const half2_t t = *reinterpret_cast<const half2_t*>(row);
+    v[0] = (float)t[0];
+    v[1] = (float)t[1];
   } else {
-    v[0] = row[0];
+    v[0] = (float)row[0];
   }
 }
 
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(64 * WAVES) void lse_merge_kernel(MergeParams p) {
   const int S = p.num_splits;
   const int64_t bh = (int64_t)b * p.num_q_heads + h;
   const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + bh * S;
-  const float* o = p.part_o + bh * S * D;
+  const _Float16* o = p.part_o + bh * S * D;
 
   __shared__ float wgt[kMaxSplitsLds];
   __shared__ float red[WAVES];
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(64 * WAVES) void lse_merge_kernel(MergeParams p) {
   for (int j = tid; j < S; j += kThreads) {
     const float2 e = ml[j];
     const float w = e.y > 0.0f ? exp2f(e.x - M) : 0.0f;
-    wgt[j] = w;
+    wgt[j] = w * e.y;                          // the row holds o / l
     dloc = fmaf(w, e.y, dloc);
   }
   const float den = block_sum<WAVES>(dloc, red);   // also orders the wgt[] writes before the reads below

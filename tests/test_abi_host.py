@@ -62,7 +62,7 @@ def test_split_heuristic_and_workspace_size(L):
     assert L.nvfp4_paged_decode_num_splits(8, 8, 256, 16) == 32        # 4096 tokens: the 128-token cap
     assert L.nvfp4_paged_decode_num_splits(2, 1, 10, 16) == 2          # 160 tokens
     assert L.nvfp4_paged_decode_num_splits(1, 1, 16, 16) == 2
-    assert L.nvfp4_paged_decode_workspace_bytes(44, 40, 128, 32) == 44 * 40 * 32 * 130 * 4
+    assert L.nvfp4_paged_decode_workspace_bytes(44, 40, 128, 32) == 44 * 40 * 32 * (128 * 2 + 8)
     assert L.nvfp4_paged_decode_workspace_bytes(0, 40, 128, 32) == 0
 
 
@@ -146,11 +146,11 @@ def test_noalloc_decode_rejects_partials_past_its_static_scratch(L):
     split does not fit, are rejected on the host (no HIP call)."""
     assert L.lib().nvfp4_paged_decode_noalloc_scratch_bytes() == 32 << 20
     g = _geom(L, H=1, d=64)
-    per_split = 100 * 16 * (64 + 2) * 4                      # batch 100, 16 query heads
+    per_split = 100 * 16 * (64 * 2 + 8)                      # batch 100, 16 query heads
     S = (32 << 20) // per_split + 1
     assert _noalloc(L, g, B=100, Hq=16, S=S) == L.EWORKSPACE
     assert "static scratch" in L.last_error()
-    assert _noalloc(L, g, B=65535, Hq=16, S=1) == L.EWORKSPACE            # one split is 276 MB
+    assert _noalloc(L, g, B=65535, Hq=16, S=1) == L.EWORKSPACE            # one split is 143 MB
     assert _noalloc(L, g, B=65535, Hq=16, S=0) == L.EWORKSPACE            # auto cannot lower below one
     assert _noalloc(L, g, out=None) == L.EINVAL
     assert _noalloc(L, g, out=FAKE + 2) == L.EALIGN

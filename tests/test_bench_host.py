@@ -21,15 +21,19 @@ def test_more_than_one_gpu_is_refused_before_any_device_work():
 
 def test_algorithmic_bytes_of_the_long_context_decode_launch():
     """The roofline's bytes are packed KV + scales (144 B per token per KV head
-    at d = 128) + q and out in bf16: 1,661,845,504 B per step at 32K, batch 44.
-    The fp32 partials (29,286,400 B at 32 splits) are reported apart."""
+    at d = 128) + q and out in bf16 + the new token of every sequence (bf16 K/V
+    rows in, 144 B encoded out per KV head): 1,662,076,416 B per step at 32K,
+    batch 44. The partials (f16 o / l and fp32 (m, l): 14,868,480 B at 32
+    splits) are reported apart."""
     wl = synth.WORKLOADS[3]
     assert (wl.batch, wl.context, wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.num_splits) == \
         (44, 32768, 8, 40, 128, 32)
     kvb = bench.kv_bytes(wl)
     assert kvb == 44 * 32768 * 8 * 144
     assert kvb + bench.io_bytes(wl) == 1_661_845_504
-    assert bench.partial_bytes(wl, wl.num_splits) == 29_286_400
+    assert bench.new_token_bytes(wl) == 44 * 8 * (2 * 128 * 2 + 144)
+    assert kvb + bench.io_bytes(wl) + bench.new_token_bytes(wl) == 1_662_076_416
+    assert bench.partial_bytes(wl, wl.num_splits) == 44 * 40 * 32 * (128 * 2 + 8) == 14_868_480
     # the FP8 cache moves d bytes per element pair instead of d/2 + d/16: 1/0.5625 as many
     assert bench.kv_bytes(wl, fp8=True) * 9 == kvb * 16
     # other batch sizes (the decode figures) scale linearly
