@@ -635,8 +635,10 @@ def extend_parity(w, qx, ox, q_offs_host, b=5, last=4):
 
 def agentic(nk, wl, iters, warmup, flush, pool, parity=True):
     """The prefix-reuse step (quantize the new chunk, dequantize every cached
-    prefix into the workspace, decode all sequences): the whole step and each
-    kernel alone, timed as time_flushed does. Run twice: with bf16 chunk and
+    prefix into the workspace, decode all sequences with the shared-prefix
+    decode, which unpacks the batch's common 2,800-token prefix once per 16
+    query columns): the whole step and each kernel alone, timed as
+    time_flushed does; the plain decode of the same batch is timed beside it. Run twice: with bf16 chunk and
     workspace (the workload definition) and with the pages' FP8 types (FP8
     chunk quantized to NVFP4 and copied into an FP8 workspace in one pass,
     FP8 workspace). Then extend attention over the workspace and the
@@ -651,10 +653,16 @@ def agentic(nk, wl, iters, warmup, flush, pool, parity=True):
     S = nk.nvfp4_paged_decode_num_splits(B, H, w.bt.shape[1], wl.page_size)
     ws = nk.decode_workspace(B, Hq, d, S)
     out = torch.empty_like(w.q)
+    out_plain = torch.empty_like(w.q)
+    shared = wl.shared_prefix
+    wsc = torch.empty(nk.nvfp4_paged_decode_shared_prefix_workspace_bytes(w.kp, w.bt.shape[1], B, Hq, shared),
+                      dtype=torch.uint8, device="cuda")
     quant = lambda: nk.nvfp4_kv_quantize(w.k_chunk, w.v_chunk, w.slot_chunk, w.kp, w.vp)
     deq = lambda: nk.nvfp4_kv_dequant_workspace(w.kp, w.vp, w.bt, w.cached_lens, w.ws_row_offsets, w.k_ws, w.v_ws)
-    decode = lambda: nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale,
-                                                num_splits=S, workspace=ws, out=out)
+    decode = lambda: nk.nvfp4_paged_decode_attn_shared_prefix(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale,
+                                                              shared, workspace=wsc, out=out)
+    decode_plain = lambda: nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale,
+                                                      num_splits=S, workspace=ws, out=out_plain)
 
     def step():
         quant()
@@ -664,7 +672,8 @@ def agentic(nk, wl, iters, warmup, flush, pool, parity=True):
     ts = time_flushed(step, iters, warmup, flush, ramp_s=0.2)
     tq = time_flushed(quant, iters, warmup, flush, ramp_s=0.1)
     td = time_flushed(deq, iters, warmup, flush, ramp_s=0.1)
-    tc = time_flushed(decode, iters, warmup, flush, ramp_s=0.1)
+    tcs = time_flushed_interleaved({"shared": decode, "plain": decode_plain}, iters, warmup, flush, ramp_s=0.1)
+    tc, tcp = tcs["shared"], tcs["plain"]
     med = lambda r: r["median_ms"] / 1e3
     res = {
         "workload": wl.name, "batch": B, "len_min": wl.len_min, "len_max": wl.len_max,
@@ -674,11 +683,15 @@ def agentic(nk, wl, iters, warmup, flush, pool, parity=True):
         "dequant_workspace": {**td, "gbs_unique": round((by["dequant_read_unique"] + by["dequant_write"]) / med(td) / 1e9, 1),
                               "write_gbs": round(by["dequant_write"] / med(td) / 1e9, 1)},
         "decode": {**tc, "kv_gbs_logical": round(by["decode_read_logical"] / med(tc) / 1e9, 1),
-                   "kv_gbs_unique": round(by["decode_read_unique"] / med(tc) / 1e9, 1)},
+                   "kv_gbs_unique": round(by["decode_read_unique"] / med(tc) / 1e9, 1),
+                   "kind": f"shared-prefix decode, {shared}-token prefix"},
+        "decode_plain": {**tcp, "kv_gbs_logical": round(by["decode_read_logical"] / med(tcp) / 1e9, 1),
+                         "kv_gbs_unique": round(by["decode_read_unique"] / med(tcp) / 1e9, 1),
+                         "num_splits": S},
         "bytes": by,
     }
     log(f"[bench] agentic step {ts['median_ms']:.4f} ms: quantize {tq['median_ms']:.4f}, workspace "
-        f"{td['median_ms']:.4f}, decode {tc['median_ms']:.4f} ms")
+        f"{td['median_ms']:.4f}, decode {tc['median_ms']:.4f} ms (plain decode {tcp['median_ms']:.4f})")
     if parity:
         step()
         torch.cuda.synchronize()

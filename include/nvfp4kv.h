@@ -293,6 +293,53 @@ int nvfp4_paged_decode_append_partial(const nvfp4kv_geom* geom, const void* q, c
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_paged_decode_attn_shared_prefix -- nvfp4_paged_decode_attn for a batch
+ * whose sequences all begin with the same cached prefix on the same physical
+ * pages (prefix caching: a ref-counted shared prefix named by every row of the
+ * block table; section A4, agentic multi-turn serving, where the turns of an
+ * agent share their context). Same result; less work: the prefix's packed K/V
+ * are unpacked once per 16 query columns (the (sequence, query head) pairs of
+ * 16 / G sequences) instead of once per sequence, then each sequence's tokens
+ * past the prefix are split as in the plain decode, all in one launch, and one
+ * log-sum-exp merge combines both kinds of partial.
+ *
+ *   shared_len     tokens [0, shared_len) of every sequence are read through
+ *                  the block-table row of the first sequence of each group of
+ *                  16 / G sequences: block_tables[b][0 .. shared_len / page_size)
+ *                  must be the same for every b (not checked: device data). A
+ *                  multiple of page_size, at most max_pages_per_seq * page_size;
+ *                  0 is the plain decode (with num_splits splits: bit-identical
+ *                  to nvfp4_paged_decode_attn). A sequence shorter than
+ *                  shared_len attends only its own tokens.
+ *   prefix_splits  items per (group of sequences, KV head) over the prefix,
+ *                  1..4096, or 0 for the library's count (items at least as
+ *                  long as the longest possible item past the prefix, at most
+ *                  one per page)
+ *   num_splits     items per (sequence, KV head) over [shared_len, seq_len),
+ *                  1..4096, or 0 for nvfp4_paged_decode_num_splits over the pages
+ *                  past the prefix; prefix_splits + num_splits at most 4096, and
+ *                  ceil(batch / (16 / G)) * prefix_splits + batch * num_splits at
+ *                  most 65535 (NVFP4KV_EUNSUPPORTED)
+ *   workspace      >= nvfp4_paged_decode_shared_prefix_workspace_bytes(...) with
+ *                  the same sizes and split arguments (the partials of
+ *                  prefix_splits + num_splits splits, layout as
+ *                  nvfp4_paged_decode_partial's)
+ * Other arguments, results and errors as nvfp4_paged_decode_attn.
+ */
+int nvfp4_paged_decode_attn_shared_prefix(const nvfp4kv_geom* geom, const void* q,
+                                          const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                                          const int32_t* block_tables, int32_t max_pages_per_seq,
+                                          const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                          float sm_scale, int32_t shared_len, int32_t prefix_splits,
+                                          int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                          void* out, void* stream);
+
+/* Workspace bytes of nvfp4_paged_decode_attn_shared_prefix (0 for invalid arguments). */
+size_t nvfp4_paged_decode_shared_prefix_workspace_bytes(const nvfp4kv_geom* geom, int32_t max_pages_per_seq,
+                                                        int32_t batch, int32_t num_q_heads, int32_t shared_len,
+                                                        int32_t prefix_splits, int32_t num_splits);
+
+/*
  * nvfp4_paged_decode_attn_noalloc -- nvfp4_paged_decode_attn for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc. Same arguments and result without

@@ -56,6 +56,11 @@ _SIGNATURES = {
                                                c_f32, c_i32, c_vp, c_size, c_vp, c_vp]),
     "nvfp4_paged_decode_partial": (ctypes.c_int, [P_GEOM, c_vp, P_NV, P_NV, c_vp, c_i32, c_vp, c_i32, c_i32,
                                                   c_f32, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "nvfp4_paged_decode_attn_shared_prefix": (ctypes.c_int, [P_GEOM, c_vp, P_NV, P_NV, c_vp, c_i32, c_vp, c_i32,
+                                                             c_i32, c_f32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp,
+                                                             c_vp]),
+    "nvfp4_paged_decode_shared_prefix_workspace_bytes": (c_size, [P_GEOM, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                                  c_i32]),
     "nvfp4_paged_decode_attn_noalloc": (ctypes.c_int, [P_GEOM, c_vp, P_NV, P_NV, c_vp, c_i32, c_vp, c_i32, c_i32,
                                                        c_f32, c_i32, c_vp, c_vp]),
     "nvfp4_paged_decode_noalloc_scratch_bytes": (c_size, []),
@@ -485,6 +490,36 @@ def nvfp4_paged_decode_attn(q, k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_table
     """Decode attention of q [B][Hq][d] (bf16) over the NVFP4 pools; returns out [B][Hq][d] bf16."""
     return _decode("nvfp4_paged_decode_attn", None, q, k_pool, v_pool, block_tables, seq_lens, sm_scale,
                    num_splits, workspace, out, stream)
+
+
+def nvfp4_paged_decode_shared_prefix_workspace_bytes(k_pool: NVFP4Pool, max_pages_per_seq, batch, num_q_heads,
+                                                     shared_len, prefix_splits=0, num_splits=0) -> int:
+    g = k_pool.geom
+    return int(lib().nvfp4_paged_decode_shared_prefix_workspace_bytes(ctypes.byref(g), max_pages_per_seq, batch,
+                                                                      num_q_heads, shared_len, prefix_splits,
+                                                                      num_splits))
+
+
+def nvfp4_paged_decode_attn_shared_prefix(q, k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables, seq_lens, sm_scale,
+                                          shared_len, prefix_splits=0, num_splits=0, workspace=None, out=None,
+                                          stream=None):
+    """nvfp4_paged_decode_attn for a batch whose first shared_len tokens sit on the same pages in
+    every block-table row; the prefix is unpacked once per 16 query columns. Returns out [B][Hq][d]."""
+    B, Hq, d = _decode_args(q, block_tables, seq_lens)
+    g = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, out)
+    if workspace is None:
+        n = nvfp4_paged_decode_shared_prefix_workspace_bytes(k_pool, block_tables.shape[1], B, Hq, shared_len,
+                                                             prefix_splits, num_splits)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.bfloat16, "out")
+    _check(lib().nvfp4_paged_decode_attn_shared_prefix(
+        ctypes.byref(g), q.data_ptr(), ctypes.byref(k_pool.desc()), ctypes.byref(v_pool.desc()),
+        block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(), B, Hq, float(sm_scale),
+        int(shared_len), int(prefix_splits), int(num_splits), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), out.data_ptr(), _stream(stream)))
+    return out
 
 
 def nvfp4_paged_decode_attn_noalloc(q, k_pool: NVFP4Pool, v_pool: NVFP4Pool, block_tables, seq_lens, sm_scale,

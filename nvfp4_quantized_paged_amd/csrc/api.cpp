@@ -488,6 +488,117 @@ NVFP4KV_API int nvfp4_kv_dequant_workspace_fp8(const nvfp4kv_geom* geom, const n
                            k_ws, v_ws, stream);
 }
 
+// ---------------------------------------------------------------------------
+// decode with a prefix shared by every sequence of the batch
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct SharedSplits {
+  int32_t spg, groups, prefix, rest;
+};
+
+// Split counts of a shared-prefix decode (0 = the library's choice): the tokens past the prefix take
+// the plain decode's count for the pages past it; the prefix takes items at least as long as the
+// longest of those (measured on MI355X, agentic workload: 2 prefix splits 83.7 us, 3 86.4, 4 88.3,
+// 8 94.0, 1 102.7; the plain decode 95 us), at most one per page; with nothing past the prefix, the
+// plain decode's count for the prefix pages.
+int resolve_shared(const nvfp4kv_geom* g, int32_t max_pages, int32_t batch, int32_t num_q_heads,
+                   int32_t shared_len, int32_t prefix_splits, int32_t num_splits, const char* fn, SharedSplits* out) {
+  const int64_t reach = (int64_t)max_pages * g->page_size;
+  if (shared_len < 0 || shared_len % g->page_size != 0 || shared_len > reach)
+    return fail(NVFP4KV_EINVAL, "%s: shared_len %d must be a multiple of page_size %d within max_pages_per_seq * page_size",
+                fn, shared_len, g->page_size);
+  if (prefix_splits < 0 || prefix_splits > kMaxSplits || num_splits < 0 || num_splits > kMaxSplits)
+    return fail(NVFP4KV_EINVAL, "%s: split counts %d, %d out of range [0, %d] (0 = auto)", fn, prefix_splits,
+                num_splits, kMaxSplits);
+  const int32_t group = num_q_heads / g->num_kv_heads;
+  SharedSplits r{};
+  r.spg = 16 / group;                                   // sequences per 16-column item
+  r.groups = (batch + r.spg - 1) / r.spg;
+  r.rest = num_splits;
+  if (r.rest == 0) {
+    const int32_t rest_pages = max_pages - shared_len / g->page_size;
+    r.rest = nvfp4_paged_decode_num_splits(batch, g->num_kv_heads, rest_pages > 0 ? rest_pages : 1, g->page_size);
+  }
+  r.prefix = 0;
+  if (shared_len > 0) {
+    r.prefix = prefix_splits;
+    if (r.prefix == 0) {
+      const int64_t rest_span = (reach - shared_len + r.rest - 1) / r.rest;
+      const int64_t pages = shared_len / g->page_size;
+      const int64_t n = rest_span > 0 ? shared_len / rest_span
+                                      : nvfp4_paged_decode_num_splits(r.groups, g->num_kv_heads, (int32_t)pages,
+                                                                      g->page_size);
+      r.prefix = (int32_t)(n < 1 ? 1 : (n > pages ? pages : n));
+    }
+  }
+  if (r.prefix + r.rest > kMaxSplits)
+    return fail(NVFP4KV_EINVAL, "%s: %d prefix + %d further splits exceed %d", fn, r.prefix, r.rest, kMaxSplits);
+  if ((int64_t)r.groups * r.prefix + (int64_t)batch * r.rest > kGridYZ)
+    return fail(NVFP4KV_EUNSUPPORTED, "%s: %d prefix items and %d items past the prefix per KV head exceed %d", fn,
+                r.groups * r.prefix, batch * r.rest, kGridYZ);
+  *out = r;
+  return NVFP4KV_OK;
+}
+
+}  // namespace
+
+NVFP4KV_API size_t nvfp4_paged_decode_shared_prefix_workspace_bytes(const nvfp4kv_geom* geom, int32_t max_pages_per_seq,
+                                                                    int32_t batch, int32_t num_q_heads,
+                                                                    int32_t shared_len, int32_t prefix_splits,
+                                                                    int32_t num_splits) {
+  const char* fn = "nvfp4_paged_decode_shared_prefix_workspace_bytes";
+  SharedSplits ss{};
+  if (check_geom(geom, fn) || batch < 0 || max_pages_per_seq <= 0 || num_q_heads <= 0 ||
+      num_q_heads % geom->num_kv_heads != 0 || num_q_heads / geom->num_kv_heads > kMaxGroup ||
+      resolve_shared(geom, max_pages_per_seq, batch, num_q_heads, shared_len, prefix_splits, num_splits, fn, &ss))
+    return 0;
+  return nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, geom->head_dim, ss.prefix + ss.rest);
+}
+
+NVFP4KV_API int nvfp4_paged_decode_attn_shared_prefix(const nvfp4kv_geom* geom, const void* q,
+                                                      const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
+                                                      const int32_t* block_tables, int32_t max_pages_per_seq,
+                                                      const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                                                      float sm_scale, int32_t shared_len, int32_t prefix_splits,
+                                                      int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                                      void* out, void* stream) {
+  const char* fn = "nvfp4_paged_decode_attn_shared_prefix";
+  int rc;
+  DecodeCheck c{};
+  SharedSplits ss{};
+  if ((rc = check_geom(geom, fn)) || (rc = check_nvfp4_cache(k_cache, "K", fn)) ||
+      (rc = check_nvfp4_cache(v_cache, "V", fn)) ||
+      (rc = check_decode_args(geom, q, block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, sm_scale, 1,
+                              false, fn, &c)) ||
+      (rc = resolve_shared(geom, max_pages_per_seq, batch, num_q_heads, shared_len, prefix_splits, num_splits, fn,
+                           &ss)))
+    return rc;
+  const int32_t total = ss.prefix + ss.rest;
+  const size_t need = nvfp4_paged_decode_workspace_bytes(batch, num_q_heads, geom->head_dim, total);
+  if (need > 0 && !workspace) return fail(NVFP4KV_EINVAL, "%s: workspace is NULL", fn);
+  if (workspace && !aligned16(workspace)) return fail(NVFP4KV_EALIGN, "%s: workspace must be 16-byte aligned", fn);
+  if (workspace_bytes < need)
+    return fail(NVFP4KV_EWORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if (!out) return fail(NVFP4KV_EINVAL, "%s: out is NULL", fn);
+  if (!aligned16(out)) return fail(NVFP4KV_EALIGN, "%s: out must be 16-byte aligned", fn);
+  if (batch == 0) return launched(hipSuccess, fn);
+  c.splits = total;
+  DecodeParams p = make_decode(geom, q, k_cache->data, k_cache->scale, v_cache->data, v_cache->scale, block_tables,
+                               max_pages_per_seq, seq_lens, batch, num_q_heads, c, sm_scale, k_cache->global_scale,
+                               workspace);
+  p.cas_shared = shared_len;
+  p.cas_splits_p = ss.prefix;
+  p.cas_groups = ss.groups;
+  p.cas_spg = ss.spg;
+  p.cas_splits_r = ss.rest;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_partial(p, geom->head_dim, false, NVFP4KV_VARIANT_MFMA, s);
+  if (e == hipSuccess) e = run_merge(p, geom->head_dim, v_cache->global_scale, out, s);
+  return launched(e, fn);
+}
+
 NVFP4KV_API int nvfp4_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,
                                            const nvfp4kv_cache* k_cache, const nvfp4kv_cache* v_cache,
                                            const int32_t* block_tables, int32_t max_pages_per_seq,

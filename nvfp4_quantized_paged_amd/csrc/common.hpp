@@ -171,6 +171,12 @@ struct DecodeParams {
   float qk_scale;           // sm_scale * K global scale * log2(e)
   uint32_t page_mul;        // token index t (0 <= t < 2^31) to page: t / page_size == umulhi(t, page_mul) >> page_sh
   int32_t page_sh;
+  // Shared-prefix decode: tokens [0, cas_shared) sit on the same pages in every block-table row.
+  // Grid (Hkv, cas_groups * cas_splits_p + batch * cas_splits_r): first the prefix items, one per
+  // (group of cas_spg sequences, prefix split), whose query columns are the group's (sequence, query
+  // head) pairs; then cas_splits_r items per sequence over [cas_shared, seq_len). A (sequence,
+  // query head) has num_splits = cas_splits_p + cas_splits_r partial slots, prefix slots first.
+  int32_t cas_shared, cas_splits_p, cas_groups, cas_spg, cas_splits_r;
   // Fused append (k_new non-null): each sequence's new token, at position seq_len - 1, is encoded
   // into its pool slot by the wave whose split holds it, which then reads it back with its chunk.
   const uint16_t* k_new;    // [B] rows of Hkv * D bf16, new_stride elements apart

@@ -292,10 +292,12 @@ struct Acc {
 };
 
 // One chunk: QK, online softmax, PV. `cs` > 0 maps raw scores to base-2 logits.
-template <int D, bool FP8, int T, bool LUT>
+// CAS (shared-prefix items): the lane's column attends tokens below lim only (its own sequence's
+// length); lim_min, the smallest over the wave's columns, is wave-uniform.
+template <int D, bool FP8, int T, bool LUT, bool CAS = false>
 __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D, FP8> (&cur)[Cfg<D, FP8, T>::kTiles],
                                      const half8_t (&qb)[Cfg<D, FP8, T>::kKSteps], _Float16* vl, float cs,
-                                     Acc<D>& a) {
+                                     Acc<D>& a, int lim = 0, int lim_min = 0) {
   using C = Cfg<D, FP8, T>;
   const int grp = lane >> 4;
 
@@ -332,6 +334,17 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
     }
   }
 
+  // ---- columns whose sequence ends inside this chunk (shared-prefix items)
+  if constexpr (CAS) {
+    if (ts + C::kChunk > lim_min) {
+#pragma unroll
+      for (int t = 0; t < C::kTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (ts + 16 * t + 4 * grp + i >= lim) sc[t][i] = -INFINITY;
+    }
+  }
+
   // ---- online softmax (base 2) per head
   float cmax = -INFINITY;
 #pragma unroll
@@ -340,12 +353,14 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
     for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[t][i]);
   cmax = max_over_rows(cmax);
   const float mnew = fmaxf(a.m, cmax * cs);
-  const float alpha = __builtin_amdgcn_exp2f(a.m - mnew);
+  // a masked column may have seen no token yet (m = -inf): its numerators and rescale are then 0
+  const float mref = (CAS && mnew == -INFINITY) ? 0.0f : mnew;
+  const float alpha = __builtin_amdgcn_exp2f(a.m - mref);
   a.m = mnew;
 #pragma unroll
   for (int t = 0; t < C::kTiles; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[t][i] = __builtin_amdgcn_exp2f(fmaf(sc[t][i], cs, -mnew));
+    for (int i = 0; i < 4; ++i) sc[t][i] = __builtin_amdgcn_exp2f(fmaf(sc[t][i], cs, -mref));
   if (__ballot(alpha != 1.0f)) {
 #pragma unroll
     for (int c = 0; c < C::kCTiles; ++c) a.o[c] *= alpha;
@@ -449,22 +464,66 @@ __device__ inline void append_token(const DecodeParams& p, const Item& it, int b
   }
 }
 
-template <int D, bool FP8, int T, int W, bool PW, bool LUT, bool APPEND>
+template <int D, bool FP8, int T, int W, bool PW, bool LUT, bool APPEND, bool CAS = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(W)))
 void decode_partial_mfma_kernel(DecodeParams p) {
   using C = Cfg<D, FP8, T>;
-  const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;   // KV heads of one split run side by side
+  const int g = blockIdx.x;         // KV heads of one split run side by side
   const int lane = threadIdx.x;
   const int col = lane & 15;        // head (QK/PV columns) or channel (transpose columns)
   const int grp = lane >> 4;        // lane group
   const int G = p.group;
   const int S = p.num_splits;
   const int P = p.page_size;
-  // wave-uniform (keeps offsets scalar); tokens past the table's reach are not read
-  const int Lraw = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
-  const int L = min(Lraw, p.max_pages * P);
-  const int per = ceil_div(ceil_div(L, S), P) * P;
-  const int t0 = j * per;
+  const int reach = p.max_pages * P;
+  // the item: sequence b (block-table row), split j, partial slot, token range [t0, t1), query
+  // columns ncol; all wave-uniform (keeps offsets scalar); tokens past the table's reach are not read
+  int b, j, slot, ncol = G, Lraw, L, per, t0, t1;
+  int lim = 0, lim_min = 0;         // shared-prefix items: the lane's column's length, the wave's least
+  if constexpr (CAS) {
+    const int np = p.cas_groups * p.cas_splits_p;
+    const int y = blockIdx.y;
+    if (y < np) {                   // prefix item: a group of sequences, tokens of the shared prefix
+      const int gi = y / p.cas_splits_p;
+      j = y - gi * p.cas_splits_p;
+      b = gi * p.cas_spg;           // the group's first sequence: its row holds the prefix pages
+      ncol = min(p.cas_spg, p.batch - b) * G;
+      slot = j;
+      per = ceil_div(ceil_div(p.cas_shared, p.cas_splits_p), P) * P;
+      t0 = j * per;
+      lim = min(p.seq_lens[b + min(col, ncol - 1) / G], reach);
+      int lmax = lim;
+      lim_min = lim;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        lmax = max(lmax, __shfl_xor(lmax, o, 64));
+        lim_min = min(lim_min, __shfl_xor(lim_min, o, 64));
+      }
+      lim_min = __builtin_amdgcn_readfirstlane(lim_min);
+      Lraw = L = __builtin_amdgcn_readfirstlane(lmax);       // tokens past every column's end are not read
+      t1 = min(min(p.cas_shared, t0 + per), L);
+    } else {                        // the tokens of one sequence past the prefix
+      const int yr = y - np;
+      b = yr / p.cas_splits_r;
+      j = yr - b * p.cas_splits_r;
+      slot = p.cas_splits_p + j;
+      Lraw = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+      L = min(Lraw, reach);
+      per = ceil_div(ceil_div(max(L - p.cas_shared, 0), p.cas_splits_r), P) * P;
+      t0 = p.cas_shared + j * per;
+      t1 = min(L, t0 + per);
+      lim = lim_min = L;
+    }
+  } else {
+    j = blockIdx.y;
+    b = blockIdx.z;
+    slot = j;
+    Lraw = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+    L = min(Lraw, reach);
+    per = ceil_div(ceil_div(L, S), P) * P;
+    t0 = j * per;
+    t1 = min(L, t0 + per);
+  }
   // the new token (fused append) sits at position L - 1 of a sequence within the table's reach,
   // in a valid page (the quantize kernels skip a slot outside the pool, and so does the append)
   int tn = -1;
@@ -475,8 +534,13 @@ void decode_partial_mfma_kernel(DecodeParams p) {
       if (pg >= 0 && pg < p.num_pages) tn = L - 1;
     }
   }
-  const Item it{p.block_tables + (int64_t)b * p.max_pages, g, min(L, t0 + per), tn};
+  const Item it{p.block_tables + (int64_t)b * p.max_pages, g, t1, tn};
   const int64_t qh0 = (int64_t)b * p.num_q_heads + (int64_t)g * G;
+  // query row of column c: head c of sequence b, or (shared-prefix items) head c mod G of sequence b + c / G
+  auto qrow = [&](int c) -> int64_t {
+    if constexpr (CAS) return (int64_t)(b + c / G) * p.num_q_heads + (int64_t)g * G + c % G;
+    else return qh0 + c;
+  };
 
   // LDS: the unpacked V rows of a chunk in the loop, the partial results at the end
   constexpr int kVlHalfs = 32 * VPitch<D>::kHalfs;
@@ -510,13 +574,14 @@ void decode_partial_mfma_kernel(DecodeParams p) {
     load_chunk<D, FP8, T, PW>(p, it, t0 + 2 * C::kChunk, lane, b2);
 
     // ---- q as the B operand: lane (head col, group grp), step kk: channels grp*D/4 + 8kk .. +7
-    const bool hv = col < G;
+    const bool hv = col < ncol;
+    const int64_t qr = qrow(col);
     float qf[C::kKSteps][8];
     float qmax = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < C::kKSteps; ++kk) {
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (hv) w = *reinterpret_cast<const uint4*>(p.q + (qh0 + col) * D + grp * C::kChanPerGroup + 8 * kk);
+      if (hv) w = *reinterpret_cast<const uint4*>(p.q + qr * D + grp * C::kChanPerGroup + 8 * kk);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -547,16 +612,16 @@ void decode_partial_mfma_kernel(DecodeParams p) {
     // compiler's wait before each chunk leaves the other two chunks in flight.
     int ts = t0;
     for (; ts + 2 * C::kChunk < it.t1; ts += 3 * C::kChunk) {
-      process_chunk<D, FP8, T, LUT>(it, ts, lane, b0, qb, vl, cs, a);
+      process_chunk<D, FP8, T, LUT, CAS>(it, ts, lane, b0, qb, vl, cs, a, lim, lim_min);
       load_chunk<D, FP8, T, PW>(p, it, ts + 3 * C::kChunk, lane, b0);
-      process_chunk<D, FP8, T, LUT>(it, ts + C::kChunk, lane, b1, qb, vl, cs, a);
+      process_chunk<D, FP8, T, LUT, CAS>(it, ts + C::kChunk, lane, b1, qb, vl, cs, a, lim, lim_min);
       load_chunk<D, FP8, T, PW>(p, it, ts + 4 * C::kChunk, lane, b1);
-      process_chunk<D, FP8, T, LUT>(it, ts + 2 * C::kChunk, lane, b2, qb, vl, cs, a);
+      process_chunk<D, FP8, T, LUT, CAS>(it, ts + 2 * C::kChunk, lane, b2, qb, vl, cs, a, lim, lim_min);
       load_chunk<D, FP8, T, PW>(p, it, ts + 5 * C::kChunk, lane, b2);
     }
     // at most two chunks remain, already loaded
-    if (ts < it.t1) process_chunk<D, FP8, T, LUT>(it, ts, lane, b0, qb, vl, cs, a);
-    if (ts + C::kChunk < it.t1) process_chunk<D, FP8, T, LUT>(it, ts + C::kChunk, lane, b1, qb, vl, cs, a);
+    if (ts < it.t1) process_chunk<D, FP8, T, LUT, CAS>(it, ts, lane, b0, qb, vl, cs, a, lim, lim_min);
+    if (ts + C::kChunk < it.t1) process_chunk<D, FP8, T, LUT, CAS>(it, ts + C::kChunk, lane, b1, qb, vl, cs, a, lim, lim_min);
   }
 
   // ---- partial results: o / l in f16 (a weighted mean of dequantized V values, so within
@@ -568,23 +633,23 @@ void decode_partial_mfma_kernel(DecodeParams p) {
   float4_t* stage = reinterpret_cast<float4_t*>(vl);
   float* stage_il = reinterpret_cast<float*>(vl) + 16 * D;         // past the G <= 16 staged rows
   const float lt = a.ls[0];
-  if (col < G) {
+  if (col < ncol) {
 #pragma unroll
     for (int ct = 0; ct < C::kCTiles; ++ct) stage[(col * D + 16 * ct + 4 * grp) / 4] = a.o[ct];
     if (grp == 0) stage_il[col] = lt > 0.0f ? 1.0f / lt : 0.0f;
   }
   __syncthreads();
-  for (int e = lane; e < G * D / 4; e += 64) {
+  for (int e = lane; e < ncol * D / 4; e += 64) {
     const int row = e / (D / 4), c4 = e % (D / 4);
-    const int64_t idx = (qh0 + row) * S + j;
+    const int64_t idx = qrow(row) * S + slot;
     const float il = stage_il[row];
     const float4_t x = stage[e];
     const half4_t h = {(_Float16)(x[0] * il), (_Float16)(x[1] * il), (_Float16)(x[2] * il),
                        (_Float16)(x[3] * il)};
     __builtin_nontemporal_store(h, reinterpret_cast<half4_t*>(p.part_o + idx * D + 4 * c4));
   }
-  if (col < G) {
-    const int64_t idx = (qh0 + col) * S + j;
+  if (col < ncol) {
+    const int64_t idx = qrow(col) * S + slot;
     if (grp == 0) {
       p.part_ml[idx * 2] = a.m;
       p.part_ml[idx * 2 + 1] = lt;
@@ -598,6 +663,16 @@ hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
   // buffer offsets and bounds are 32-bit: whole-pool descriptors only below 2 GiB per array
   const int64_t pool_bytes = (int64_t)p.num_pages * p.num_kv_heads * p.page_size * Cfg<D, FP8, T>::kRowBytes;
   const bool pw = pool_bytes <= INT32_MAX;
+  if (p.cas_splits_r > 0) {                  // shared-prefix decode (NVFP4 only)
+    if constexpr (!FP8 && !LUT) {
+      const dim3 cg(p.num_kv_heads, p.cas_groups * p.cas_splits_p + p.batch * p.cas_splits_r, 1);
+      if (pw) hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, true, LUT, false, true>), cg, dim3(64), 0, s, p);
+      else hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, false, LUT, false, true>), cg, dim3(64), 0, s, p);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (p.k_new) {
     if (pw) hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, true, LUT, true>), grid, dim3(64), 0, s, p);
     else hipLaunchKernelGGL((decode_partial_mfma_kernel<D, FP8, T, W, false, LUT, true>), grid, dim3(64), 0, s, p);

@@ -134,6 +134,40 @@ def test_decode_rejects_bad_arguments(L):
     assert _decode(L, g, B=0, ws=None, ws_bytes=0) == L.OK
 
 
+def _shared(L, g, B=1, Hq=4, maxp=16, shared=16, sp=0, sr=0, ws_bytes=1 << 20, out=FAKE, ws=FAKE):
+    kc, vc = _nv(L), _nv(L)
+    return L.lib().nvfp4_paged_decode_attn_shared_prefix(ctypes.byref(g), FAKE, ctypes.byref(kc), ctypes.byref(vc),
+                                                          FAKE, maxp, FAKE, B, Hq, 0.125, shared, sp, sr, ws,
+                                                          ws_bytes, out, None)
+
+
+def test_shared_prefix_decode_checks_its_arguments(L):
+    """The shared-prefix decode validates the prefix length (whole pages within
+    the table's reach), the split counts and the grid on the host, and sizes
+    its workspace as the partials of prefix + further splits."""
+    g = _geom(L, P=16, H=2, d=128)
+    f = L.lib().nvfp4_paged_decode_shared_prefix_workspace_bytes
+    assert f(ctypes.byref(g), 16, 13, 8, 96, 2, 3) == 13 * 8 * 5 * (128 * 2 + 8)
+    # automatic counts: the plain decode's count past the prefix; prefix items at least as long
+    rest = L.nvfp4_paged_decode_num_splits(13, 2, 16 - 96 // 16, 16)
+    span = -(-(16 * 16 - 96) // rest)
+    pref = min(max(96 // span, 1), 96 // 16)
+    assert f(ctypes.byref(g), 16, 13, 8, 96, 0, 0) == 13 * 8 * (pref + rest) * (128 * 2 + 8)
+    assert f(ctypes.byref(g), 16, 13, 8, 0, 0, 3) == 13 * 8 * 3 * (128 * 2 + 8)   # no prefix items
+    for bad in (8, -16, 16 * 16 + 16):                                      # not whole pages, negative, past the reach
+        assert f(ctypes.byref(g), 16, 13, 8, bad, 0, 0) == 0
+        assert _shared(L, g, shared=bad) == L.EINVAL
+    assert "shared_len" in L.last_error()
+    assert f(ctypes.byref(g), 16, 13, 8, 96, 5000, 0) == 0
+    assert _shared(L, g, sp=5000) == L.EINVAL
+    assert _shared(L, g, sp=4000, sr=200) == L.EINVAL                    # more than 4096 slots in all
+    assert _shared(L, g, B=40000, sp=1, sr=2) == L.EUNSUPPORTED            # grid past 65535 items per KV head
+    assert _shared(L, g, ws_bytes=16) == L.EWORKSPACE
+    assert _shared(L, g, out=None) == L.EINVAL
+    assert _shared(L, g, Hq=2 * 17) == L.EUNSUPPORTED                      # query group above 16
+    assert _shared(L, g, B=0, ws=None, ws_bytes=0) == L.OK                 # nothing to do, nothing launched
+
+
 def _noalloc(L, g, B=1, Hq=4, S=1, q=FAKE, out=FAKE, maxp=16):
     kc, vc = _nv(L), _nv(L)
     return L.lib().nvfp4_paged_decode_attn_noalloc(ctypes.byref(g), q, ctypes.byref(kc), ctypes.byref(vc), FAKE,

@@ -1146,6 +1146,75 @@ def test_fp8_decode_moderate(nk):
         check_out(out, ref, mass, f"fp8 variant={var}")
 
 
+def _shared_prefix_problem(nk, seed, B, H, G, d, P, shared, lens):
+    """A batch whose first `shared` tokens sit on the same physical pages in
+    every block-table row (a sequence shorter than the prefix reads its own
+    first tokens from those pages), private pages after it, quantized on both
+    sides. Returns device inputs, the pools and the oracle's output."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n_sh = shared // P
+    priv = [max(0, -(-(L - shared) // P)) for L in lens]
+    max_pages = max(1, n_sh + max(priv))
+    num_pages = n_sh + sum(priv) + 2
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.zeros((B, max_pages), dtype=np.int32)
+    pos = n_sh
+    for b in range(B):
+        bt[b, :n_sh] = perm[:n_sh]
+        bt[b, n_sh:n_sh + priv[b]] = perm[pos:pos + priv[b]]
+        bt[b, n_sh + priv[b]:] = perm[-1]                  # unused entries name a real page
+        pos += priv[b]
+    slots = [bt[0, t // P].astype(np.int64) * P + t % P for t in [np.arange(shared)]]
+    for b, L in enumerate(lens):
+        t = np.arange(shared, max(L, shared))
+        slots.append(bt[b, t // P].astype(np.int64) * P + t % P)
+    slots = np.concatenate(slots)
+    k = synth.host_values(rng, (len(slots), H, d))
+    v = synth.host_values(rng, (len(slots), H, d))
+    q = synth.host_values(rng, (B, H * G, d))
+    kp, vp = gpu_quantize_nv(nk, num_pages, H, P, d, k, v, slots)
+    kd, ks, vd, vs = oracle_nv(num_pages, H, P, d, k, v, slots)
+    sl = np.array(lens, dtype=np.int32)
+    ref, mass = oatt.paged_decode(q, onv.dequant_cache(kd, ks), onv.dequant_cache(vd, vs), bt, sl, 0.125)
+    return (synth.to_device_bf16(q), synth.to_device(bt), synth.to_device(sl)), (kp, vp), (ref, mass)
+
+
+@pytest.mark.parametrize("G,d,P,shared,lens,sp,sr", [
+    (4, 128, 16, 96, [0, 5, 96, 97, 300, 160, 95, 241, 96, 1, 400, 130, 17], 0, 0),   # partial last group
+    (5, 128, 16, 64, [64, 200, 33, 150, 64, 90, 300], 3, 2),                            # 3 sequences = 15 columns
+    (1, 64, 48, 144, [144 + 7 * i for i in range(20)] + [0, 3], 2, 3),                  # 16 sequences per item
+    (16, 64, 16, 32, [40, 10, 100], 1, 1),                                              # one sequence per item
+    (8, 128, 32, 128, [128, 64, 100, 128, 1], 4, 2),                                    # nothing past the prefix
+    (4, 128, 16, 2048, [2048 + 37 * i for i in range(9)] + [1000], 0, 0),              # prefix over many chunks
+])
+def test_shared_prefix_decode_against_oracle(nk, G, d, P, shared, lens, sp, sr):
+    """The shared-prefix decode (prefix items over 16 / G sequences' query
+    columns, per-column length masks, the rest split per sequence, one merge)
+    against the oracle, and beside the plain decode of the same pools."""
+    B, H = len(lens), 2
+    say(f"case shared prefix G{G} d{d} P{P} shared {shared} B {B} splits {sp}/{sr}")
+    (q, bt, sl), (kp, vp), (ref, mass) = _shared_prefix_problem(nk, 1300 + G + d + P + shared, B, H, G, d, P, shared,
+                                                                  lens)
+    out = nk.nvfp4_paged_decode_attn_shared_prefix(q, kp, vp, bt, sl, 0.125, shared, prefix_splits=sp, num_splits=sr)
+    plain = nk.nvfp4_paged_decode_attn(q, kp, vp, bt, sl, 0.125)
+    torch.cuda.synchronize()
+    check_out(out, ref, mass, "shared prefix")
+    check_out(plain, ref, mass, "plain decode")
+    assert torch.all(out[torch.tensor(lens, device=out.device) == 0].float() == 0)
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_shared_prefix_of_length_zero_is_the_plain_decode(nk, S):
+    """With no shared prefix the items are the plain decode's splits: the
+    output is bit-identical to nvfp4_paged_decode_attn at the same count."""
+    lens = [0, 17, 300, 64, 129, 1000]
+    (q, bt, sl), (kp, vp), _ = _shared_prefix_problem(nk, 1400 + S, len(lens), 2, 4, 128, 16, 0, lens)
+    out = nk.nvfp4_paged_decode_attn_shared_prefix(q, kp, vp, bt, sl, 0.125, 0, num_splits=S)
+    plain = nk.nvfp4_paged_decode_attn(q, kp, vp, bt, sl, 0.125, num_splits=S)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)
+
+
 def _append_case(nk, fmt, d, G, P, gs, S, seed, special=False, partial=False):
     """Pools holding each sequence's earlier tokens, a block table over a page
     permutation, the step's new token per sequence, and lengths that cover an
@@ -1561,7 +1630,7 @@ def test_full_size_agentic_sampled(nk):
     """64 sequences, L_b ~ U[3200, 10000], a 2,800-token prefix on 175 shared
     pages, 500-token chunks: the whole step at full size, then sampled
     sequences checked against the oracle (cache bytes, workspace rows,
-    decode output)."""
+    decode output of both the plain and the shared-prefix decode)."""
     from synth.workload import build_agentic_workload
     wl = synth.WORKLOADS[5]
     say(f"case full size agentic: B {wl.batch} prefix {wl.shared_prefix} chunk {wl.chunk}")
@@ -1572,6 +1641,7 @@ def test_full_size_agentic_sampled(nk):
     nk.nvfp4_kv_quantize(w.k_chunk, w.v_chunk, w.slot_chunk, w.kp, w.vp)
     nk.nvfp4_kv_dequant_workspace(w.kp, w.vp, w.bt, w.cached_lens, w.ws_row_offsets, w.k_ws, w.v_ws)
     out = nk.nvfp4_paged_decode_attn(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale)
+    outc = nk.nvfp4_paged_decode_attn_shared_prefix(w.q, w.kp, w.vp, w.bt, w.seq_lens, wl.sm_scale, wl.shared_prefix)
     torch.cuda.synchronize()
     after = (w.kp.data[shared], w.kp.scale[shared], w.vp.data[shared], w.vp.scale[shared])
     assert all(torch.equal(x, y) for x, y in zip(before, after)), "shared prefix pages were written"
@@ -1601,5 +1671,6 @@ def test_full_size_agentic_sampled(nk):
         qb = onv.bf16_to_f64(synth.bf16_tensor_bits(w.q[b]))
         ref, mass = oatt.decode_heads(qb, khat, vhat, wl.sm_scale)
         check_out(out[b], ref, mass, f"agentic b{b}")
+        check_out(outc[b], ref, mass, f"agentic shared-prefix decode b{b}")
     del w
     torch.cuda.empty_cache()
