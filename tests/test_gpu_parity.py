@@ -1371,7 +1371,9 @@ def test_decode_pool_above_2gib(nk, fmt):
     """Pools of more than 2 GiB per array (buffer offsets are 32-bit, so the
     decode kernel switches to per-page addressing): the same pages placed at
     the far end of a large pool give bit-identical outputs to a small pool,
-    and both match the oracle."""
+    and both match the oracle; on both pools the shared-prefix form (no
+    prefix) and the decode step that appends each sequence's last token again
+    give the plain decode's bits."""
     wl = synth.Workload(94, "bigpool", 3, 16, 2, 128, 64, 700, True, 3)
     inp = synth.host_uniform_decode(wl)
     H, P, d = wl.num_kv_heads, wl.page_size, wl.head_dim
@@ -1391,11 +1393,24 @@ def test_decode_pool_above_2gib(nk, fmt):
             kp, vp = nk.NVFP4Pool.empty(pages, H, P, d), nk.NVFP4Pool.empty(pages, H, P, d)
             nk.nvfp4_kv_quantize(kt, vt, synth.to_device(slots), kp, vp)
             out = nk.nvfp4_paged_decode_attn(q, kp, vp, synth.to_device(bt), sl, wl.sm_scale, num_splits=3)
+            # the shared-prefix instantiation with no prefix: the same splits, the same bits
+            outc = nk.nvfp4_paged_decode_attn_shared_prefix(q, kp, vp, synth.to_device(bt), sl, wl.sm_scale, 0,
+                                                            num_splits=3)
+            app = nk.nvfp4_paged_decode_append_attn
         else:
             kp, vp = nk.FP8Pool.empty(pages, H, P, d), nk.FP8Pool.empty(pages, H, P, d)
             nk.fp8_kv_quantize(kt, vt, synth.to_device(slots), kp, vp)
             out = nk.fp8_paged_decode_attn(q, kp, vp, synth.to_device(bt), sl, wl.sm_scale, num_splits=3)
+            outc = out
+            app = nk.fp8_paged_decode_append_attn
+        # the decode step with each sequence's last token appended again (same values, same bytes):
+        # the append's stores and read-back through this pool's addressing leave the result unchanged
+        L = int(inp.seq_lens[0])
+        last = torch.arange(len(inp.seq_lens), device="cuda") * L + (L - 1)
+        outa = app(q, kt[last].contiguous(), vt[last].contiguous(), kp, vp, synth.to_device(bt), sl, wl.sm_scale,
+                   num_splits=3)
         torch.cuda.synchronize()
+        assert torch.equal(outc, out) and torch.equal(outa, out), "shared-prefix or append form differs"
         outs.append(out)
         del kp, vp
     torch.cuda.empty_cache()
