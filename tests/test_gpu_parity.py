@@ -1333,7 +1333,7 @@ def test_decode_append_matches_quantize_then_decode(nk, fmt, d, G, P, gs, S):
 @pytest.mark.parametrize("fmt,d,G,P,gs,S", [("nvfp4", 128, 5, 64, 1.0, 4), ("nvfp4", 64, 4, 48, 0.3, 2),
                                              ("fp8", 128, 8, 16, 0.5, 3), ("fp8", 64, 2, 32, 1.0, 1)])
 def test_decode_append_partial_then_merge(nk, fmt, d, G, P, gs, S):
-    """The append step without the merge: pool bytes and fp32 partials equal,
+    """The append step without the merge: pool bytes and partials equal,
     bit for bit, quantize-on-write followed by the MFMA partial kernel, and the
     merge of those partials gives the full append step's output."""
     say(f"case append partial {fmt} d{d} G{G} P{P} gs {gs} splits {S}")
