@@ -39,28 +39,31 @@ __device__ inline void slot_position(const QuantizeParams& p, int64_t slot, int6
 constexpr int kTokPerWave = 16;
 constexpr int kWavesPerGroup = 4;
 
-// Source block of 16 elements as floats: bf16 (two 128-bit loads) or
-// FP8-E4M3 bytes times the source scale (one 128-bit load). With ws_rows the
-// source bytes also go, unchanged, to the token's workspace row (the current
-// chunk of the extend path next to the dequantized prefix).
+// Source block of 16 elements: its raw bytes (bf16: two 128-bit loads; FP8-E4M3: one), as
+// floats (FP8 times the source scale), and, with ws_rows, the source bytes copied unchanged to
+// the token's workspace row (the current chunk of the extend path next to the dequantized
+// prefix).
 template <int D, bool FP8SRC>
-__device__ inline void load_source_block(const QuantizeParams& p, int which, int64_t t, int h, int blk, float x[16]) {
-  constexpr int kEsize = FP8SRC ? 1 : 2;
+struct SourceBlock {
+  static constexpr int kEsize = FP8SRC ? 1 : 2;
+  uint4 raw[kEsize];
+};
+
+template <int D, bool FP8SRC>
+__device__ inline void load_source_block(const QuantizeParams& p, int which, int64_t t, int h, int blk,
+                                         SourceBlock<D, FP8SRC>& sb) {
+  constexpr int kEsize = SourceBlock<D, FP8SRC>::kEsize;
   const int64_t elem = t * p.src_stride + (int64_t)h * D + blk * kBlock;
   const uint8_t* src = static_cast<const uint8_t*>(p.src[which]) + elem * kEsize;
-  uint4 raw[kEsize];
 #pragma unroll
-  for (int i = 0; i < kEsize; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
-  if (p.ws_rows) {
-    const int64_t r = p.ws_rows[t];
-    if (r >= 0) {
-      uint4* dst = reinterpret_cast<uint4*>(p.ws[which] + ((r * p.num_kv_heads + h) * D + blk * kBlock) * kEsize);
-#pragma unroll
-      for (int i = 0; i < kEsize; ++i) dst[i] = raw[i];
-    }
-  }
+  for (int i = 0; i < kEsize; ++i) sb.raw[i] = reinterpret_cast<const uint4*>(src)[i];
+}
+
+template <int D, bool FP8SRC>
+__device__ inline void source_to_f32(const QuantizeParams& p, int which, const SourceBlock<D, FP8SRC>& sb,
+                                     float x[16]) {
   if constexpr (FP8SRC) {
-    const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+    const uint32_t w[4] = {sb.raw[0].x, sb.raw[0].y, sb.raw[0].z, sb.raw[0].w};
     const float ss = p.src_scale[which];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -69,37 +72,71 @@ __device__ inline void load_source_block(const QuantizeParams& p, int which, int
       for (int e = 0; e < 4; ++e) x[4 * i + e] *= ss;
     }
   } else {
-    bf16x16_to_f32(raw[0], raw[kEsize - 1], x);
+    bf16x16_to_f32(sb.raw[0], sb.raw[SourceBlock<D, FP8SRC>::kEsize - 1], x);
   }
 }
 
+template <int D, bool FP8SRC>
+__device__ inline void copy_to_workspace(const QuantizeParams& p, int which, int64_t r, int h, int blk,
+                                         const SourceBlock<D, FP8SRC>& sb) {
+  constexpr int kEsize = SourceBlock<D, FP8SRC>::kEsize;
+  if (r >= 0) {
+    uint4* dst = reinterpret_cast<uint4*>(p.ws[which] + ((r * p.num_kv_heads + h) * D + blk * kBlock) * kEsize);
+#pragma unroll
+    for (int i = 0; i < kEsize; ++i) dst[i] = sb.raw[i];
+  }
+}
+
+// Every load of a wave (its passes' source blocks, slots and workspace rows, at token indices
+// clamped into the batch) is issued before its first encode, and every pass is encoded before its
+// first store: the compiler cannot move a later pass's loads above an earlier pass's stores by
+// itself (the pool might alias the source). Measured on MI355X, agentic 500-token chunks: bf16
+// source 39.6 -> 36.4 us, FP8 source with the chunk copy 35.9 -> 33.4 us, bytes identical.
 template <int D, bool FP8SRC, bool QUOT>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void nvfp4_quantize_kernel(QuantizeParams p) {
   constexpr int nb = D / kBlock;                 // blocks per head row
   constexpr int kTokPerPass = 64 / nb;
+  constexpr int kPasses = kTokPerWave / kTokPerPass;
   const int which = blockIdx.z, h = blockIdx.y;   // 0 = K, 1 = V
   const int lane = threadIdx.x & 63, blk = lane % nb;
   const int64_t tw = ((int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6)) * kTokPerWave;
+  SourceBlock<D, FP8SRC> sb[kPasses];
+  int64_t slot[kPasses], wsr[kPasses];
+  const bool copy = p.ws_rows != nullptr;
 #pragma unroll
-  for (int k = 0; k < kTokPerWave / kTokPerPass; ++k) {
+  for (int k = 0; k < kPasses; ++k) {
+    const int64_t t = min(tw + k * kTokPerPass + lane / nb, (int64_t)p.num_tokens - 1);
+    load_source_block<D, FP8SRC>(p, which, t, h, blk, sb[k]);
+    slot[k] = p.slot_mapping[t];
+    wsr[k] = copy ? p.ws_rows[t] : -1;
+  }
+  // every pass encoded before the first store (the load counter also counts stores, so a wait for
+  // a later pass's data after an earlier pass's stores would wait for those stores too)
+  uint32_t lo[kPasses], hi[kPasses], sbyte[kPasses];
+  int64_t row[kPasses];
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    float x[16];
+    source_to_f32<D, FP8SRC>(p, which, sb[k], x);
+    nvfp4_encode_block<QUOT>(x, p.gscale[which], lo[k], hi[k], sbyte[k]);
+    int64_t page, off;
+    slot_position(p, slot[k], page, off);
+    row[k] = (slot[k] < 0 || slot[k] >= p.num_slots) ? -1 : (page * p.num_kv_heads + h) * p.page_size + off;
+  }
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
     const int64_t t = tw + k * kTokPerPass + lane / nb;
     if (t >= p.num_tokens) break;
-    float x[16];
-    load_source_block<D, FP8SRC>(p, which, t, h, blk, x);
-    const int64_t slot = p.slot_mapping[t];
-    if (slot < 0 || slot >= p.num_slots) continue;
-
-    uint32_t lo, hi, sbyte;
-    nvfp4_encode_block<QUOT>(x, p.gscale[which], lo, hi, sbyte);
-    int64_t page, off;
-    slot_position(p, slot, page, off);
-    const int64_t row = (page * p.num_kv_heads + h) * p.page_size + off;
-    *reinterpret_cast<uint2*>(p.data[which] + row * (D / 2) + blk * 8) = make_uint2(lo, hi);
-    p.scale[which][row * nb + blk] = (uint8_t)sbyte;
+    if (copy) copy_to_workspace<D, FP8SRC>(p, which, wsr[k], h, blk, sb[k]);
+    if (row[k] < 0) continue;
+    *reinterpret_cast<uint2*>(p.data[which] + row[k] * (D / 2) + blk * 8) = make_uint2(lo[k], hi[k]);
+    p.scale[which][row[k] * nb + blk] = (uint8_t)sbyte[k];
   }
 }
 
-// FP8: the same mapping, one 128-bit store per block.
+// FP8: the same mapping, one 128-bit store per block, token by token (loading every pass first and
+// encoding both before the stores, as the NVFP4 kernel does, measured 3% slower here: the software
+// E4M3 encode with its division is the larger cost).
 template <int D>
 __global__ __launch_bounds__(64 * kWavesPerGroup) void fp8_quantize_kernel(QuantizeParams p) {
   constexpr int nb = D / kBlock;
