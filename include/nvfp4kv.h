@@ -493,6 +493,32 @@ int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, const void* k
                       float sm_scale, void* out, void* stream);
 
 /*
+ * nvfp4_extend_attn_fp8 -- nvfp4_extend_attn over the pages' FP8-E4M3
+ * workspace (section A2, path 2: the cached prefix is dequantized into an
+ * FP8 workspace, the current chunk's FP8 K/V are copied next to it, and the
+ * attention runs over that whole FP8 view as in an initial prefill), the
+ * consumer of nvfp4_kv_dequant_workspace_fp8 and of the chunk copy of
+ * nvfp4_kv_quantize_fp8.
+ *
+ *   k_ws, v_ws       device E4M3 bytes [rows][num_kv_heads][head_dim], rows as
+ *                    nvfp4_extend_attn's (16-byte aligned)
+ *   k_scale, v_scale FP32 per-tensor scales of the workspaces (finite, > 0):
+ *                    key t is e4m3(k_ws[t]) * k_scale, value t is
+ *                    e4m3(v_ws[t]) * v_scale. They act as scaling parameters of
+ *                    the two products (same section, Fig. 3): the logits use
+ *                    fl32(fl32(sm_scale * k_scale) * log2(e)), the normalised
+ *                    output is multiplied by v_scale.
+ * The E4M3 values enter the bf16 products exactly (every E4M3 value is a bf16
+ * value). NaN bytes (0x7F, 0xFF) are outside the contract. Other arguments,
+ * results and errors as nvfp4_extend_attn; also NVFP4KV_EINVAL for a scale
+ * that is not finite and > 0, or sm_scale * k_scale overflowing FP32.
+ */
+int nvfp4_extend_attn_fp8(const void* q, const int64_t* q_row_offsets, const void* k_ws, const void* v_ws,
+                          const int64_t* ws_row_offsets, const int32_t* prefix_lens, int32_t batch,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_chunk,
+                          float sm_scale, float k_scale, float v_scale, void* out, void* stream);
+
+/*
  * nvfp4kv_hbm_read_probe -- a measurement utility, not a step of the method:
  * streams `bytes` from `buf` with 16-byte loads (eight loads in flight per
  * thread, `blocks` workgroups of 256 threads) and folds them so that nothing

@@ -82,6 +82,8 @@ _SIGNATURES = {
     "nvfp4_kv_absmax": (ctypes.c_int, [c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "nvfp4_extend_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                                          c_f32, c_vp, c_vp]),
+    "nvfp4_extend_attn_fp8": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                             c_i32, c_f32, c_f32, c_f32, c_vp, c_vp]),
     "nvfp4_kv_quantize_fp8": (ctypes.c_int, [P_GEOM, c_vp, c_vp, c_i64, c_i32, c_vp, c_f32, c_f32, P_NV, P_NV,
                                              c_vp, c_vp, c_vp, c_vp]),
     "nvfp4_kv_dequant_workspace_fp8": (ctypes.c_int, [P_GEOM, P_NV, P_NV, c_vp, c_i32, c_vp, c_vp, c_i32,
@@ -359,6 +361,29 @@ def nvfp4_extend_attn(q, q_row_offsets, k_ws, v_ws, ws_row_offsets, prefix_lens,
                                    ws_row_offsets.data_ptr(), prefix_lens.data_ptr(), prefix_lens.shape[0],
                                    q.shape[1], k_ws.shape[1], q.shape[2], int(max_chunk), float(sm_scale),
                                    out.data_ptr(), _stream(stream)))
+    return out
+
+
+def nvfp4_extend_attn_fp8(q, q_row_offsets, k_ws, v_ws, ws_row_offsets, prefix_lens, sm_scale, k_scale=1.0,
+                          v_scale=1.0, max_chunk=None, out=None, stream=None):
+    """nvfp4_extend_attn over the FP8-E4M3 workspaces k_ws, v_ws ([rows][Hkv][d] uint8 bytes) with per-tensor
+    scales: key t is e4m3(k_ws[t]) * k_scale, value t is e4m3(v_ws[t]) * v_scale. Returns out (bf16)."""
+    _need(q, torch.bfloat16, "q")
+    _need(k_ws, torch.uint8, "k_ws")
+    _need(v_ws, torch.uint8, "v_ws")
+    _need(q_row_offsets, torch.int64, "q_row_offsets")
+    _need(ws_row_offsets, torch.int64, "ws_row_offsets")
+    _need(prefix_lens, torch.int32, "prefix_lens")
+    _check_extend_shapes(q, q_row_offsets, k_ws, v_ws, ws_row_offsets, prefix_lens, out)
+    if max_chunk is None:
+        max_chunk = int((q_row_offsets[1:] - q_row_offsets[:-1]).max().item()) if prefix_lens.numel() else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.bfloat16, "out")
+    _check(lib().nvfp4_extend_attn_fp8(q.data_ptr(), q_row_offsets.data_ptr(), k_ws.data_ptr(), v_ws.data_ptr(),
+                                       ws_row_offsets.data_ptr(), prefix_lens.data_ptr(), prefix_lens.shape[0],
+                                       q.shape[1], k_ws.shape[1], q.shape[2], int(max_chunk), float(sm_scale),
+                                       float(k_scale), float(v_scale), out.data_ptr(), _stream(stream)))
     return out
 
 

@@ -247,11 +247,12 @@ NVFP4KV_API int nvfp4kv_hbm_read_probe(const void* buf, int64_t bytes, int32_t b
                   fn);
 }
 
-NVFP4KV_API int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, const void* k_ws,
-                                  const void* v_ws, const int64_t* ws_row_offsets, const int32_t* prefix_lens,
-                                  int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t max_chunk, float sm_scale, void* out, void* stream) {
-  const char* fn = "nvfp4_extend_attn";
+namespace {
+
+int extend_attn(const char* fn, const void* q, const int64_t* q_row_offsets, const void* k_ws, const void* v_ws,
+                const int64_t* ws_row_offsets, const int32_t* prefix_lens, int32_t batch, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t max_chunk, float sm_scale, bool fp8, float k_scale,
+                float v_scale, void* out, void* stream) {
   if (batch < 0) return fail(NVFP4KV_EINVAL, "%s: batch %d < 0", fn, batch);
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return fail(NVFP4KV_EINVAL, "%s: heads %d / %d (num_q_heads must be a multiple of num_kv_heads)", fn,
@@ -263,6 +264,11 @@ NVFP4KV_API int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, c
     return fail(NVFP4KV_EUNSUPPORTED, "%s: head_dim %d not supported (64 or 128)", fn, head_dim);
   if (max_chunk < 0) return fail(NVFP4KV_EINVAL, "%s: max_chunk %d < 0", fn, max_chunk);
   if (!isfinite(sm_scale)) return fail(NVFP4KV_EINVAL, "%s: sm_scale must be finite", fn);
+  if (fp8 && !(isfinite(k_scale) && k_scale > 0.0f && isfinite(v_scale) && v_scale > 0.0f))
+    return fail(NVFP4KV_EINVAL, "%s: k_scale and v_scale must be finite and > 0", fn);
+  // the logit scale in base-2 units, the K tensor scale folded in as the decode folds its global scale
+  const float qk = (fp8 ? sm_scale * k_scale : sm_scale) * 1.4426950408889634f;
+  if (!isfinite(qk)) return fail(NVFP4KV_EINVAL, "%s: sm_scale * k_scale overflows FP32", fn);
   // one workgroup per (at least 16 queries, KV head, sequence); a 64-row key block addressed in 32 bits
   if ((int64_t)((max_chunk + 15) / 16) * num_kv_heads * batch > 0x7FFFFFFFLL)
     return fail(NVFP4KV_EINVAL, "%s: max_chunk / 16 * num_kv_heads * batch exceeds 2^31 - 1", fn);
@@ -277,17 +283,38 @@ NVFP4KV_API int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, c
   ExtendParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.q_row_offsets = q_row_offsets;
-  p.k = static_cast<const uint16_t*>(k_ws);
-  p.v = static_cast<const uint16_t*>(v_ws);
+  p.k = k_ws;
+  p.v = v_ws;
   p.ws_row_offsets = ws_row_offsets;
   p.prefix_lens = prefix_lens;
   p.batch = batch;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.max_chunk = max_chunk;
-  p.qk_scale = sm_scale * 1.4426950408889634f;
+  p.fp8 = fp8 ? 1 : 0;
+  p.qk_scale = qk;
+  p.out_scale = fp8 ? v_scale : 1.0f;
   p.out = static_cast<uint16_t*>(out);
   return launched(launch_extend_attn(p, head_dim, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+NVFP4KV_API int nvfp4_extend_attn(const void* q, const int64_t* q_row_offsets, const void* k_ws,
+                                  const void* v_ws, const int64_t* ws_row_offsets, const int32_t* prefix_lens,
+                                  int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_chunk, float sm_scale, void* out, void* stream) {
+  return extend_attn("nvfp4_extend_attn", q, q_row_offsets, k_ws, v_ws, ws_row_offsets, prefix_lens, batch,
+                     num_q_heads, num_kv_heads, head_dim, max_chunk, sm_scale, false, 1.0f, 1.0f, out, stream);
+}
+
+NVFP4KV_API int nvfp4_extend_attn_fp8(const void* q, const int64_t* q_row_offsets, const void* k_ws,
+                                      const void* v_ws, const int64_t* ws_row_offsets, const int32_t* prefix_lens,
+                                      int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_chunk, float sm_scale, float k_scale, float v_scale, void* out,
+                                      void* stream) {
+  return extend_attn("nvfp4_extend_attn_fp8", q, q_row_offsets, k_ws, v_ws, ws_row_offsets, prefix_lens, batch,
+                     num_q_heads, num_kv_heads, head_dim, max_chunk, sm_scale, true, k_scale, v_scale, out, stream);
 }
 
 NVFP4KV_API float nvfp4_global_scale_from_absmax(float amax) {

@@ -193,12 +193,14 @@ struct DecodeParams {
 struct ExtendParams {
   const uint16_t* q;            // [q rows][Hq][D] bf16
   const int64_t* q_row_offsets; // [B + 1]
-  const uint16_t* k;            // workspace [rows][Hkv][D] bf16
-  const uint16_t* v;
+  const void* k;                // workspace [rows][Hkv][D] bf16, or E4M3 bytes (fp8)
+  const void* v;
   const int64_t* ws_row_offsets;  // [B + 1]
   const int32_t* prefix_lens;   // [B]
   int32_t batch, num_q_heads, num_kv_heads, max_chunk;
-  float qk_scale;               // sm_scale * log2(e)
+  int32_t fp8;                  // workspace of E4M3 bytes
+  float qk_scale;               // sm_scale * log2(e) (* the K tensor scale, fp8)
+  float out_scale;              // 1, or the V tensor scale (fp8)
   uint16_t* out;                // [q rows][Hq][D] bf16
 };
 

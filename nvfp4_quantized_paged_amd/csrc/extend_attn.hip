@@ -24,6 +24,16 @@
 // The next block is loaded into registers while the current one is computed
 // and written to the second of two LDS buffers (one barrier per block). Row
 // pitches are padded so the lanes of one read spread over the LDS banks.
+//
+// The same kernel reads the pages' FP8-E4M3 workspace (section A2, path 2:
+// the prefix dequantized into an FP8 workspace, the chunk's FP8 K/V copied
+// next to it, attention over the whole FP8 view). Every E4M3 value is a bf16
+// value, so the staging converts the bytes to bf16 exactly (gfx950's
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1) and the products are the bf16
+// kernel's; the K tensor scale joins the logit scale and the V tensor scale
+// the final normalisation, as scaling parameters of the two products (same
+// section, Fig. 3). Half the bytes per key are read from memory; the LDS
+// holds bf16 rows as before.
 #include "common.hpp"
 
 namespace nvfp4kv {
@@ -37,6 +47,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline __attribute__((address_space(3))) v4i16* lds4(const __bf16* p) {
   return (__attribute__((address_space(3))) v4i16*)(p);
@@ -76,7 +87,20 @@ struct ExtCfg {
 // the same up to rounding.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int G>
+// 16 E4M3 bytes -> 16 bf16 values (exact: every E4M3 value is a bf16 value)
+__device__ inline void e4m3x16_to_bf16(const u32x4_t& w, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+    h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+  }
+  lo = u32x4_t{h[0], h[1], h[2], h[3]};
+  hi = u32x4_t{h[4], h[5], h[6], h[7]};
+}
+
+// F8: the workspace holds E4M3 bytes (the tensor scales are in qk_scale and out_scale).
+template <int D, int G, bool F8>
 __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kernel(ExtendParams p, int num_qblocks) {
   using C = ExtCfg<D, G>;
   constexpr int NT = C::kNT;
@@ -141,26 +165,27 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
   const bf16x8_t ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                          (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 
-  // Staging of a 64-key block through registers: K in 16-byte pieces (8 channels of one key),
-  // stored row-major; V in quads of 4 keys x 4 channels (four 8-byte loads, consecutive quads
-  // along the channels so that a wave reads whole rows), transposed with byte permutes and
-  // stored as four 8-byte pieces of V^T rows.
+  // Staging of a 64-key block through registers: K and V in 16-byte pieces (8 bf16 or 16 E4M3
+  // channels of one key, consecutive pieces along a row so that a wave reads whole rows), stored
+  // row-major as bf16.
   constexpr int kThreads = 64 * C::kWaves;
-  constexpr int kKPieces = kKB * D / 8;
+  constexpr int kElemBytes = F8 ? 1 : 2;
+  constexpr int kPieceElems = 16 / kElemBytes;                 // channels per 16-byte piece
+  constexpr int kKPieces = kKB * D / kPieceElems;
   constexpr int kKPer = (kKPieces + kThreads - 1) / kThreads;
   u32x4_t kreg[kKPer];
   u32x4_t vreg[kKPer];
   // A block's rows are read through a buffer descriptor based at its first row (head g) that
   // covers only the block's keys below nkeys: rows past them read as zeros (and are masked).
   // The per-thread offsets within a block are fixed.
-  const uint32_t rs_bytes = (uint32_t)(p.num_kv_heads * D * 2);  // bytes between workspace rows
-  const char* kseq = reinterpret_cast<const char*>(p.k + (kv0 * p.num_kv_heads + g) * D);
-  const char* vseq = reinterpret_cast<const char*>(p.v + (kv0 * p.num_kv_heads + g) * D);
+  const uint32_t rs_bytes = (uint32_t)(p.num_kv_heads * D * kElemBytes);  // bytes between workspace rows
+  const char* kseq = reinterpret_cast<const char*>(p.k) + (kv0 * p.num_kv_heads + g) * D * kElemBytes;
+  const char* vseq = reinterpret_cast<const char*>(p.v) + (kv0 * p.num_kv_heads + g) * D * kElemBytes;
   uint32_t koff[kKPer];
 #pragma unroll
   for (int i = 0; i < kKPer; ++i) {
     const uint32_t piece = threadIdx.x + i * kThreads;
-    koff[i] = piece / (D / 8) * rs_bytes + piece % (D / 8) * 16;
+    koff[i] = piece / (D / kPieceElems) * rs_bytes + piece % (D / kPieceElems) * 16;
   }
   auto load_block = [&](int k0) {
     const int nrec = (int)(min(nkeys - k0, kKB) * rs_bytes);
@@ -182,9 +207,19 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
     for (int i = 0; i < kKPer; ++i) {
       const int piece = threadIdx.x + i * kThreads;
       if (kKPieces % kThreads == 0 || piece < kKPieces) {
-        const int kr = piece / (D / 8), c8 = piece % (D / 8);
-        *reinterpret_cast<u32x4_t*>(&k_lds[buf][kr * C::kKPitch + c8 * 8]) = kreg[i];
-        *reinterpret_cast<u32x4_t*>(&vt_lds[buf][kr * C::kKPitch + c8 * 8]) = vreg[i];
+        const int kr = piece / (D / kPieceElems), c0 = piece % (D / kPieceElems) * kPieceElems;
+        if constexpr (F8) {
+          u32x4_t lo, hi;
+          e4m3x16_to_bf16(kreg[i], lo, hi);
+          *reinterpret_cast<u32x4_t*>(&k_lds[buf][kr * C::kKPitch + c0]) = lo;
+          *reinterpret_cast<u32x4_t*>(&k_lds[buf][kr * C::kKPitch + c0 + 8]) = hi;
+          e4m3x16_to_bf16(vreg[i], lo, hi);
+          *reinterpret_cast<u32x4_t*>(&vt_lds[buf][kr * C::kKPitch + c0]) = lo;
+          *reinterpret_cast<u32x4_t*>(&vt_lds[buf][kr * C::kKPitch + c0 + 8]) = hi;
+        } else {
+          *reinterpret_cast<u32x4_t*>(&k_lds[buf][kr * C::kKPitch + c0]) = kreg[i];
+          *reinterpret_cast<u32x4_t*>(&vt_lds[buf][kr * C::kKPitch + c0]) = vreg[i];
+        }
       }
     }
   };
@@ -303,7 +338,7 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
     const float lt = lsum[n][0];
     const int qi = qw + 16 * (n / C::kHPW) + col;
     if (qi < chunk) {
-      const float inv = 1.0f / lt;
+      const float inv = p.out_scale / lt;
       uint16_t* orow = p.out + ((q_begin + qi) * p.num_q_heads + h0 + n % C::kHPW) * D;
 #pragma unroll
       for (int c = 0; c < C::kCTiles; ++c) {
@@ -322,7 +357,12 @@ hipError_t launch_ext(const ExtendParams& p, hipStream_t s) {
   const int64_t tiles = nqb * p.num_kv_heads * p.batch;
   // grid size, and a 64-row block's byte extent for its buffer descriptor
   if (tiles > INT32_MAX || (int64_t)p.num_kv_heads * D * 2 * kKB > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((extend_attn_kernel<D, G>), dim3((unsigned)tiles), dim3(64 * C::kWaves), 0, s, p, (int)nqb);
+  if (p.fp8)
+    hipLaunchKernelGGL((extend_attn_kernel<D, G, true>), dim3((unsigned)tiles), dim3(64 * C::kWaves), 0, s, p,
+                       (int)nqb);
+  else
+    hipLaunchKernelGGL((extend_attn_kernel<D, G, false>), dim3((unsigned)tiles), dim3(64 * C::kWaves), 0, s, p,
+                       (int)nqb);
   return hipGetLastError();
 }
 

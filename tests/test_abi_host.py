@@ -329,6 +329,28 @@ def test_extend_rejects_bad_arguments(L):
     assert call(q=F + 2) == L.EALIGN and call(k=F + 8) == L.EALIGN and call(out=F + 4) == L.EALIGN
 
 
+def test_extend_fp8_rejects_bad_arguments(L):
+    f = L.lib().nvfp4_extend_attn_fp8
+    F = 1 << 20
+    ok = dict(batch=2, hq=8, hkv=2, d=128, mc=64, sm=0.088, ks=0.5, vs=2.0)
+
+    def call(q=F, qo=F, k=F, v=F, wo=F, pl=F, out=F, **kw):
+        a = dict(ok, **kw)
+        return f(q, qo, k, v, wo, pl, a["batch"], a["hq"], a["hkv"], a["d"], a["mc"], a["sm"], a["ks"], a["vs"],
+                 out, None)
+
+    assert call(batch=0) == L.OK and call(mc=0) == L.OK            # nothing to do
+    assert call(batch=-1) == L.EINVAL and call(mc=-1) == L.EINVAL
+    assert call(hq=6, hkv=2) == L.EUNSUPPORTED and call(d=96) == L.EUNSUPPORTED
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(ks=bad) == L.EINVAL and call(vs=bad) == L.EINVAL
+        assert call(ks=bad, batch=0) == L.EINVAL                  # scales are checked before the no-op
+    assert call(sm=1e30, ks=1e30) == L.EINVAL                       # logit scale overflows FP32
+    assert call(sm=float("nan")) == L.EINVAL
+    assert call(k=None) == L.EINVAL and call(v=None) == L.EINVAL
+    assert call(k=F + 8) == L.EALIGN and call(v=F + 4) == L.EALIGN and call(q=F + 2) == L.EALIGN
+
+
 def test_read_probe_rejects_bad_arguments(L):
     f = L.lib().nvfp4kv_hbm_read_probe
     FAKE16, FAKE4 = 1 << 20, (1 << 20) + 4

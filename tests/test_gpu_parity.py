@@ -695,6 +695,147 @@ def test_extend_attention_randomized(nk, case):
     check_out(out, ref, mass, f"extend random {case}")
 
 
+def _e4m3_f64(b, scale):
+    """Workspace bytes -> float64 values e4m3(byte) * scale (the oracle's E4M3 table)."""
+    return onv.E4M3_VALUES[np.asarray(b, dtype=np.int64)] * float(scale)
+
+
+@pytest.mark.parametrize("G,Hkv,d,P,scale", [(4, 2, 128, 16, 1.0), (1, 2, 64, 32, 0.5), (8, 1, 128, 16, 0.37),
+                                             (16, 1, 64, 16, 1.0)])
+def test_extend_fp8_path2_end_to_end(nk, G, Hkv, d, P, scale):
+    """The pages' path 2 in its own types at a small size: FP8 K/V of earlier
+    turns quantized into the NVFP4 pool, the cached prefix dequantized into the
+    FP8 workspace, the current chunk quantized into the pool and copied into the
+    workspace in the same pass, then the chunk's queries attend through
+    nvfp4_extend_attn_fp8 with the workspace scale as K and V tensor scale.
+    Workspace bytes bit-exact against the oracle; the output against the
+    oracle's attention over the oracle's workspace values. Ragged chunks, an
+    empty prefix, a one-token and an empty chunk."""
+    rng = np.random.default_rng(4242)
+    prefix = np.array([37, 0, 120, 64, 5, 90], np.int32)
+    chunk = np.array([33, 17, 1, 48, 0, 40], np.int32)
+    B, Hq = len(prefix), G * Hkv
+    say(f"case extend fp8 path 2: G {G} Hkv {Hkv} d {d} P {P} scale {scale}")
+    pages_per = -(-(prefix + chunk).max() // P)
+    num_pages = B * pages_per
+    bt = rng.permutation(num_pages).astype(np.int32).reshape(B, pages_per)
+    pos_p = [np.arange(prefix[b]) for b in range(B)]
+    pos_c = [prefix[b] + np.arange(chunk[b]) for b in range(B)]
+    slot = lambda b, t: bt[b, t // P].astype(np.int64) * P + t % P
+    slots_p = np.concatenate([slot(b, pos_p[b]) for b in range(B)])
+    slots_c = np.concatenate([slot(b, pos_c[b]) for b in range(B)])
+    kp_src, vp_src = _fp8_bytes(rng, (len(slots_p), Hkv, d)), _fp8_bytes(rng, (len(slots_p), Hkv, d))
+    kc_src, vc_src = _fp8_bytes(rng, (len(slots_c), Hkv, d)), _fp8_bytes(rng, (len(slots_c), Hkv, d))
+    ws_offs = np.zeros(B + 1, np.int64)
+    ws_offs[1:] = np.cumsum(prefix + chunk + 3)                  # 3 spare rows per sequence
+    rows = int(ws_offs[-1])
+    crow = np.concatenate([ws_offs[b] + pos_c[b] for b in range(B)]).astype(np.int64)
+    # library side
+    kp, vp = nv_pools(nk, num_pages, Hkv, P, d)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    nk.nvfp4_kv_quantize_fp8(dev(kp_src), dev(vp_src), synth.to_device(slots_p), kp, vp, scale, scale)
+    kws = torch.zeros((rows, Hkv, d), dtype=torch.uint8, device="cuda")
+    vws = torch.zeros((rows, Hkv, d), dtype=torch.uint8, device="cuda")
+    nk.nvfp4_kv_dequant_workspace_fp8(kp, vp, synth.to_device(bt), synth.to_device(prefix), synth.to_device(ws_offs),
+                                      kws, vws, scale, scale)
+    nk.nvfp4_kv_quantize_fp8(dev(kc_src), dev(vc_src), synth.to_device(slots_c), kp, vp, scale, scale,
+                             synth.to_device(crow), kws, vws)
+    q_offs = np.zeros(B + 1, np.int64)
+    q_offs[1:] = np.cumsum(chunk)
+    qb = synth.host_values(rng, (int(chunk.sum()), Hq, d))
+    sm = 1.0 / math.sqrt(d)
+    out = nk.nvfp4_extend_attn_fp8(synth.to_device_bf16(qb), synth.to_device(q_offs), kws, vws,
+                                   synth.to_device(ws_offs), synth.to_device(prefix), sm, scale, scale,
+                                   max_chunk=int(chunk.max()) + 5)
+    torch.cuda.synchronize()
+    # oracle side: the pool of the prefix, its FP8 workspace rows, the chunk's source bytes after them
+    ref_ws = []
+    for src in (kp_src, vp_src):
+        dd, ss = onv.empty_cache(num_pages, Hkv, P, d, fill=0)
+        rd, rs = onv.quantize_rows_fp8(src, scale, 1.0)
+        dd[slots_p // P, :, slots_p % P] = rd
+        ss[slots_p // P, :, slots_p % P] = rs
+        cache_b = onv.workspace_fp8_bytes(dd, ss, 1.0, scale)
+        ws = np.zeros((rows, Hkv, d), np.uint8)
+        for b in range(B):
+            ws[ws_offs[b]:ws_offs[b] + prefix[b]] = oatt.gather_tokens(cache_b, bt[b], int(prefix[b]))
+        ref_ws.append(ws)
+    ref_ws[0][crow], ref_ws[1][crow] = kc_src, vc_src
+    assert_pool_equal(kws, ref_ws[0], "fp8 K workspace")
+    assert_pool_equal(vws, ref_ws[1], "fp8 V workspace")
+    ref, mass = oatt.extend_attention(synth.bf16_bits_to_f64(qb), _e4m3_f64(ref_ws[0], scale),
+                                      _e4m3_f64(ref_ws[1], scale), q_offs, ws_offs, prefix, sm)
+    check_out(out, ref, mass, f"extend fp8 G{G} d{d} scale {scale}")
+
+
+@pytest.mark.parametrize("v_scale", [1.0, 0.125])
+def test_extend_fp8_every_value_byte(nk, v_scale):
+    """A query that sees one key returns that key's value row: with the value
+    rows holding every finite E4M3 byte, the output is each E4M3 value times a
+    power-of-two scale, exactly (the conversion to bf16 is exact)."""
+    d, Hkv, G = 128, 1, 1
+    vals = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    vals = np.concatenate([vals, np.zeros(2 * d - len(vals), np.uint8)])
+    B = 2
+    say(f"case extend fp8 every value byte: v_scale {v_scale}")
+    prefix = np.zeros(B, np.int32)
+    ws_offs = np.arange(B + 1, dtype=np.int64)
+    q_offs = np.arange(B + 1, dtype=np.int64)
+    vb = vals.reshape(B, Hkv, d)
+    kb = np.full((B, Hkv, d), 0x38, np.uint8)                    # keys of 1.0
+    qb = synth.host_values(np.random.default_rng(3), (B, G * Hkv, d))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out = nk.nvfp4_extend_attn_fp8(synth.to_device_bf16(qb), synth.to_device(q_offs), dev(kb), dev(vb),
+                                   synth.to_device(ws_offs), synth.to_device(prefix), 0.09, 0.75, v_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    want = onv.E4M3_VALUES[vb.astype(np.int64)] * v_scale
+    bad = np.argwhere(got != want)
+    assert len(bad) == 0, f"{len(bad)} values differ; first at {tuple(bad[0])}: {got[tuple(bad[0])]} vs " \
+                          f"{want[tuple(bad[0])]}"
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_extend_fp8_randomized(nk, case):
+    """Seeded random extend problems over FP8 workspaces filled directly with
+    random finite E4M3 bytes: batch, query group, KV heads, head_dim, ragged
+    prefixes to 1,000 keys and chunks (zeros included), spare rows, K and V
+    tensor scales, either sign of the logit scale; against the oracle."""
+    rng = np.random.default_rng(6161 + case)
+    B = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 3]))
+    d = int(rng.choice([64, 128]))
+    Hq = G * Hkv
+    prefix = rng.integers(0, 1001, B).astype(np.int32)
+    chunk = rng.integers(0, 201, B).astype(np.int32)
+    full = int(rng.integers(0, B))
+    chunk[full] = int(rng.integers(1, 201))
+    if case % 2 == 0:
+        prefix[0] = 0
+    spare = rng.integers(0, 6, B)
+    ws_offs = np.zeros(B + 1, np.int64)
+    ws_offs[1:] = np.cumsum(prefix + chunk + spare)
+    rows = int(ws_offs[-1])
+    k_scale = float(rng.choice([1.0 / 64, 1.0 / 300, 0.02]))
+    v_scale = float(rng.choice([1.0, 0.01, 3.7]))
+    sm = float(rng.choice([1.0, -1.0])) / math.sqrt(d)
+    say(f"case extend fp8 random {case}: B {B} G {G} Hkv {Hkv} d {d} prefix {prefix.tolist()} "
+        f"chunk {chunk.tolist()} k_scale {k_scale:.4g} v_scale {v_scale} sm {sm:+.3f}")
+    kb, vb = _fp8_bytes(rng, (rows, Hkv, d)), _fp8_bytes(rng, (rows, Hkv, d))
+    q_offs = np.zeros(B + 1, np.int64)
+    q_offs[1:] = np.cumsum(chunk)
+    qb = synth.host_values(rng, (int(chunk.sum()), Hq, d))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out = nk.nvfp4_extend_attn_fp8(synth.to_device_bf16(qb), synth.to_device(q_offs), dev(kb), dev(vb),
+                                   synth.to_device(ws_offs), synth.to_device(prefix), sm, k_scale, v_scale,
+                                   max_chunk=int(chunk.max()) + int(rng.integers(0, 40)))
+    torch.cuda.synchronize()
+    ref, mass = oatt.extend_attention(synth.bf16_bits_to_f64(qb), _e4m3_f64(kb, k_scale), _e4m3_f64(vb, v_scale),
+                                      q_offs, ws_offs, prefix, sm)
+    check_out(out, ref, mass, f"extend fp8 random {case}")
+
+
 # ---------------------------------------------------------------------------
 # decode attention
 # ---------------------------------------------------------------------------
