@@ -556,6 +556,24 @@ def decode_figures(nk, variant, iters, warmup, flush, measured):
 # agentic prefix reuse
 # ---------------------------------------------------------------------------
 
+def _oracle_sequence_rows(w, b, pool):
+    """The oracle's NVFP4 rows (K data, K scales, V data, V scales) of every
+    token of agentic sequence b (shared prefix, private tokens, the new chunk),
+    quantized from the generated bf16 sources."""
+    import numpy as np
+    import synth
+    C, H = w.wl.chunk, w.wl.num_kv_heads
+    kb = np.concatenate([synth.bf16_tensor_bits(w.k_shared), synth.bf16_tensor_bits(w.k_private[b]),
+                         synth.bf16_tensor_bits(w.k_chunk[b * C:(b + 1) * C])])
+    vb = np.concatenate([synth.bf16_tensor_bits(w.v_shared), synth.bf16_tensor_bits(w.v_private[b]),
+                         synth.bf16_tensor_bits(w.v_chunk[b * C:(b + 1) * C])])
+    step = max(1, PIECE // H)
+    jobs = [("nvfp4", kb[t:t + step], vb[t:t + step]) for t in range(0, len(kb), step)]
+    parts = pool.map(_oracle_quantize_piece, jobs, chunksize=1) if pool is not None else \
+        [_oracle_quantize_piece(j) for j in jobs]
+    return tuple(np.concatenate([p[i][j] for p in parts]) for i in (0, 1) for j in (0, 1))
+
+
 def agentic_parity(nk, w, out, pool, seqs=(0, 37)):
     """Oracle check of the agentic step's outputs for sampled sequences: the
     pool bytes of every token (shared prefix, private tokens, the new chunk),
@@ -573,18 +591,7 @@ def agentic_parity(nk, w, out, pool, seqs=(0, 37)):
     t0 = time.time()
     for b in seqs:
         L = int(w.host_cached_lens[b])
-        kb = np.concatenate([synth.bf16_tensor_bits(w.k_shared), synth.bf16_tensor_bits(w.k_private[b]),
-                             synth.bf16_tensor_bits(w.k_chunk[b * C:(b + 1) * C])])
-        vb = np.concatenate([synth.bf16_tensor_bits(w.v_shared), synth.bf16_tensor_bits(w.v_private[b]),
-                             synth.bf16_tensor_bits(w.v_chunk[b * C:(b + 1) * C])])
-        step = max(1, PIECE // H)
-        jobs = [("nvfp4", kb[t:t + step], vb[t:t + step]) for t in range(0, L + C, step)]
-        parts = pool.map(_oracle_quantize_piece, jobs, chunksize=1) if pool is not None else \
-            [_oracle_quantize_piece(j) for j in jobs]
-        kd = np.concatenate([p[0][0] for p in parts])
-        ks = np.concatenate([p[0][1] for p in parts])
-        vd = np.concatenate([p[1][0] for p in parts])
-        vs = np.concatenate([p[1][1] for p in parts])
+        kd, ks, vd, vs = _oracle_sequence_rows(w, b, pool)
         t = np.arange(L + C)
         pages = torch.from_numpy(w.host_bt[b][t // P].astype(np.int64)).cuda()
         offp = torch.from_numpy(t % P).cuda()
@@ -608,19 +615,30 @@ def agentic_parity(nk, w, out, pool, seqs=(0, 37)):
     return res
 
 
-def extend_parity(w, qx, ox, q_offs_host, b=5, last=4):
+def extend_parity(w, qx, ox, q_offs_host, pool, b=5, last=4, chunk8=None):
     """Oracle check of the extend output: the last `last` queries of sequence b,
     as an extend problem whose prefix is the cached prefix plus the chunk
-    tokens before them (the same keys and positions)."""
+    tokens before them (the same keys and positions). The keys and values are
+    the oracle's: the cached prefix quantized and dequantized by the oracle
+    (bf16 workspace), or its E4M3 workspace bytes (chunk8 = the chunk's FP8
+    source bytes: FP8 workspace, scales 1), then the chunk's own rows."""
     import numpy as np
     import synth
     from oracle import attention as oatt
+    from oracle import nvfp4 as onv
     wl = w.wl
     C, L = wl.chunk, int(w.host_cached_lens[b])
-    off = int(w.ws_row_offsets[b].item())
     n = L + C
-    kw = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(w.k_ws[off:off + n]))
-    vw = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(w.v_ws[off:off + n]))
+    kd, ks, vd, vs = _oracle_sequence_rows(w, b, pool)
+    if chunk8 is None:
+        kc = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(w.k_chunk[b * C:(b + 1) * C]))
+        vc = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(w.v_chunk[b * C:(b + 1) * C]))
+        kw = np.concatenate([onv.dequant_rows(kd[:L], ks[:L]), kc])
+        vw = np.concatenate([onv.dequant_rows(vd[:L], vs[:L]), vc])
+    else:
+        k8, v8 = (c[b * C:(b + 1) * C].cpu().numpy() for c in chunk8)
+        kw = onv.E4M3_VALUES[np.concatenate([onv.workspace_fp8_bytes(kd[:L], ks[:L]), k8]).astype(np.int64)]
+        vw = onv.E4M3_VALUES[np.concatenate([onv.workspace_fp8_bytes(vd[:L], vs[:L]), v8]).astype(np.int64)]
     r0 = int(q_offs_host[b]) + C - last
     q = synth.bf16_bits_to_f64(synth.bf16_tensor_bits(qx[r0:r0 + last]))
     ref, mass = oatt.extend_attention(q, kw, vw, np.array([0, last]), np.array([0, n]),
@@ -641,8 +659,8 @@ def agentic(nk, wl, iters, warmup, flush, pool, parity=True):
     time_flushed does; the plain decode of the same batch is timed beside it. Run twice: with bf16 chunk and
     workspace (the workload definition) and with the pages' FP8 types (FP8
     chunk quantized to NVFP4 and copied into an FP8 workspace in one pass,
-    FP8 workspace). Then extend attention over the workspace and the
-    calibration absmax, outside the step."""
+    FP8 workspace). Then extend attention over the bf16 workspace and over
+    the FP8 one, and the calibration absmax, outside the step."""
     import numpy as np
     import torch
     from synth.workload import agentic_bytes, build_agentic_workload
@@ -749,7 +767,22 @@ def agentic(nk, wl, iters, warmup, flush, pool, parity=True):
                                "bf16_mfma_peak_frac": round(flops / med(te) / 2.5e15, 4), "flops": flops}
     log(f"[bench] extend attention {te['median_ms']:.3f} ms, {flops / med(te) / 1e12:.1f} TFLOP/s")
     if parity:
-        res["extend_attention"]["parity"] = extend_parity(w, qx, ox, q_offs_host)
+        res["extend_attention"]["parity"] = extend_parity(w, qx, ox, q_offs_host, pool)
+
+    # the same over the pages' FP8 workspace: the prefix from the FP8 workspace kernel, the chunk's FP8 bytes
+    # copied next to it by the FP8 quantize (both above), workspace scales 1
+    deq8()
+    quant8()
+    ext8 = lambda: nk.nvfp4_extend_attn_fp8(qx, q_offs, kws8, vws8, w.ws_row_offsets, w.cached_lens, wl.sm_scale,
+                                            1.0, 1.0, max_chunk=C, out=ox)
+    te8 = time_flushed(ext8, max(5, iters // 3), 2, flush, ramp_s=0.0)
+    res["fp8_path2"]["extend_attention_fp8"] = {**te8, "tflops": round(flops / med(te8) / 1e12, 1),
+                                                "bf16_mfma_peak_frac": round(flops / med(te8) / 2.5e15, 4)}
+    log(f"[bench] extend attention over the FP8 workspace {te8['median_ms']:.3f} ms, "
+        f"{flops / med(te8) / 1e12:.1f} TFLOP/s")
+    if parity:
+        res["fp8_path2"]["extend_attention_fp8"]["parity"] = extend_parity(w, qx, ox, q_offs_host, pool,
+                                                                           chunk8=(k8, v8))
 
     # global-scale calibration of the chunk (absmax of K and V), not part of the step
     amax = torch.zeros(2, dtype=torch.float32, device="cuda")
@@ -920,9 +953,12 @@ def main():
                     (4, synth.WORKLOADS[4].batch, False): (c4["nvfp4"]["step"]["median_ms"] / 1e3,
                                                           c4["nvfp4"]["num_splits"])}
         result["decode_figures"] = decode_figures(nk, variant, iters, warmup, flush, measured)
+        ag = configs["agentic_prefix_reuse"]
+        agentic_checks = (ag.get("parity"), ag.get("extend_attention", {}).get("parity"),
+                          ag.get("fp8_path2", {}).get("extend_attention_fp8", {}).get("parity"))
         result["parity_all_pass"] = all(
             c[f]["parity"]["pass"] for c in configs.values() for f in ("nvfp4", "fp8") if f in c and "parity" in c[f]
-        ) and configs["agentic_prefix_reuse"].get("parity", {"pass": True})["pass"] if parity else None
+        ) and all(p["pass"] for p in agentic_checks if p is not None) if parity else None
 
     if not args.no_cpu_baseline:
         t = time.time()
