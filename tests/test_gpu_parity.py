@@ -1287,7 +1287,7 @@ def test_fp8_decode_moderate(nk):
         check_out(out, ref, mass, f"fp8 variant={var}")
 
 
-def _shared_prefix_problem(nk, seed, B, H, G, d, P, shared, lens):
+def _shared_prefix_problem(nk, seed, B, H, G, d, P, shared, lens, gs=1.0, dev_lens=None):
     """A batch whose first `shared` tokens sit on the same physical pages in
     every block-table row (a sequence shorter than the prefix reads its own
     first tokens from those pages), private pages after it, quantized on both
@@ -1313,11 +1313,12 @@ def _shared_prefix_problem(nk, seed, B, H, G, d, P, shared, lens):
     k = synth.host_values(rng, (len(slots), H, d))
     v = synth.host_values(rng, (len(slots), H, d))
     q = synth.host_values(rng, (B, H * G, d))
-    kp, vp = gpu_quantize_nv(nk, num_pages, H, P, d, k, v, slots)
-    kd, ks, vd, vs = oracle_nv(num_pages, H, P, d, k, v, slots)
+    kp, vp = gpu_quantize_nv(nk, num_pages, H, P, d, k, v, slots, gs)
+    kd, ks, vd, vs = oracle_nv(num_pages, H, P, d, k, v, slots, gs)
     sl = np.array(lens, dtype=np.int32)
-    ref, mass = oatt.paged_decode(q, onv.dequant_cache(kd, ks), onv.dequant_cache(vd, vs), bt, sl, 0.125)
-    return (synth.to_device_bf16(q), synth.to_device(bt), synth.to_device(sl)), (kp, vp), (ref, mass)
+    ref, mass = oatt.paged_decode(q, onv.dequant_cache(kd, ks, gs), onv.dequant_cache(vd, vs, gs), bt, sl, 0.125)
+    sl_dev = sl if dev_lens is None else np.array(dev_lens, dtype=np.int32)   # lengths the library is given
+    return (synth.to_device_bf16(q), synth.to_device(bt), synth.to_device(sl_dev)), (kp, vp), (ref, mass)
 
 
 @pytest.mark.parametrize("G,d,P,shared,lens,sp,sr", [
@@ -1342,6 +1343,24 @@ def test_shared_prefix_decode_against_oracle(nk, G, d, P, shared, lens, sp, sr):
     check_out(out, ref, mass, "shared prefix")
     check_out(plain, ref, mass, "plain decode")
     assert torch.all(out[torch.tensor(lens, device=out.device) == 0].float() == 0)
+
+
+@pytest.mark.parametrize("G,d", [(4, 128), (5, 64)])
+def test_shared_prefix_decode_scaled_and_clamped(nk, G, d):
+    """The shared-prefix decode with calibrated (non-power-of-two) K and V
+    tensor scales, and one sequence length past the block table's reach (taken
+    as the reach, like the plain decode): against the oracle at the clamped
+    length."""
+    P, shared, H = 16, 64, 2
+    lens = [64, 200, 33, 150, 64, 90, 304]                      # the last fills the table's reach (19 pages)
+    dev_lens = lens[:6] + [lens[6] + 500]
+    say(f"case shared prefix scaled and clamped G{G} d{d}: reach {lens[6]}, length {dev_lens[6]}")
+    (q, bt, sl), (kp, vp), (ref, mass) = _shared_prefix_problem(nk, 1700 + G + d, len(lens), H, G, d, P, shared,
+                                                                  lens, gs=GS_THIRD, dev_lens=dev_lens)
+    assert bt.shape[1] * P == lens[6]
+    out = nk.nvfp4_paged_decode_attn_shared_prefix(q, kp, vp, bt, sl, 0.125, shared)
+    torch.cuda.synchronize()
+    check_out(out, ref, mass, "shared prefix, scaled and clamped")
 
 
 @pytest.mark.parametrize("S", [1, 3])
