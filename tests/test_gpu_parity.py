@@ -701,7 +701,7 @@ def _e4m3_f64(b, scale):
 
 
 @pytest.mark.parametrize("G,Hkv,d,P,scale", [(4, 2, 128, 16, 1.0), (1, 2, 64, 32, 0.5), (8, 1, 128, 16, 0.37),
-                                             (16, 1, 64, 16, 1.0)])
+                                             (16, 1, 64, 16, 1.0), (16, 2, 128, 16, 0.5), (8, 3, 64, 64, 2.0)])
 def test_extend_fp8_path2_end_to_end(nk, G, Hkv, d, P, scale):
     """The pages' path 2 in its own types at a small size: FP8 K/V of earlier
     turns quantized into the NVFP4 pool, the cached prefix dequantized into the
