@@ -196,6 +196,20 @@ hipError_t run_merge(const DecodeParams& d, int head_dim, float out_scale, void*
   return launch_lse_merge(m, s);
 }
 
+// The whole decode: partials, then the merge. With one split the matrix-core kernel writes the
+// output itself, by the merge's arithmetic (same bits), and the merge launch is skipped.
+hipError_t run_decode(DecodeParams p, int head_dim, bool fp8, int32_t variant, float out_scale, void* out,
+                      hipStream_t s) {
+  if (p.num_splits == 1 && variant != NVFP4KV_VARIANT_VALU) {
+    p.out_direct = static_cast<uint16_t*>(out);
+    p.out_scale = out_scale;
+    return run_partial(p, head_dim, fp8, variant, s);
+  }
+  hipError_t e = run_partial(p, head_dim, fp8, variant, s);
+  if (e == hipSuccess) e = run_merge(p, head_dim, out_scale, out, s);
+  return e;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -666,9 +680,7 @@ NVFP4KV_API int nvfp4_paged_decode_attn(const nvfp4kv_geom* geom, const void* q,
                                      block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, c,
                                      sm_scale, k_cache->global_scale, workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = run_partial(p, geom->head_dim, false, NVFP4KV_VARIANT_AUTO, s);
-  if (e == hipSuccess) e = run_merge(p, geom->head_dim, v_cache->global_scale, out, s);
-  return launched(e, fn);
+  return launched(run_decode(p, geom->head_dim, false, NVFP4KV_VARIANT_AUTO, v_cache->global_scale, out, s), fn);
 }
 
 // ---------------------------------------------------------------------------
@@ -746,9 +758,8 @@ int append_decode(const char* fn, bool merge, const nvfp4kv_geom* geom, const vo
     out_scale = v_cache->global_scale;
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = run_partial(p, geom->head_dim, FP8, NVFP4KV_VARIANT_MFMA, s);
-  if (e == hipSuccess && merge) e = run_merge(p, geom->head_dim, out_scale, out, s);
-  return launched(e, fn);
+  if (merge) return launched(run_decode(p, geom->head_dim, FP8, NVFP4KV_VARIANT_MFMA, out_scale, out, s), fn);
+  return launched(run_partial(p, geom->head_dim, FP8, NVFP4KV_VARIANT_MFMA, s), fn);
 }
 
 }  // namespace
@@ -867,9 +878,7 @@ NVFP4KV_API int nvfp4_paged_decode_attn_noalloc(const nvfp4kv_geom* geom, const 
                                      block_tables, max_pages_per_seq, seq_lens, batch, num_q_heads, c,
                                      sm_scale, k_cache->global_scale, ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = run_partial(p, geom->head_dim, false, NVFP4KV_VARIANT_AUTO, s);
-  if (e == hipSuccess) e = run_merge(p, geom->head_dim, v_cache->global_scale, out, s);
-  return launched(e, fn);
+  return launched(run_decode(p, geom->head_dim, false, NVFP4KV_VARIANT_AUTO, v_cache->global_scale, out, s), fn);
 }
 
 NVFP4KV_API int fp8_paged_decode_partial(const nvfp4kv_geom* geom, const void* q,
@@ -911,9 +920,7 @@ NVFP4KV_API int fp8_paged_decode_attn(const nvfp4kv_geom* geom, const void* q, c
                                      max_pages_per_seq, seq_lens, batch, num_q_heads, c, sm_scale,
                                      k_cache->scale, workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = run_partial(p, geom->head_dim, true, NVFP4KV_VARIANT_AUTO, s);
-  if (e == hipSuccess) e = run_merge(p, geom->head_dim, v_cache->scale, out, s);
-  return launched(e, fn);
+  return launched(run_decode(p, geom->head_dim, true, NVFP4KV_VARIANT_AUTO, v_cache->scale, out, s), fn);
 }
 
 NVFP4KV_API int nvfp4kv_lse_merge(const void* workspace, size_t workspace_bytes, int32_t batch,

@@ -166,6 +166,10 @@ struct DecodeParams {
   const int32_t* seq_lens;
   _Float16* part_o;         // [B][Hq][S][D] f16: each split's o / l (0 for an empty split)
   float* part_ml;           // [B][Hq][S][2]: (m, l)
+  // One split (num_splits == 1, not the shared-prefix items): if non-null, the kernel writes the
+  // bf16 output [B][Hq][D] itself, with the merge's arithmetic, instead of the partials
+  uint16_t* out_direct;
+  float out_scale;          // V tensor scale, for out_direct
   int32_t max_pages, batch, num_q_heads, num_kv_heads, group, page_size, num_splits;
   int32_t num_pages;        // pool size: page indices are clamped into [0, num_pages)
   float qk_scale;           // sm_scale * K global scale * log2(e)

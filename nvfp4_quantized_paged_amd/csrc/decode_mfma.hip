@@ -544,7 +544,7 @@ void decode_partial_mfma_kernel(DecodeParams p) {
 
   // LDS: the unpacked V rows of a chunk in the loop, the partial results at the end
   constexpr int kVlHalfs = 32 * VPitch<D>::kHalfs;
-  constexpr int kStageHalfs = 16 * D * 2 + 2 * 16;               // G <= 16 fp32 rows, 16 fp32 1 / l
+  constexpr int kStageHalfs = 16 * D * 2 + 4 * 16;               // G <= 16 fp32 rows, 16 fp32 1 / l and l
   __shared__ __attribute__((aligned(16))) _Float16 vl[kVlHalfs > kStageHalfs ? kVlHalfs : kStageHalfs];
   Acc<D> a;
 #pragma unroll
@@ -632,13 +632,38 @@ void decode_partial_mfma_kernel(DecodeParams p) {
   // then cut the decode call by 2%).
   float4_t* stage = reinterpret_cast<float4_t*>(vl);
   float* stage_il = reinterpret_cast<float*>(vl) + 16 * D;         // past the G <= 16 staged rows
+  float* stage_l = stage_il + 16;
   const float lt = a.ls[0];
   if (col < ncol) {
 #pragma unroll
     for (int ct = 0; ct < C::kCTiles; ++ct) stage[(col * D + 16 * ct + 4 * grp) / 4] = a.o[ct];
-    if (grp == 0) stage_il[col] = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (grp == 0) {
+      stage_il[col] = lt > 0.0f ? 1.0f / lt : 0.0f;
+      stage_l[col] = lt;
+    }
   }
   __syncthreads();
+  if constexpr (!CAS) {
+    if (p.out_direct != nullptr) {
+      // One split: the output itself, by the log-sum-exp merge's arithmetic for a single partial
+      // (the f16 row u = o / l, then fl(l * u) * fl(out_scale / l), rounded to bf16; zeros for a
+      // split without tokens), so the result is bit for bit that of the partial and the merge.
+      for (int e = lane; e < ncol * D / 4; e += 64) {
+        const int row = e / (D / 4), c4 = e % (D / 4);
+        const float il = stage_il[row], l = stage_l[row];
+        const float4_t x = stage[e];
+        uint16_t h[4] = {0, 0, 0, 0};
+        if (l > 0.0f) {
+          const float sc = p.out_scale / l;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) h[k] = f32_to_bf16_rne(l * (float)(_Float16)(x[k] * il) * sc);
+        }
+        const uint2 w = make_uint2((uint32_t)h[0] | (uint32_t)h[1] << 16, (uint32_t)h[2] | (uint32_t)h[3] << 16);
+        *reinterpret_cast<uint2*>(p.out_direct + qrow(row) * D + 4 * c4) = w;
+      }
+      return;
+    }
+  }
   for (int e = lane; e < ncol * D / 4; e += 64) {
     const int row = e / (D / 4), c4 = e % (D / 4);
     const int64_t idx = qrow(row) * S + slot;

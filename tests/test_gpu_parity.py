@@ -1287,6 +1287,59 @@ def test_fp8_decode_moderate(nk):
         check_out(out, ref, mass, f"fp8 variant={var}")
 
 
+@pytest.mark.parametrize("fmt,G,d,P,gs", [("nvfp4", 4, 128, 16, 1.0), ("nvfp4", 5, 64, 32, GS_THIRD),
+                                          ("nvfp4", 16, 128, 64, 0.5), ("fp8", 8, 128, 16, 0.37),
+                                          ("fp8", 1, 64, 48, 1.0)])
+def test_single_split_decode_equals_partial_and_merge(nk, fmt, G, d, P, gs):
+    """With one split the decode kernel writes the output itself (no merge
+    launch): bit for bit the output of the one-split partial followed by the
+    merge, for every entry point that takes that route (the decode, the decode
+    with the append, the allocation-free decode), with an empty sequence and
+    one past the block table's reach; and within tolerance of the oracle."""
+    H = 2
+    wl = synth.Workload(95, "single", 5, G * H, H, d, P, 150, True, 1)
+    inp = synth.host_uniform_decode(wl)
+    reach = inp.block_tables.shape[1] * P
+    inp.seq_lens[:] = np.array([150, 0, 1, 77, 150], np.int32)
+    say(f"case single split {fmt} G{G} d{d} P{P} gs {gs}")
+    q = synth.to_device_bf16(inp.q)
+    bt = synth.to_device(inp.block_tables)
+    sl_np = inp.seq_lens.copy()
+    sl_np[4] = reach + 300                                   # taken as the reach
+    sl = synth.to_device(sl_np)
+    if fmt == "nvfp4":
+        kp, vp = gpu_quantize_nv(nk, inp.num_pages, H, P, d, inp.k, inp.v, inp.slot_mapping, gs)
+        attn, part, vscale = nk.nvfp4_paged_decode_attn, nk.nvfp4_paged_decode_partial, vp.global_scale
+        kd, ks, vd, vs = oracle_nv(inp.num_pages, H, P, d, inp.k, inp.v, inp.slot_mapping, gs)
+        kh, vh = onv.dequant_cache(kd, ks, gs), onv.dequant_cache(vd, vs, gs)
+    else:
+        kp, vp = f8_pools(nk, inp.num_pages, H, P, d, gs)
+        nk.fp8_kv_quantize(synth.to_device_bf16(inp.k), synth.to_device_bf16(inp.v),
+                           synth.to_device(inp.slot_mapping), kp, vp)
+        attn, part, vscale = nk.fp8_paged_decode_attn, nk.fp8_paged_decode_partial, vp.scale
+        kr = np.full((inp.num_pages, H, P, d), SENT, np.uint8)
+        vr = kr.copy()
+        of8.write_cache(kr, inp.k, inp.slot_mapping, gs)
+        of8.write_cache(vr, inp.v, inp.slot_mapping, gs)
+        kh, vh = of8.dequant_cache(kr, gs), of8.dequant_cache(vr, gs)
+    ws = part(q, kp, vp, bt, sl, wl.sm_scale, 1)
+    ref2 = torch.empty_like(q)
+    nk.nvfp4kv_lse_merge(ws, q.shape[0], q.shape[1], d, 1, vscale, ref2)
+    direct = attn(q, kp, vp, bt, sl, wl.sm_scale, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(direct.view(torch.int16), ref2.view(torch.int16)), "one-split decode differs from partial + merge"
+    if fmt == "nvfp4":
+        noalloc = torch.empty_like(q)
+        nk.nvfp4_paged_decode_attn_noalloc(q, kp, vp, bt, sl, wl.sm_scale, noalloc, num_splits=1)
+        torch.cuda.synchronize()
+        assert torch.equal(noalloc.view(torch.int16), ref2.view(torch.int16)), "allocation-free decode differs"
+    assert torch.all(direct[1].float() == 0)                 # the empty sequence
+    rl = inp.seq_lens.copy()
+    rl[4] = reach
+    ref, mass = oatt.paged_decode(inp.q, kh, vh, inp.block_tables, rl, wl.sm_scale)
+    check_out(direct, ref, mass, f"single split {fmt}")
+
+
 def _shared_prefix_problem(nk, seed, B, H, G, d, P, shared, lens, gs=1.0, dev_lens=None):
     """A batch whose first `shared` tokens sit on the same physical pages in
     every block-table row (a sequence shorter than the prefix reads its own
