@@ -207,10 +207,10 @@ int nvfp4_kv_dequant_workspace_fp8(const nvfp4kv_geom* geom, const nvfp4kv_cache
  * [j*C, min(L_b, (j+1)*C)) with C = ceil(ceil(L_b / num_splits) / P) * P
  * (page-aligned), producing a partial (m, l, o[d] / l); a second kernel merges
  * the splits by log-sum-exp. Query head h reads KV head h / G. With one split,
- * the entry points that return `out` (the *_attn calls, not *_partial) skip the
- * merge: the decode kernel writes `out` itself with the merge's arithmetic (the
- * same bits as the partial followed by nvfp4kv_lse_merge) and leaves the
- * workspace unwritten.
+ * nvfp4_paged_decode_attn, fp8_paged_decode_attn, the two *_append_attn calls
+ * and nvfp4_paged_decode_attn_noalloc skip the merge: the decode kernel writes
+ * `out` itself with the merge's arithmetic (the same bits as the partial
+ * followed by nvfp4kv_lse_merge) and leaves the workspace unwritten.
  *
  * nvfp4_paged_decode_num_splits -- the library's split count for a batch when
  *   the caller passes num_splits = 0 (depends on sizes only: as many splits
