@@ -11,9 +11,10 @@ One step = quantize-on-write of the step's new token of every sequence into
 the pool (it overwrites the last slot, so the shape stays fixed) + split-KV
 decode partials + log-sum-exp merge. The library's decode-with-append call
 does the first two in one kernel (the wave whose split holds the new token
-encodes and stores it); the same step as separate launches (quantize kernel,
-partial kernel, merge) is timed beside it. Inputs are resident in HBM before
-timing.
+encodes and stores it), and with one split (the tiny workload) that kernel
+also writes the output, so there is no merge launch; the same step as
+separate launches (quantize kernel, partial kernel, merge) is timed beside
+it. Inputs are resident in HBM before timing.
 
 Timing method (every figure): after an untimed ramp and the warm-up, each
 timed iteration is preceded by an untimed flush (a 1 GiB write, four times
@@ -389,7 +390,8 @@ class Bench:
 
     def step(self):
         """One decode step: each sequence's new token quantized into its pool slot by the decode
-        kernel itself (quantize-on-write fused into the partial kernel), the partials, the merge.
+        kernel itself (quantize-on-write fused into the partial kernel), the partials, the merge
+        (with one split the decode kernel writes the output and no merge runs).
         The VALU variant has no fused form and runs the separate step."""
         if self.variant == self.nk.VARIANT_VALU:
             return self.step_separate()
