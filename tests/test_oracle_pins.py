@@ -541,6 +541,34 @@ def test_extend_attention_pins():
             assert np.allclose(out[i, h], o, rtol=1e-12, atol=1e-12)
 
 
+def test_extend_attention_matches_torch_sdpa():
+    """Ragged sequences (an empty prefix, a one-query chunk, spare workspace
+    rows between sequences, GQA groups of 4): each sequence's chunk against
+    torch's scaled_dot_product_attention in float64 with the causal mask
+    shifted by the prefix length (query i sees keys j <= prefix + i)."""
+    rng = np.random.default_rng(37)
+    Hq, Hkv, d, sm = 8, 2, 32, -0.17
+    G = Hq // Hkv
+    prefix, chunk, spare = np.array([13, 0, 40]), np.array([7, 5, 1]), np.array([2, 0, 3])
+    qo = np.concatenate([[0], np.cumsum(chunk)])
+    wo = np.concatenate([[0], np.cumsum(prefix + chunk + spare)])
+    q = rng.standard_normal((int(qo[-1]), Hq, d))
+    k = rng.standard_normal((int(wo[-1]), Hkv, d))
+    v = rng.standard_normal((int(wo[-1]), Hkv, d))
+    out, mass = attention.extend_attention(q, k, v, qo, wo, prefix.astype(np.int32), sm)
+    for b in range(len(prefix)):
+        n, c = int(prefix[b] + chunk[b]), int(chunk[b])
+        kb = k[wo[b]:wo[b] + n].transpose(1, 0, 2)                    # [Hkv][n][d]
+        vb = v[wo[b]:wo[b] + n].transpose(1, 0, 2)
+        kq = torch.from_numpy(np.repeat(kb, G, axis=0))[None]         # [1][Hq][n][d]
+        vq = torch.from_numpy(np.repeat(vb, G, axis=0))[None]
+        qq = torch.from_numpy(q[qo[b]:qo[b + 1]].transpose(1, 0, 2).copy())[None]   # [1][Hq][c][d]
+        mask = torch.from_numpy(np.arange(n)[None, :] <= prefix[b] + np.arange(c)[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kq, vq, attn_mask=mask, scale=sm)
+        np.testing.assert_allclose(out[qo[b]:qo[b + 1]], ref[0].numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+    assert np.all(mass >= np.abs(out) - 1e-12)
+
+
 # ---------------------------------------------------------------------------
 # bf16 rounding (the workspace at a calibrated scale, and the input generator)
 # ---------------------------------------------------------------------------
