@@ -962,14 +962,14 @@ def test_decode_global_scale(nk, gs):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_many_splits_against_oracle(nk, d):
-    """Split counts above 64 (the merge's 16-wave branch) up to 1024, so that
-    most splits of the shorter sequence are empty, through the one-call
+    """Split counts above 64 (the merge's 16-wave branch) up to the maximum,
+    4096, so that most splits are empty, through the one-call
     decode and the separate partial + merge with each kernel variant, over the
     NVFP4 cache and the FP8-E4M3 cache; whole outputs against the oracle."""
     wl = synth.Workload(94, "many-splits", 2, 10, 2, d, 16, 4096, True, 0)
     inp = synth.host_uniform_decode(wl)
     inp.seq_lens[1] = 1000
-    splits = (65, 200, 256, 1024)
+    splits = (65, 200, 256, 1024, 4096)
     say(f"case decode many splits: d {d} lens {inp.seq_lens.tolist()} splits {splits}")
     decode_problem(nk, inp, splits_list=splits, variants=(None, nk.VARIANT_MFMA, nk.VARIANT_VALU),
                    label=f"many-splits d{d}")
