@@ -875,7 +875,8 @@ def test_decode_ragged_and_degenerate_lengths(nk, L):
     decode_problem(nk, inp, splits_list=(1, 4), variants=(None, nk.VARIANT_VALU), label=f"L={L}")
 
 
-@pytest.mark.parametrize("shape", [(1, 1, 64, 16), (16, 1, 128, 64), (4, 4, 64, 48), (7, 1, 128, 16)])
+@pytest.mark.parametrize("shape", [(1, 1, 64, 16), (16, 1, 128, 64), (4, 4, 64, 48), (7, 1, 128, 16),
+                                   (5, 2, 128, 208), (2, 1, 64, 1024)])
 def test_decode_group_and_shape_coverage(nk, shape):
     G, H, d, P = shape
     wl = synth.Workload(91, "shape", 2, G * H, H, d, P, 333, False, 3)
