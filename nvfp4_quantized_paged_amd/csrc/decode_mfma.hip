@@ -345,6 +345,22 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
     }
   }
 
+  // ---- V rows of the chunk to LDS (token-major), ahead of the softmax, whose exponentials then
+  // cover the write-to-read latency of the transposing reads below (measured on MI355X: agentic
+  // decode -1.1%, 32K and 1M unchanged, partials bit-identical)
+  {
+    const int r = lane & 15;
+#pragma unroll
+    for (int t = 0; t < C::kTiles; t += 2)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int kk = 0; kk < C::kKSteps; ++kk) {
+          const half8_t v = unpack<D, FP8, LUT>(cur[t + tt].v, cur[t + tt].vs >> ssh, kk);
+          *reinterpret_cast<half8_t*>(vl + (16 * (t + tt) + r) * VPitch<D>::kHalfs + grp * C::kChanPerGroup + 8 * kk) = v;
+        }
+  }
+
   // ---- online softmax (base 2) per head
   float cmax = -INFINITY;
 #pragma unroll
@@ -367,8 +383,8 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
     a.ls *= alpha;
   }
 
-  // ---- PV over pairs of tiles (32 tokens = one MFMA K). The unpacked V rows of the two tiles go
-  // to the wave's LDS rows (token-major); gfx950's transposing read returns them as the A operand of
+  // ---- PV over pairs of tiles (32 tokens = one MFMA K). The unpacked V rows of the two tiles are in
+  // the wave's LDS rows (token-major, written above); gfx950's transposing read returns them as the A operand of
   // O^T = V^T P: in each 16-lane group kg, lane L names row 4kg + L/4 and channels 16ct + 4(L%4) .. +3,
   // and lane i receives channel 16ct + i of rows 4kg .. 4kg + 3.
   const int r = lane & 15;
@@ -377,14 +393,7 @@ __device__ inline void process_chunk(const Item& it, int ts, int lane, TileRaw<D
   for (int t = 0; t < C::kTiles; t += 2) {
     const half8_t pb = pack_half8(float4_t{sc[t][0], sc[t][1], sc[t][2], sc[t][3]},
                                   float4_t{sc[t + 1][0], sc[t + 1][1], sc[t + 1][2], sc[t + 1][3]});
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int kk = 0; kk < C::kKSteps; ++kk) {
-        const half8_t v = unpack<D, FP8, LUT>(cur[t + tt].v, cur[t + tt].vs >> ssh, kk);
-        *reinterpret_cast<half8_t*>(vl + (16 * tt + r) * VPitch<D>::kHalfs + grp * C::kChanPerGroup + 8 * kk) = v;
-      }
-    const int rd = (4 * kg + (r >> 2)) * VPitch<D>::kHalfs + 4 * (r & 3);
+    const int rd = (16 * t + 4 * kg + (r >> 2)) * VPitch<D>::kHalfs + 4 * (r & 3);
 #pragma unroll
     for (int ct = 0; ct < C::kCTiles; ++ct) {
       const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr(vl + rd + 16 * ct));
