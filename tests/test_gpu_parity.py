@@ -695,6 +695,45 @@ def test_extend_attention_randomized(nk, case):
     check_out(out, ref, mass, f"extend random {case}")
 
 
+@pytest.mark.parametrize("B", [9, 37, 64, 70])
+def test_extend_attention_many_sequences(nk, B):
+    """Batches around the 64-sequence limit of the longest-first workgroup
+    order (above it the natural order): ragged prefixes and chunks with ties
+    and empty chunks; every query against the oracle, for both workspace
+    types."""
+    rng = np.random.default_rng(9100 + B)
+    G, Hkv, d = 4, 2, 64
+    prefix = rng.integers(0, 260, B).astype(np.int32)
+    chunk = rng.integers(0, 40, B).astype(np.int32)
+    chunk[::7] = 0                                            # empty chunks
+    prefix[1::5] = prefix[0]                                  # equal work for several sequences
+    chunk[1::5] = chunk[0]
+    chunk[2] = max(int(chunk[2]), 1)
+    ws_offs = np.zeros(B + 1, np.int64)
+    ws_offs[1:] = np.cumsum(prefix + chunk + 1)
+    rows = int(ws_offs[-1])
+    q_offs = np.zeros(B + 1, np.int64)
+    q_offs[1:] = np.cumsum(chunk)
+    say(f"case extend many sequences: B {B}, {int(chunk.sum())} queries")
+    qb = synth.host_values(rng, (int(chunk.sum()), G * Hkv, d))
+    kb = synth.host_values(rng, (rows, Hkv, d))
+    vb = synth.host_values(rng, (rows, Hkv, d))
+    sm = 1.0 / math.sqrt(d)
+    out = nk.nvfp4_extend_attn(synth.to_device_bf16(qb), synth.to_device(q_offs), synth.to_device_bf16(kb),
+                               synth.to_device_bf16(vb), synth.to_device(ws_offs), synth.to_device(prefix), sm)
+    k8, v8 = _fp8_bytes(rng, (rows, Hkv, d)), _fp8_bytes(rng, (rows, Hkv, d))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out8 = nk.nvfp4_extend_attn_fp8(synth.to_device_bf16(qb), synth.to_device(q_offs), dev(k8), dev(v8),
+                                    synth.to_device(ws_offs), synth.to_device(prefix), sm, 1.0 / 64, 0.5)
+    torch.cuda.synchronize()
+    q64 = synth.bf16_bits_to_f64(qb)
+    ref, mass = oatt.extend_attention(q64, synth.bf16_bits_to_f64(kb), synth.bf16_bits_to_f64(vb), q_offs, ws_offs,
+                                      prefix, sm)
+    check_out(out, ref, mass, f"extend B{B}")
+    ref8, mass8 = oatt.extend_attention(q64, _e4m3_f64(k8, 1.0 / 64), _e4m3_f64(v8, 0.5), q_offs, ws_offs, prefix, sm)
+    check_out(out8, ref8, mass8, f"extend fp8 B{B}")
+
+
 def _e4m3_f64(b, scale):
     """Workspace bytes -> float64 values e4m3(byte) * scale (the oracle's E4M3 table)."""
     return onv.E4M3_VALUES[np.asarray(b, dtype=np.int64)] * float(scale)
