@@ -117,24 +117,26 @@ __global__ __launch_bounds__((64 * ExtCfg<D, G>::kWaves)) void extend_attn_kerne
   const int qb_idx = tile % num_qblocks;
   const int g = (tile / num_qblocks) % p.num_kv_heads;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // The tile's sequence slot. With at most 64 sequences, slots go to sequences longest first
-  // (work = chunk x keys, ties by index), dealt round-robin over the XCDs' contiguous slot ranges
-  // (XCD x's slots take ranks x, x + 8, x + 16, ... in that order), so the last workgroups to start
-  // are short ones and every XCD gets a like share (measured on MI355X, agentic chunk: without it the
-  // last long workgroups started at 94% of the kernel's time; bf16 workspace -4.0%, FP8 -5.0%,
-  // outputs bit-identical). Every wave ranks the sequences itself (one per lane).
+  // The tile's sequence slot. With at most 64 sequences, slots go to sequences most work first
+  // (work = chunk x (2 prefix + chunk), the query-key pairs doubled; ties by index), dealt over the
+  // XCDs' contiguous slot ranges in snake order (round k of 8 ranks goes to XCDs 0..7 for even k,
+  // 7..0 for odd k; a last partial round forward), so the last workgroups to start are short ones
+  // and the XCDs get like shares (measured on MI355X, agentic chunk: in sequence order the last long
+  // workgroups started at 94% of the kernel's time; longest first dealt round-robin -4 to -5%, then
+  // the snake order and the causal weighting another -4%; outputs bit-identical). Every wave ranks
+  // the sequences itself (one per lane).
   int b = tile / (num_qblocks * p.num_kv_heads);
   if (p.batch <= 64) {
     const int q8 = p.batch >> 3, m8 = p.batch & 7;
     const int big = m8 * (q8 + 1);                               // slots of the XCDs holding q8 + 1 ranks
     const int x = b < big ? b / (q8 + 1) : m8 + (b - big) / q8;
     const int k = b < big ? b % (q8 + 1) : (b - big) % q8;
-    const int r = x + 8 * k;
+    const int r = 8 * k + ((k & 1) && k < q8 ? 7 - x : x);
     float key = -1.0f;
     if (lane < p.batch) {
       const int L = max(p.prefix_lens[lane], 0);
       const int c = (int)(p.q_row_offsets[lane + 1] - p.q_row_offsets[lane]);
-      key = (float)c * (float)(L + c);
+      key = (float)c * (float)(2 * L + c);
     }
     int rank = 0;
     for (int j = 0; j < p.batch; ++j) {
